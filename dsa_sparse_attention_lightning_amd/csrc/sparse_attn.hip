@@ -1,0 +1,331 @@
+// Sparse attention over the top-k selected positions (gfx950).
+//
+// DSA glossary entry ("Optimizing speculative decoding", section "IndexShare
+// and KVShare"): full attention runs over only the selected subset.  With
+// IndexShare every draft step passes the same index set, so each step reads
+// only target-written KV.
+//
+// Per-head KV (H_q / H_kv in {1, 2, 4}, D in {64, 128}): the work is a gather
+// of k KV rows per head with one FMA per byte, so it is HBM-bound and runs on
+// VALU, not MFMA.  A KV row of D bf16 is read by D/8 lanes (16 bytes each);
+// a wave covers 64/(D/8) KV heads of one token, so every load instruction
+// reads one contiguous stretch of the token's K (or V) row.  The workgroup's
+// four waves walk disjoint tokens of its split with their own online-softmax
+// state (exp2 domain), merge in LDS in a fixed order, and write either the
+// final output (one split) or a partial (o, m, l) that a combine kernel folds
+// in split order.
+//
+// Latent MQA (H_kv = 1, D_qk = 576, D_v = 512): every query head reads the
+// same gathered rows, so QK^T and PV are dense contractions over the heads and
+// run on bf16 MFMA (see latent_attn_kernel).
+#include <cmath>
+
+#include "dsa_common.h"
+
+namespace dsa {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+
+struct AttnArgs {
+  const uint16_t* q;
+  const uint16_t* kc;
+  const uint16_t* vc;
+  int64_t page_stride, row_stride, head_stride;
+  const int32_t* bt;
+  const int32_t* idx;
+  int idx_rows;
+  int S_q, H_q, H_kv, page, max_pages, k;
+  float scale_log2;        // sm_scale * log2(e)
+  float* out;
+  float* lse;
+  float* part_o;           // [B*S_q*H_q][nsplit][D_v]
+  float* part_ml;          // [B*S_q*H_q][nsplit][2]
+  int nsplit;
+  int tok_per_split;
+};
+
+// ---------------------------------------------------------------------------
+// Per-head KV gather kernel
+// ---------------------------------------------------------------------------
+template <int D, int GQ, int U>
+__global__ __launch_bounds__(kThreads) void mha_attn_kernel(AttnArgs a) {
+  constexpr int SLOT = D / 8;            // lanes per KV row
+  constexpr int NSLOT = 64 / SLOT;       // KV heads per wave
+  __shared__ float s_ml[kWaves][NSLOT * GQ][2];
+  __shared__ float s_o[kWaves][NSLOT * GQ][D];
+
+  const int split = blockIdx.x;
+  const int hg = blockIdx.y;                         // KV head group
+  const int bs = blockIdx.z;                         // b * S_q + s
+  const int b = bs / a.S_q;
+  const int s = bs % a.S_q;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int slot = lane / SLOT;
+  const int sub = lane % SLOT;
+  const int g = hg * NSLOT + slot;                   // KV head of this lane
+  const bool head_ok = g < a.H_kv;
+
+  // query values: 8 dims x GQ heads
+  float qv[GQ][8];
+#pragma unroll
+  for (int j = 0; j < GQ; ++j) {
+    uint4 raw = make_uint4(0, 0, 0, 0);
+    if (head_ok) {
+      const int h = g * GQ + j;
+      raw = *reinterpret_cast<const uint4*>(a.q + ((size_t)bs * a.H_q + h) * D + sub * 8);
+    }
+    qv[j][0] = bf16_lo(raw.x); qv[j][1] = bf16_hi(raw.x);
+    qv[j][2] = bf16_lo(raw.y); qv[j][3] = bf16_hi(raw.y);
+    qv[j][4] = bf16_lo(raw.z); qv[j][5] = bf16_hi(raw.z);
+    qv[j][6] = bf16_lo(raw.w); qv[j][7] = bf16_hi(raw.w);
+  }
+  float m[GQ], l[GQ], acc[GQ][8];
+#pragma unroll
+  for (int j = 0; j < GQ; ++j) {
+    m[j] = -INFINITY;
+    l[j] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
+  }
+
+  const int32_t* idx = a.idx + ((size_t)b * a.idx_rows + (a.idx_rows > 1 ? s : 0)) * a.k;
+  const int32_t* bt = a.bt + (size_t)b * a.max_pages;
+  const int t_lo = split * a.tok_per_split;
+  const int t_hi = min(t_lo + a.tok_per_split, a.k);
+  const size_t lane_off = (size_t)g * a.head_stride + sub * 8;
+
+  for (int i0 = t_lo + wave; i0 < t_hi; i0 += kWaves * U) {
+    uint4 kr[U], vr[U];
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * kWaves;
+      const int t = i < t_hi ? idx[i] : -1;
+      ok[u] = t >= 0;
+      kr[u] = make_uint4(0, 0, 0, 0);
+      vr[u] = make_uint4(0, 0, 0, 0);
+      if (ok[u] && head_ok) {
+        const size_t row = (size_t)bt[t / a.page] * a.page_stride + (size_t)(t % a.page) * a.row_stride;
+        kr[u] = *reinterpret_cast<const uint4*>(a.kc + row + lane_off);
+        vr[u] = *reinterpret_cast<const uint4*>(a.vc + row + lane_off);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (!ok[u]) continue;   // wave-uniform
+      float kf[8], vf[8];
+      kf[0] = bf16_lo(kr[u].x); kf[1] = bf16_hi(kr[u].x);
+      kf[2] = bf16_lo(kr[u].y); kf[3] = bf16_hi(kr[u].y);
+      kf[4] = bf16_lo(kr[u].z); kf[5] = bf16_hi(kr[u].z);
+      kf[6] = bf16_lo(kr[u].w); kf[7] = bf16_hi(kr[u].w);
+      vf[0] = bf16_lo(vr[u].x); vf[1] = bf16_hi(vr[u].x);
+      vf[2] = bf16_lo(vr[u].y); vf[3] = bf16_hi(vr[u].y);
+      vf[4] = bf16_lo(vr[u].z); vf[5] = bf16_hi(vr[u].z);
+      vf[6] = bf16_lo(vr[u].w); vf[7] = bf16_hi(vr[u].w);
+#pragma unroll
+      for (int j = 0; j < GQ; ++j) {
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d = fmaf(qv[j][e], kf[e], d);
+#pragma unroll
+        for (int o = SLOT / 2; o >= 1; o >>= 1) d += __shfl_xor(d, o, 64);
+        const float sc = d * a.scale_log2;
+        const float mn = fmaxf(m[j], sc);
+        const float corr = fast_exp2(m[j] - mn);
+        const float p = fast_exp2(sc - mn);
+        l[j] = l[j] * corr + p;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[j][e] = fmaf(p, vf[e], acc[j][e] * corr);
+        m[j] = mn;
+      }
+    }
+  }
+
+  // merge the four waves (fixed order)
+#pragma unroll
+  for (int j = 0; j < GQ; ++j) {
+    if (sub == 0) {
+      s_ml[wave][slot * GQ + j][0] = m[j];
+      s_ml[wave][slot * GQ + j][1] = l[j];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s_o[wave][slot * GQ + j][sub * 8 + e] = acc[j][e];
+  }
+  __syncthreads();
+  // thread -> (head-in-group, dim) pairs
+  for (int p = threadIdx.x; p < NSLOT * GQ * D; p += kThreads) {
+    const int hj = p / D;
+    const int d = p % D;
+    const int gg = hg * NSLOT + hj / GQ;
+    if (gg >= a.H_kv) continue;
+    const int h = gg * GQ + hj % GQ;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_ml[w][hj][0]);
+    float Lsum = 0.f, O = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float c = fast_exp2(s_ml[w][hj][0] - M);
+        Lsum += c * s_ml[w][hj][1];
+        O += c * s_o[w][hj][d];
+      }
+    }
+    const size_t row = (size_t)bs * a.H_q + h;
+    if (a.nsplit == 1) {
+      a.out[row * D + d] = M == -INFINITY ? 0.f : O / Lsum;
+      if (d == 0 && a.lse) a.lse[row] = M == -INFINITY ? -INFINITY : (M + __log2f(Lsum)) * kLn2;
+    } else {
+      a.part_o[(row * a.nsplit + split) * D + d] = O;
+      if (d == 0) {
+        a.part_ml[(row * a.nsplit + split) * 2 + 0] = M;
+        a.part_ml[(row * a.nsplit + split) * 2 + 1] = Lsum;
+      }
+    }
+  }
+}
+
+// Folds split partials in split order.  One wave per (b, s, h) row.
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part_o,
+                                                      const float* __restrict__ part_ml, int rows,
+                                                      int nsplit, int D, float* __restrict__ out,
+                                                      float* __restrict__ lse) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const float* ml = part_ml + (size_t)row * nsplit * 2;
+  float M = -INFINITY;
+  for (int i = 0; i < nsplit; ++i) M = fmaxf(M, ml[2 * i]);
+  float Lsum = 0.f;
+  if (M != -INFINITY)
+    for (int i = 0; i < nsplit; ++i) Lsum += fast_exp2(ml[2 * i] - M) * ml[2 * i + 1];
+  for (int d = lane; d < D; d += 64) {
+    float O = 0.f;
+    if (M != -INFINITY)
+      for (int i = 0; i < nsplit; ++i) O += fast_exp2(ml[2 * i] - M) * part_o[((size_t)row * nsplit + i) * D + d];
+    out[(size_t)row * D + d] = M == -INFINITY ? 0.f : O / Lsum;
+  }
+  if (lane == 0 && lse) lse[row] = M == -INFINITY ? -INFINITY : (M + __log2f(Lsum)) * kLn2;
+}
+
+// ---------------------------------------------------------------------------
+// Launch planning (shared by the workspace query and the call)
+// ---------------------------------------------------------------------------
+struct Plan {
+  int nsplit;
+  int tok_per_split;
+  int head_groups;
+  size_t ws_bytes;
+  size_t part_o_off, part_ml_off;
+};
+
+Plan make_plan(int B, int S_q, int H_q, int H_kv, int D_qk, int D_v, int k) {
+  Plan p{};
+  const int nslot = 64 / (D_qk / 8);
+  p.head_groups = (H_kv + nslot - 1) / nslot;
+  const long long base = (long long)B * S_q * p.head_groups;
+  constexpr int kMinTok = 32;
+  int ns = (int)((1024 + base - 1) / base);
+  const int max_ns = (k + kMinTok - 1) / kMinTok;
+  if (ns > max_ns) ns = max_ns;
+  if (ns < 1) ns = 1;
+  p.tok_per_split = (k + ns - 1) / ns;
+  p.nsplit = (k + p.tok_per_split - 1) / p.tok_per_split;
+  const size_t rows = (size_t)B * S_q * H_q;
+  if (p.nsplit > 1) {
+    p.part_o_off = 0;
+    p.part_ml_off = align_up(rows * p.nsplit * D_v * sizeof(float), 256);
+    p.ws_bytes = p.part_ml_off + align_up(rows * p.nsplit * 2 * sizeof(float), 256);
+  }
+  return p;
+}
+
+template <int D, int GQ>
+void launch_mha(const AttnArgs& a, const Plan& p, int B, hipStream_t s) {
+  dim3 grid(p.nsplit, p.head_groups, B * a.S_q);
+  hipLaunchKernelGGL((mha_attn_kernel<D, GQ, 8>), grid, dim3(kThreads), 0, s, a);
+}
+
+}  // namespace
+}  // namespace dsa
+
+extern "C" size_t dsa_sparse_attn_workspace_size(int B, int S_q, int H_q, int H_kv, int D_qk, int D_v, int k) {
+  if (B < 1 || S_q < 1 || H_q < 1 || H_kv < 1 || D_qk < 8 || D_v < 1 || k < 1) return 0;
+  if (D_qk != 64 && D_qk != 128) return 0;
+  return dsa::make_plan(B, S_q, H_q, H_kv, D_qk, D_v, k).ws_bytes;
+}
+
+extern "C" dsa_status dsa_sparse_attn(const void* q, const void* k_cache, const void* v_cache,
+                                      int64_t kv_page_stride, int64_t kv_row_stride, int64_t kv_head_stride,
+                                      const int32_t* block_table, const int32_t* idx, int idx_rows, int B,
+                                      int S_q, int H_q, int H_kv, int D_qk, int D_v, int page, int max_pages,
+                                      int k, float sm_scale, float* out, float* lse, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  using namespace dsa;
+  clear_error();
+  DSA_REQUIRE(q && k_cache && v_cache && block_table && idx && out, DSA_ERR_INVALID_ARG,
+              "dsa_sparse_attn: null pointer argument");
+  DSA_REQUIRE(B >= 1 && S_q >= 1 && H_q >= 1 && H_kv >= 1 && D_qk >= 1 && D_v >= 1 && page >= 1 &&
+                  max_pages >= 1 && k >= 1,
+              DSA_ERR_INVALID_ARG, "dsa_sparse_attn: sizes must be positive");
+  DSA_REQUIRE(idx_rows == 1 || idx_rows == S_q, DSA_ERR_INVALID_ARG,
+              "dsa_sparse_attn: idx_rows=%d must be 1 or S_q=%d", idx_rows, S_q);
+  DSA_REQUIRE(kv_page_stride >= 0 && kv_row_stride >= 0 && kv_head_stride >= 0, DSA_ERR_INVALID_ARG,
+              "dsa_sparse_attn: strides must be non-negative");
+  DSA_REQUIRE(H_q % H_kv == 0, DSA_ERR_INVALID_ARG, "dsa_sparse_attn: H_q=%d not a multiple of H_kv=%d", H_q, H_kv);
+  DSA_REQUIRE(std::isfinite(sm_scale), DSA_ERR_INVALID_ARG, "dsa_sparse_attn: sm_scale not finite");
+  const int gq = H_q / H_kv;
+  DSA_REQUIRE((D_qk == 64 || D_qk == 128) && D_v == D_qk && (gq == 1 || gq == 2 || gq == 4),
+              DSA_ERR_UNSUPPORTED, "dsa_sparse_attn: (H_q=%d, H_kv=%d, D_qk=%d, D_v=%d) not supported",
+              H_q, H_kv, D_qk, D_v);
+  DSA_REQUIRE(aligned16(q) && aligned16(k_cache) && aligned16(v_cache) && kv_page_stride % 8 == 0 &&
+                  kv_row_stride % 8 == 0 && kv_head_stride % 8 == 0,
+              DSA_ERR_INVALID_ARG, "dsa_sparse_attn: q/K/V rows must be 16-byte aligned");
+  const Plan p = make_plan(B, S_q, H_q, H_kv, D_qk, D_v, k);
+  DSA_REQUIRE(p.ws_bytes == 0 || (workspace && workspace_bytes >= p.ws_bytes), DSA_ERR_WORKSPACE,
+              "dsa_sparse_attn: workspace of %zu bytes needed, %zu given", p.ws_bytes, workspace_bytes);
+  AttnArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.kc = static_cast<const uint16_t*>(k_cache);
+  a.vc = static_cast<const uint16_t*>(v_cache);
+  a.page_stride = kv_page_stride;
+  a.row_stride = kv_row_stride;
+  a.head_stride = kv_head_stride;
+  a.bt = block_table;
+  a.idx = idx;
+  a.idx_rows = idx_rows;
+  a.S_q = S_q;
+  a.H_q = H_q;
+  a.H_kv = H_kv;
+  a.page = page;
+  a.max_pages = max_pages;
+  a.k = k;
+  a.scale_log2 = sm_scale * kLog2e;
+  a.out = out;
+  a.lse = lse;
+  a.nsplit = p.nsplit;
+  a.tok_per_split = p.tok_per_split;
+  if (p.nsplit > 1) {
+    a.part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.part_o_off);
+    a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.part_ml_off);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (D_qk == 64) {
+    if (gq == 1) launch_mha<64, 1>(a, p, B, s);
+    else if (gq == 2) launch_mha<64, 2>(a, p, B, s);
+    else launch_mha<64, 4>(a, p, B, s);
+  } else {
+    if (gq == 1) launch_mha<128, 1>(a, p, B, s);
+    else if (gq == 2) launch_mha<128, 2>(a, p, B, s);
+    else launch_mha<128, 4>(a, p, B, s);
+  }
+  dsa_status st = launch_status("dsa_sparse_attn");
+  if (st != DSA_OK || p.nsplit == 1) return st;
+  const int rows = B * S_q * H_q;
+  hipLaunchKernelGGL(combine_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, a.part_o, a.part_ml, rows, p.nsplit,
+                     D_v, out, lse);
+  return launch_status("dsa_sparse_attn(combine)");
+}

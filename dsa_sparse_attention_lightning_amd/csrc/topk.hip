@@ -1,0 +1,376 @@
+// Top-k selection per (sequence, row) by radix select (gfx950).
+//
+// DSA glossary entry ("Optimizing speculative decoding", section "IndexShare
+// and KVShare"): a top-k selection keeps the most relevant past positions.
+// Order: score descending, then position ascending; output ascending, -1 pad.
+//
+// Scores are mapped to order-preserving 32-bit keys (-0.0 canonicalised to
+// +0.0).  The kept set is {key > K*} plus the lowest positions with key == K*,
+// where K* is the k-th largest key.  Five launches per call, all multi-
+// workgroup except the last:
+//   1 zero     clear the per-row histograms and counters
+//   2 hist1    histogram of key bits 31..20 (4096 bins; LDS, then integer
+//              atomics into the row's global histogram)
+//   3 hist2    every workgroup scans hist1 for the threshold bin T1, then
+//              histograms key bits 19..8 of the elements in bin T1
+//   4 collect  with T1 and T2 known, elements above the 24-bit threshold are
+//              appended to the row's `sel` list and those on it to `cand`
+//              (wave-aggregated integer atomics; list order is irrelevant)
+//   5 finish   one workgroup per row radix-selects the missing elements among
+//              the candidates on the composite (key low 8 bits, ~position),
+//              merges them with `sel` and bitonic-sorts the kept positions.
+// Rows with row_len <= k skip 2-4 and are written directly by 5.
+// Integer atomics only: the result is a function of the input set, and the
+// final sort makes the output order canonical, so runs are bitwise identical.
+#include "dsa_common.h"
+
+namespace dsa {
+namespace {
+
+constexpr int kBins = 4096;
+constexpr int kHistThreads = 256;
+constexpr int kChunk = 4096;          // positions per workgroup in passes 2-4
+constexpr int kFinThreads = 1024;
+constexpr int kMaxK = 8192;
+constexpr int kCandCap = 8192;        // candidates held in LDS by pass 5
+
+struct RowWs {
+  uint32_t* hist1;   // [rows][kBins]
+  uint32_t* hist2;   // [rows][kBins]
+  uint32_t* cnt;     // [rows][4]: n_sel, n_cand
+  int32_t* sel;      // [rows][k]
+  uint2* cand;       // [rows][ld]: (key, position)
+};
+
+__host__ __device__ inline size_t ws_bytes(int rows, int64_t ld, int k, RowWs* out, char* base) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  };
+  size_t h1 = take((size_t)rows * kBins * 4);
+  size_t h2 = take((size_t)rows * kBins * 4);
+  size_t cn = take((size_t)rows * 4 * 4);
+  size_t sl = take((size_t)rows * k * 4);
+  size_t cd = take((size_t)rows * ld * 8);
+  if (out) {
+    out->hist1 = reinterpret_cast<uint32_t*>(base + h1);
+    out->hist2 = reinterpret_cast<uint32_t*>(base + h2);
+    out->cnt = reinterpret_cast<uint32_t*>(base + cn);
+    out->sel = reinterpret_cast<int32_t*>(base + sl);
+    out->cand = reinterpret_cast<uint2*>(base + cd);
+  }
+  return off;
+}
+
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// Exclusive prefix of the lanes below this one in a 64-bit ballot mask.
+__device__ __forceinline__ uint32_t mask_rank(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Appends `pred` lanes to a list with one atomic per wave; returns the slot
+// of this lane (valid where pred).
+__device__ __forceinline__ uint32_t wave_append(bool pred, uint32_t* counter) {
+  const uint64_t m = __ballot(pred);
+  if (m == 0) return 0;
+  const int leader = __ffsll((long long)m) - 1;
+  uint32_t base = 0;
+  if (lane_id() == leader) base = atomicAdd(counter, (uint32_t)__popcll(m));
+  base = __shfl(base, leader, 64);
+  return base + mask_rank(m);
+}
+
+// Threshold bin of a 4096-bin histogram, scanning from the top: the bin T
+// with above(T) < need <= above(T) + hist[T].  Run by all kHistThreads
+// threads; result in *t_out / *above_out (shared).
+__device__ void find_threshold_4096(const uint32_t* hist, uint32_t need, uint32_t* s_wave,
+                                    int* t_out, uint32_t* above_out) {
+  constexpr int per = kBins / kHistThreads;   // 16 bins per thread
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    *t_out = 0;
+    *above_out = 0;
+  }
+  // thread tid owns bins [top - per*tid - per + 1, top - per*tid], top = 4095
+  const int hi_bin = kBins - 1 - tid * per;
+  uint32_t c[per];
+  uint32_t tot = 0;
+#pragma unroll
+  for (int j = 0; j < per; ++j) {
+    c[j] = hist[hi_bin - j];
+    tot += c[j];
+  }
+  // inclusive scan over threads (descending bin order)
+  uint32_t inc = tot;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    uint32_t v = __shfl_up(inc, o, 64);
+    if (lane_id() >= o) inc += v;
+  }
+  const int wave = tid >> 6;
+  if (lane_id() == 63) s_wave[wave] = inc;
+  __syncthreads();
+  uint32_t before = 0;
+  for (int wv = 0; wv < wave; ++wv) before += s_wave[wv];
+  uint32_t run = before + inc - tot;  // elements in bins above this thread's range
+#pragma unroll
+  for (int j = 0; j < per; ++j) {
+    if (run < need && run + c[j] >= need) {
+      *t_out = hi_bin - j;
+      *above_out = run;
+    }
+    run += c[j];
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kHistThreads) void topk_zero_kernel(RowWs ws) {
+  const int row = blockIdx.x;
+  for (int i = threadIdx.x; i < kBins; i += kHistThreads) {
+    ws.hist1[(size_t)row * kBins + i] = 0;
+    ws.hist2[(size_t)row * kBins + i] = 0;
+  }
+  if (threadIdx.x < 4) ws.cnt[row * 4 + threadIdx.x] = 0;
+}
+
+__global__ __launch_bounds__(kHistThreads) void topk_hist1_kernel(const float* __restrict__ scores,
+                                                                  const int32_t* __restrict__ row_len,
+                                                                  int64_t ld, int k, RowWs ws) {
+  __shared__ uint32_t h[kBins];
+  const int row = blockIdx.y;
+  const int L = row_len[row];
+  const int t0 = blockIdx.x * kChunk;
+  if (L <= k || t0 >= L) return;
+  for (int i = threadIdx.x; i < kBins; i += kHistThreads) h[i] = 0;
+  __syncthreads();
+  const float* s = scores + (size_t)row * ld;
+  const int t1 = min(t0 + kChunk, L);
+  for (int t = t0 + threadIdx.x; t < t1; t += kHistThreads) atomicAdd(&h[order_key(s[t]) >> 20], 1u);
+  __syncthreads();
+  uint32_t* g = ws.hist1 + (size_t)row * kBins;
+  for (int i = threadIdx.x; i < kBins; i += kHistThreads)
+    if (h[i]) atomicAdd(&g[i], h[i]);
+}
+
+__global__ __launch_bounds__(kHistThreads) void topk_hist2_kernel(const float* __restrict__ scores,
+                                                                  const int32_t* __restrict__ row_len,
+                                                                  int64_t ld, int k, RowWs ws) {
+  __shared__ uint32_t h[kBins];
+  __shared__ uint32_t s_wave[kHistThreads / 64];
+  __shared__ int s_t1;
+  __shared__ uint32_t s_a1;
+  const int row = blockIdx.y;
+  const int L = row_len[row];
+  const int t0 = blockIdx.x * kChunk;
+  if (L <= k || t0 >= L) return;
+  for (int i = threadIdx.x; i < kBins; i += kHistThreads) h[i] = 0;
+  find_threshold_4096(ws.hist1 + (size_t)row * kBins, (uint32_t)k, s_wave, &s_t1, &s_a1);
+  const uint32_t T1 = (uint32_t)s_t1;
+  const float* s = scores + (size_t)row * ld;
+  const int t1 = min(t0 + kChunk, L);
+  for (int t = t0 + threadIdx.x; t < t1; t += kHistThreads) {
+    const uint32_t key = order_key(s[t]);
+    if ((key >> 20) == T1) atomicAdd(&h[(key >> 8) & 0xfffu], 1u);
+  }
+  __syncthreads();
+  uint32_t* g = ws.hist2 + (size_t)row * kBins;
+  for (int i = threadIdx.x; i < kBins; i += kHistThreads)
+    if (h[i]) atomicAdd(&g[i], h[i]);
+}
+
+__global__ __launch_bounds__(kHistThreads) void topk_collect_kernel(const float* __restrict__ scores,
+                                                                    const int32_t* __restrict__ row_len,
+                                                                    int64_t ld, int k, RowWs ws) {
+  __shared__ uint32_t s_wave[kHistThreads / 64];
+  __shared__ int s_t1, s_t2;
+  __shared__ uint32_t s_a1, s_a2;
+  const int row = blockIdx.y;
+  const int L = row_len[row];
+  const int t0 = blockIdx.x * kChunk;
+  if (L <= k || t0 >= L) return;
+  find_threshold_4096(ws.hist1 + (size_t)row * kBins, (uint32_t)k, s_wave, &s_t1, &s_a1);
+  find_threshold_4096(ws.hist2 + (size_t)row * kBins, (uint32_t)k - s_a1, s_wave, &s_t2, &s_a2);
+  const uint32_t prefix = ((uint32_t)s_t1 << 12) | (uint32_t)s_t2;  // key bits 31..8
+  const float* s = scores + (size_t)row * ld;
+  int32_t* sel = ws.sel + (size_t)row * k;
+  uint2* cand = ws.cand + (size_t)row * ld;
+  uint32_t* cnt = ws.cnt + row * 4;
+  const int t1 = min(t0 + kChunk, L);
+  // whole waves iterate together so the ballots see every lane
+  for (int tb = t0; tb < t1; tb += kHistThreads) {
+    const int t = tb + threadIdx.x;
+    uint32_t key = 0;
+    bool valid = t < t1;
+    if (valid) key = order_key(s[t]);
+    const uint32_t top = key >> 8;
+    const bool is_sel = valid && top > prefix;
+    const bool is_cand = valid && top == prefix;
+    const uint32_t ps = wave_append(is_sel, &cnt[0]);
+    if (is_sel && ps < (uint32_t)k) sel[ps] = t;
+    const uint32_t pc = wave_append(is_cand, &cnt[1]);
+    if (is_cand && pc < (uint32_t)ld) cand[pc] = make_uint2(key, (uint32_t)t);
+  }
+}
+
+// Composite rank of a candidate: key bits 7..0, then ~position (lower
+// position ranks higher).  40 bits; bits above are equal for all candidates.
+__device__ __forceinline__ uint64_t cand_rank(uint2 c) {
+  return ((uint64_t)(c.x & 0xffu) << 32) | (uint64_t)(~c.y);
+}
+
+template <bool kInLds>
+__device__ void select_candidates(const uint2* cand_g, const uint64_t* cand_l, int n_cand, uint32_t m,
+                                  uint32_t* hist, int32_t* out, uint32_t* out_cnt, uint32_t* s_misc) {
+  // s_misc[0] = chosen digit, s_misc[1] = count above, s_misc[2] = count equal
+  uint64_t prefix = 0;
+  int shift = 40;
+  uint32_t m_rem = m;
+  const int tid = threadIdx.x;
+  while (shift > 0) {
+    const int nshift = shift - 8;
+    for (int i = tid; i < 256; i += kFinThreads) hist[i] = 0;
+    __syncthreads();
+    for (int i = tid; i < n_cand; i += kFinThreads) {
+      const uint64_t c = kInLds ? cand_l[i] : cand_rank(cand_g[i]);
+      if ((c >> shift) == (prefix >> shift)) atomicAdd(&hist[(c >> nshift) & 0xffu], 1u);
+    }
+    __syncthreads();
+    if (tid < 64) {
+      // lane owns bins 255-4*lane .. 252-4*lane (descending)
+      uint32_t c4[4];
+      uint32_t tot = 0;
+      for (int j = 0; j < 4; ++j) {
+        c4[j] = hist[255 - 4 * tid - j];
+        tot += c4[j];
+      }
+      uint32_t inc = tot;
+      for (int o = 1; o < 64; o <<= 1) {
+        uint32_t v = __shfl_up(inc, o, 64);
+        if (tid >= o) inc += v;
+      }
+      uint32_t run = inc - tot;
+      for (int j = 0; j < 4; ++j) {
+        if (run < m_rem && run + c4[j] >= m_rem) {
+          s_misc[0] = 255 - 4 * tid - j;
+          s_misc[1] = run;
+          s_misc[2] = c4[j];
+        }
+        run += c4[j];
+      }
+    }
+    __syncthreads();
+    const uint32_t digit = s_misc[0];
+    m_rem -= s_misc[1];
+    const uint32_t eq = s_misc[2];
+    __syncthreads();
+    prefix |= (uint64_t)digit << nshift;
+    shift = nshift;
+    if (eq == m_rem) break;   // every candidate on this prefix is kept
+  }
+  for (int i = tid; i < n_cand; i += kFinThreads) {
+    const uint64_t c = kInLds ? cand_l[i] : cand_rank(cand_g[i]);
+    if ((c >> shift) >= (prefix >> shift)) {
+      const uint32_t slot = atomicAdd(out_cnt, 1u);
+      if (slot < (uint32_t)kMaxK) out[slot] = (int32_t)(~(uint32_t)c);
+    }
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const int32_t* __restrict__ row_len, int k,
+                                                                  int32_t* __restrict__ idx, RowWs ws,
+                                                                  int64_t ld) {
+  __shared__ int32_t list[kMaxK];
+  __shared__ uint64_t cand_l[kCandCap];
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t s_misc[4];
+  __shared__ uint32_t s_cnt;
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int L = row_len[row];
+  int32_t* dst = idx + (size_t)row * k;
+  if (L <= k) {
+    for (int i = tid; i < k; i += kFinThreads) dst[i] = i < L ? i : -1;
+    return;
+  }
+  // counts are bounded by construction; the clamps only keep a broken
+  // precondition (row_len > ld) from writing out of bounds
+  const uint32_t n_sel = min(ws.cnt[row * 4 + 0], (uint32_t)k - 1u);
+  const int n_cand = (int)min((int64_t)ws.cnt[row * 4 + 1], ld);
+  const uint32_t m = (uint32_t)k - n_sel;
+  const int32_t* sel = ws.sel + (size_t)row * k;
+  const uint2* cand = ws.cand + (size_t)row * ld;
+  for (uint32_t i = tid; i < n_sel; i += kFinThreads) list[i] = sel[i];
+  if (tid == 0) s_cnt = n_sel;
+  if (n_cand <= kCandCap) {
+    for (int i = tid; i < n_cand; i += kFinThreads) cand_l[i] = cand_rank(cand[i]);
+    __syncthreads();
+    select_candidates<true>(cand, cand_l, n_cand, m, hist, list, &s_cnt, s_misc);
+  } else {
+    __syncthreads();
+    select_candidates<false>(cand, cand_l, n_cand, m, hist, list, &s_cnt, s_misc);
+  }
+  // bitonic sort of the k kept positions, ascending
+  int P = 1;
+  while (P < k) P <<= 1;
+  for (int i = k + tid; i < P; i += kFinThreads) list[i] = 0x7fffffff;
+  __syncthreads();
+  for (int size = 2; size <= P; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < P / 2; i += kFinThreads) {
+        const int lo = 2 * i - (i & (stride - 1));
+        const int hi = lo + stride;
+        const bool up = (lo & size) == 0;
+        const int32_t a = list[lo], b = list[hi];
+        if ((a > b) == up) {
+          list[lo] = b;
+          list[hi] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = tid; i < k; i += kFinThreads) dst[i] = list[i];
+}
+
+}  // namespace
+}  // namespace dsa
+
+extern "C" size_t dsa_topk_workspace_size(int B, int R, int64_t ld, int k) {
+  if (B < 1 || R < 1 || ld < 1 || k < 1) return 0;
+  return dsa::ws_bytes(B * R, ld, k, nullptr, nullptr);
+}
+
+extern "C" dsa_status dsa_topk(const float* scores, const int32_t* row_len, int B, int R, int64_t ld, int k,
+                               int32_t* idx, void* workspace, size_t workspace_bytes, void* stream) {
+  using namespace dsa;
+  clear_error();
+  DSA_REQUIRE(scores && row_len && idx, DSA_ERR_INVALID_ARG, "dsa_topk: null pointer argument");
+  DSA_REQUIRE(B >= 1 && R >= 1 && ld >= 1 && k >= 1, DSA_ERR_INVALID_ARG,
+              "dsa_topk: sizes must be positive (B=%d R=%d ld=%lld k=%d)", B, R, (long long)ld, k);
+  DSA_REQUIRE(k <= kMaxK, DSA_ERR_UNSUPPORTED, "dsa_topk: k=%d > %d", k, kMaxK);
+  DSA_REQUIRE(ld <= ((int64_t)1 << 31) - 1, DSA_ERR_UNSUPPORTED, "dsa_topk: ld too large");
+  const int rows = B * R;
+  const size_t need = ws_bytes(rows, ld, k, nullptr, nullptr);
+  DSA_REQUIRE(workspace && workspace_bytes >= need, DSA_ERR_WORKSPACE,
+              "dsa_topk: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  RowWs ws;
+  ws_bytes(rows, ld, k, &ws, static_cast<char*>(workspace));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const unsigned chunks = (unsigned)((ld + kChunk - 1) / kChunk);
+  hipLaunchKernelGGL(topk_zero_kernel, dim3(rows), dim3(kHistThreads), 0, s, ws);
+  hipLaunchKernelGGL(topk_hist1_kernel, dim3(chunks, rows), dim3(kHistThreads), 0, s, scores, row_len, ld, k, ws);
+  hipLaunchKernelGGL(topk_hist2_kernel, dim3(chunks, rows), dim3(kHistThreads), 0, s, scores, row_len, ld, k, ws);
+  hipLaunchKernelGGL(topk_collect_kernel, dim3(chunks, rows), dim3(kHistThreads), 0, s, scores, row_len, ld, k, ws);
+  hipLaunchKernelGGL(topk_finish_kernel, dim3(rows), dim3(kFinThreads), 0, s, row_len, k, idx, ws, ld);
+  return launch_status("dsa_topk");
+}

@@ -1,0 +1,116 @@
+"""Host-side checks of libdsa.so that need no GPU: it loads, exports every
+entry point include/dsa.h declares, and rejects bad arguments before any HIP
+call (so no kernel is ever launched here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from dsa_sparse_attention_lightning_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+lib = _lib.load()
+FAKE = ctypes.c_void_p(0x10000)       # 16-byte aligned, never dereferenced
+MISALIGNED = ctypes.c_void_p(0x10004)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"if", "defined"})
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"dsa_index_scores", "dsa_topk", "dsa_sparse_attn", "spec_verify"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.SIGNATURES)
+
+
+def test_status_strings_and_version():
+    assert lib.dsa_abi_version() == 1
+    for code in range(5):
+        assert lib.dsa_status_str(code).decode().startswith("DSA_")
+    assert b"unknown" in lib.dsa_status_str(99)
+
+
+def _scores_call(**over):
+    a = dict(q=FAKE, w=FAKE, k=FAKE, bt=FAKE, rl=FAKE, out=FAKE, B=1, R=1, H=64, D=128, page=64,
+             max_pages=4, ld=256)
+    a.update(over)
+    return lib.dsa_index_scores(a["q"], a["w"], a["k"], a["bt"], a["rl"], a["out"], a["B"], a["R"],
+                                a["H"], a["D"], a["page"], a["max_pages"], a["ld"], None)
+
+
+def test_index_scores_validation():
+    assert _scores_call(q=None) == _lib.DSA_ERR_INVALID_ARG
+    assert b"null" in lib.dsa_last_error()
+    assert _scores_call(B=0) == _lib.DSA_ERR_INVALID_ARG
+    assert _scores_call(D=96) == _lib.DSA_ERR_UNSUPPORTED
+    assert _scores_call(H=65) == _lib.DSA_ERR_UNSUPPORTED
+    assert _scores_call(R=9) == _lib.DSA_ERR_UNSUPPORTED
+    assert _scores_call(q=MISALIGNED) == _lib.DSA_ERR_INVALID_ARG
+
+
+def test_topk_validation():
+    ws = lib.dsa_topk_workspace_size(2, 1, 1000, 64)
+    assert ws > 0
+    assert lib.dsa_topk_workspace_size(0, 1, 1000, 64) == 0
+    assert lib.dsa_topk(None, FAKE, 1, 1, 100, 8, FAKE, FAKE, ws, None) == _lib.DSA_ERR_INVALID_ARG
+    assert lib.dsa_topk(FAKE, FAKE, 1, 1, 100, 0, FAKE, FAKE, ws, None) == _lib.DSA_ERR_INVALID_ARG
+    assert lib.dsa_topk(FAKE, FAKE, 1, 1, 100, 9000, FAKE, FAKE, ws, None) == _lib.DSA_ERR_UNSUPPORTED
+    assert lib.dsa_topk(FAKE, FAKE, 2, 1, 1000, 64, FAKE, FAKE, ws - 1, None) == _lib.DSA_ERR_WORKSPACE
+    assert lib.dsa_topk(FAKE, FAKE, 2, 1, 1000, 64, FAKE, None, ws, None) == _lib.DSA_ERR_WORKSPACE
+
+
+def _attn_call(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, ps=64 * 64 * 128, rs=64 * 128, hs=128, bt=FAKE, idx=FAKE, idx_rows=1,
+             B=1, S_q=1, H_q=64, H_kv=64, D_qk=128, D_v=128, page=64, max_pages=4, kk=2048, scale=0.1,
+             out=FAKE, lse=None, ws=FAKE, ws_bytes=1 << 30)
+    a.update(over)
+    return lib.dsa_sparse_attn(a["q"], a["k"], a["v"], a["ps"], a["rs"], a["hs"], a["bt"], a["idx"],
+                               a["idx_rows"], a["B"], a["S_q"], a["H_q"], a["H_kv"], a["D_qk"], a["D_v"],
+                               a["page"], a["max_pages"], a["kk"], a["scale"], a["out"], a["lse"],
+                               a["ws"], a["ws_bytes"], None)
+
+
+def test_sparse_attn_validation():
+    assert _attn_call(q=None) == _lib.DSA_ERR_INVALID_ARG
+    assert _attn_call(H_q=63) == _lib.DSA_ERR_INVALID_ARG            # H_q % H_kv
+    assert _attn_call(H_kv=8, H_q=64) == _lib.DSA_ERR_UNSUPPORTED     # group 8
+    assert _attn_call(D_qk=96, D_v=96) == _lib.DSA_ERR_UNSUPPORTED
+    assert _attn_call(idx_rows=3, S_q=2) == _lib.DSA_ERR_INVALID_ARG
+    assert _attn_call(rs=64 * 128 + 4) == _lib.DSA_ERR_INVALID_ARG    # row not 16-byte aligned
+    assert _attn_call(scale=float("nan")) == _lib.DSA_ERR_INVALID_ARG
+    need = lib.dsa_sparse_attn_workspace_size(1, 1, 64, 64, 128, 128, 2048)
+    assert need > 0
+    assert _attn_call(ws_bytes=need - 1) == _lib.DSA_ERR_WORKSPACE
+
+
+def test_spec_verify_validation():
+    ws = lib.spec_verify_workspace_size(4, 7, 1024)
+    assert ws > 0
+    call = lambda **o: lib.spec_verify(o.get("t", FAKE), FAKE, FAKE, o.get("B", 4), o.get("G", 7),
+                                       o.get("V", 1024), None, 0, 0, FAKE, FAKE, None,
+                                       o.get("ws", FAKE), o.get("wsb", ws), None)
+    assert call(t=None) == _lib.DSA_ERR_INVALID_ARG
+    assert call(G=0) == _lib.DSA_ERR_INVALID_ARG
+    assert call(G=33) == _lib.DSA_ERR_UNSUPPORTED
+    assert call(V=(1 << 20) + 1) == _lib.DSA_ERR_UNSUPPORTED
+    assert call(B=5000) == _lib.DSA_ERR_UNSUPPORTED
+    assert call(wsb=ws - 1) == _lib.DSA_ERR_WORKSPACE
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(ImportError):
+        _lib._lib_backup = _lib._lib
+        try:
+            _lib._lib = None
+            _lib.load(str(tmp_path / "missing.so"))
+        finally:
+            _lib._lib = _lib._lib_backup

@@ -1,0 +1,309 @@
+"""GPU parity: the HIP library against the CPU oracle on seeded inputs.
+
+Top-k indices and accept decisions are compared bit for bit; indexer scores
+bit for bit on integer/dyadic inputs (exact in fp32 under any summation
+order); attention within max abs error 1e-2 (bf16 inputs, fp32 accumulate).
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import dsa_inputs as I
+from oracle import dsa_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import dsa_sparse_attention_lightning_amd as dsa
+    from gpu_util import DEV, DraftDev, to_dev, bits_to_dev
+
+ATTN_TOL = 1e-2
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+# ----------------------------------------------------------------------------
+# a1 indexer
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("case", [
+    dict(lens=[512], H_I=4, D_I=32, page=64, shuffle=False, R=1),          # tiny shape
+    dict(lens=[3001, 1500], H_I=64, D_I=128, page=64, shuffle=True, R=1),  # ragged, paged
+    dict(lens=[777], H_I=20, D_I=64, page=16, shuffle=True, R=3),          # odd heads, 3 rows
+    dict(lens=[2048], H_I=64, D_I=128, page=64, shuffle=False, R=8),       # verify-pass rows
+])
+def test_index_scores_exact(case):
+    log("index_scores", case)
+    d = I.draft_inputs(7, case["lens"], H_I=case["H_I"], D_I=case["D_I"], H_q=4, H_kv=4, D_qk=64,
+                       D_v=64, k=64, R=case["R"], page=case["page"], shuffle_pages=case["shuffle"],
+                       integer_indexer=True)
+    row_len = d.row_len.copy()
+    if case["R"] > 1:   # rows see different prefixes
+        for r in range(case["R"]):
+            row_len[:, r] = np.maximum(d.lens - 37 * r, 0)
+    dd = DraftDev(d)
+    rl = to_dev(row_len)
+    ld = dd.ld + 5
+    out = torch.full((d.B, d.R, ld), -7.0, device=DEV)
+    dsa.index_scores(dd.q_index, dd.w, dd.kidx, dd.bt, rl, page=d.page, out=out)
+    got = out.cpu().numpy()
+    for b in range(d.B):
+        ref = O.index_scores(d.q_index[b], d.w[b].astype(np.float64), d.keys[b], row_len[b])
+        for r in range(d.R):
+            n = row_len[b, r]
+            np.testing.assert_array_equal(got[b, r, :n], ref[r, :n].astype(np.float32))
+            assert np.all(got[b, r, n:] == -7.0)   # untouched beyond row_len
+
+
+def test_index_scores_bf16_normal_bound():
+    """Continuous N(0,1) bf16 inputs: error within the fp32 accumulation bound."""
+    d = I.draft_inputs(8, [4000], H_I=64, D_I=128, H_q=4, H_kv=4, D_qk=64, D_v=64, k=64)
+    dd = DraftDev(d)
+    got = dsa.index_scores(dd.q_index, dd.w, dd.kidx, dd.bt, dd.row_len, page=d.page).cpu().numpy()
+    ref = O.index_scores(d.q_index[0], d.w[0].astype(np.float64), d.keys[0], d.row_len[0])[0]
+    bound = 2.0**-16 * (d.w[0, 0].astype(np.float64) @ np.abs(d.q_index[0, 0]) @ np.abs(d.keys[0][:4000]).T)
+    err = np.abs(got[0, 0, :4000] - ref[:4000])
+    assert np.all(err <= bound + 1e-30), err.max()
+
+
+# ----------------------------------------------------------------------------
+# a2 top-k
+# ----------------------------------------------------------------------------
+def _topk_case(scores, lens, k):
+    B = len(lens)
+    ld = scores.shape[1]
+    s = to_dev(scores.astype(np.float32).reshape(B, 1, ld))
+    rl = to_dev(np.asarray(lens, np.int32).reshape(B, 1))
+    got = dsa.topk(s, rl, k).cpu().numpy()[:, 0]
+    for b in range(B):
+        ref = O.topk(scores[b].astype(np.float32).astype(np.float64), lens[b], k)
+        np.testing.assert_array_equal(got[b], ref, err_msg=f"row {b} L={lens[b]} k={k}")
+
+
+@pytest.mark.parametrize("name", ["normal", "ties", "allequal", "zeros_signed", "small_L", "k_ge_L",
+                                  "negative", "wide_range"])
+def test_topk_exact(name):
+    rng = np.random.default_rng(abs(hash(name)) % 2**32)
+    k = 2048
+    lens = [20000, 9000, 4097, 2048, 2049, 1, 0, 130000]
+    ld = max(lens) + 3
+    s = rng.standard_normal((len(lens), ld)).astype(np.float32)
+    if name == "ties":
+        s = rng.integers(-20, 20, (len(lens), ld)).astype(np.float32)
+    elif name == "allequal":
+        s[:] = 1.5
+    elif name == "zeros_signed":
+        s = np.where(rng.random((len(lens), ld)) < 0.5, np.float32(0.0), np.float32(-0.0))
+        s[:, ::7] = 1.0
+    elif name == "small_L":
+        lens = [5, 64, 100, 2047]
+        k = 64
+    elif name == "k_ge_L":
+        lens = [2048, 100, 1000]
+    elif name == "negative":
+        s = -np.abs(s) - 1.0
+    elif name == "wide_range":
+        s = (rng.standard_normal((len(lens), ld)) * 10.0 ** rng.integers(-30, 30, (len(lens), ld))).astype(np.float32)
+    log("topk", name, lens, k)
+    _topk_case(s[: len(lens)], lens, k)
+
+
+@pytest.mark.parametrize("k", [1, 7, 64, 2048, 8192])
+def test_topk_various_k(k):
+    rng = np.random.default_rng(k)
+    lens = [50000, 8191, 300]
+    s = rng.integers(0, 1000, (3, 50000)).astype(np.float32)
+    _topk_case(s, lens, k)
+
+
+# ----------------------------------------------------------------------------
+# a3 sparse attention
+# ----------------------------------------------------------------------------
+def _attn_vs_oracle(d, dd, idx_np, step=0, tol=ATTN_TOL, out_check=True):
+    idx = to_dev(idx_np.astype(np.int32))
+    out, lse = dsa.sparse_attn(dd.q[step][:, None], dd.k, dd.v, dd.bt, idx, page=d.page,
+                               D_v=d.D_v, sm_scale=d.sm_scale)
+    out = out.cpu().numpy()[:, 0]
+    lse = lse.cpu().numpy()[:, 0]
+    err = 0.0
+    for b in range(d.B):
+        o_ref, lse_ref = O.sparse_attn(d.q[step, b], d.K[b], d.V[b], idx_np[b], d.sm_scale)
+        err = max(err, np.abs(out[b] - o_ref).max())
+        fin = np.isfinite(lse_ref)
+        np.testing.assert_array_equal(np.isfinite(lse[b]), fin)
+        if fin.any():
+            assert np.abs(lse[b][fin] - lse_ref[fin]).max() < tol
+    assert err <= tol, err
+    return out, lse, err
+
+
+@pytest.mark.parametrize("case", [
+    dict(lens=[512], H=4, Hkv=4, D=64, k=64, shuffle=False),
+    dict(lens=[5000, 3001], H=64, Hkv=64, D=128, k=2048, shuffle=True),
+    dict(lens=[900], H=8, Hkv=2, D=128, k=300, shuffle=True),
+    dict(lens=[1200, 640], H=16, Hkv=4, D=64, k=1000, shuffle=True),
+    dict(lens=[100], H=6, Hkv=3, D=64, k=64, shuffle=False),
+])
+def test_sparse_attn_matches_oracle(case):
+    log("sparse_attn", case)
+    d = I.draft_inputs(11, case["lens"], H_I=4, D_I=32, H_q=case["H"], H_kv=case["Hkv"], D_qk=case["D"],
+                       D_v=case["D"], k=case["k"], page=64, shuffle_pages=case["shuffle"], G=2)
+    dd = DraftDev(d)
+    rng = np.random.default_rng(5)
+    idx = np.full((d.B, d.k), -1, np.int64)
+    for b in range(d.B):
+        n = min(d.k, int(d.lens[b]))
+        idx[b, :n] = np.sort(rng.choice(int(d.lens[b]), n, replace=False))
+    _attn_vs_oracle(d, dd, idx)
+    # set semantics: shuffled order and scattered -1 entries give the same result
+    idx2 = idx.copy()
+    for b in range(d.B):
+        rng.shuffle(idx2[b])
+    _attn_vs_oracle(d, dd, idx2)
+
+
+def test_sparse_attn_k_covers_context_equals_dense():
+    d = I.draft_inputs(12, [700, 333], H_I=4, D_I=32, H_q=8, H_kv=8, D_qk=128, D_v=128, k=1024, G=1)
+    dd = DraftDev(d)
+    idx = np.full((d.B, d.k), -1, np.int64)
+    for b in range(d.B):
+        idx[b, : d.lens[b]] = np.arange(d.lens[b])
+    out, lse, _ = _attn_vs_oracle(d, dd, idx)
+    for b in range(d.B):
+        o_dense, l_dense = O.dense_attn(d.q[0, b], d.K[b], d.V[b], d.lens[b], d.sm_scale)
+        assert np.abs(out[b] - o_dense).max() <= ATTN_TOL
+        assert np.abs(lse[b] - l_dense).max() <= ATTN_TOL
+
+
+def test_sparse_attn_empty_and_single():
+    d = I.draft_inputs(13, [300], H_I=4, D_I=32, H_q=4, H_kv=4, D_qk=64, D_v=64, k=64, G=1)
+    dd = DraftDev(d)
+    idx = np.full((1, 64), -1, np.int64)
+    out, lse = dsa.sparse_attn(dd.q[0][:, None], dd.k, dd.v, dd.bt, to_dev(idx.astype(np.int32)),
+                               page=d.page, sm_scale=d.sm_scale)
+    assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+    idx[0, 17] = 123
+    out, _, _ = _attn_vs_oracle(d, dd, idx)
+    np.testing.assert_allclose(out[0], d.V[0][123], atol=1e-6)
+
+
+# ----------------------------------------------------------------------------
+# the draft block: IndexShare + KVShare on the tiny configuration
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("poison", [False, True])
+def test_draft_block_tiny(poison):
+    w = I.WORKLOADS["tiny"]
+    d = I.draft_inputs(w["seed"], w["lens"], H_I=w["H_I"], D_I=w["D_I"], H_q=w["H_q"], H_kv=w["H_kv"],
+                       D_qk=w["D_qk"], D_v=w["D_v"], k=w["k"], G=w["G"], integer_indexer=True,
+                       poison=poison)
+    dd = DraftDev(d)
+    scores = dsa.index_scores(dd.q_index, dd.w, dd.kidx, dd.bt, dd.row_len, page=d.page, ld=dd.ld)
+    idx = dsa.topk(scores, dd.row_len, d.k)[:, 0]
+    idx_before = idx.clone()
+    ref_idx, ref_o, ref_lse = O.draft_block(d.q_index[0, 0], d.w[0, 0], d.keys[0], d.lens[0], d.k,
+                                            d.q[:, 0], d.K[0], d.V[0], d.sm_scale)
+    np.testing.assert_array_equal(idx.cpu().numpy()[0], ref_idx)
+    assert np.all(ref_idx < d.lens[0])
+    outs = []
+    for j in range(d.G):
+        o, lse = dsa.sparse_attn(dd.q[j][:, None], dd.k, dd.v, dd.bt, idx, page=d.page, sm_scale=d.sm_scale)
+        o = o.cpu().numpy()[0, 0]
+        assert np.all(np.isfinite(o))
+        assert np.abs(o - ref_o[j]).max() <= ATTN_TOL
+        outs.append(o)
+    assert torch.equal(idx, idx_before)      # steps 2..7 reuse the step-1 indices unchanged
+    if poison:
+        clean = I.draft_inputs(w["seed"], w["lens"], H_I=w["H_I"], D_I=w["D_I"], H_q=w["H_q"], H_kv=w["H_kv"],
+                               D_qk=w["D_qk"], D_v=w["D_v"], k=w["k"], G=w["G"], integer_indexer=True)
+        cd = DraftDev(clean)
+        for j in range(d.G):
+            o, _ = dsa.sparse_attn(cd.q[j][:, None], cd.k, cd.v, cd.bt, idx, page=d.page, sm_scale=d.sm_scale)
+            np.testing.assert_array_equal(o.cpu().numpy()[0, 0], outs[j])
+
+
+# ----------------------------------------------------------------------------
+# a4 verification
+# ----------------------------------------------------------------------------
+def _verify_case(vi, use_philox, tol_margin=1e-5):
+    B, G, V = vi.shape
+    ua, us = I.verify_uniforms(vi.seed, vi.offset, B, G)
+    tl = to_dev(vi.target_logits)
+    dl = to_dev(vi.draft_logits)
+    dr = to_dev(vi.drafts)
+    diag = torch.empty((B, G + 1, 4), device=DEV)
+    if use_philox:
+        n, em = dsa.spec_verify(tl, dl, dr, seed=vi.seed, offset=vi.offset, diag=diag)
+    else:
+        uni = np.zeros((B, G + 1, 2), np.float32)
+        uni[:, :G, 0] = ua
+        uni[:, :, 1] = us
+        n, em = dsa.spec_verify(tl, dl, dr, uniforms=to_dev(uni), diag=diag)
+    n = n.cpu().numpy()
+    em = em.cpu().numpy()
+    dg = diag.cpu().numpy()
+    ref_n, ref_em, res = O.spec_verify(vi.target_logits, vi.draft_logits, vi.drafts, ua, us)
+    near = 0
+    for b in range(B):
+        r = res[b]
+        j = min(n[b], ref_n[b])
+        # uniforms actually used match the generator bit for bit
+        np.testing.assert_array_equal(dg[b, : j + 1 if j < G else G, 2], ua[b, : j + 1 if j < G else G])
+        assert dg[b, n[b], 3] == us[b, n[b]]
+        if n[b] != ref_n[b]:
+            jj = min(n[b], ref_n[b])
+            assert r["accept_margin"][jj] < tol_margin, (b, n[b], ref_n[b], r["accept_margin"][jj])
+            near += 1
+            continue
+        np.testing.assert_array_equal(em[b, : n[b]], vi.drafts[b, : n[b]])
+        assert np.all(em[b, n[b] + 1:] == -1)
+        if em[b, n[b]] != ref_em[b, n[b]]:
+            assert r["sample_margin"] < tol_margin, (b, em[b, n[b]], ref_em[b, n[b]], r["sample_margin"])
+            near += 1
+        # probabilities of the drafted tokens as the kernel used them
+        m = n[b] + (1 if n[b] < G else 0)
+        np.testing.assert_allclose(dg[b, :m, 0], r["p_draft"][:m], rtol=2e-5, atol=1e-30)
+        np.testing.assert_allclose(dg[b, :m, 1], r["q_draft"][:m], rtol=2e-5, atol=1e-30)
+    log(f"verify B={B} G={G} V={V}: mean n={n.mean():.3f}, near-margin cases={near}")
+    return n, em, near
+
+
+@pytest.mark.parametrize("use_philox", [False, True])
+def test_spec_verify_tiny(use_philox):
+    w = I.WORKLOADS["tiny"]
+    vi = I.verify_inputs(w["seed"], 1, w["G"], w["vocab"], w["logit_std"], independent=True)
+    n, em, near = _verify_case(vi, use_philox)
+    assert near == 0
+
+
+@pytest.mark.parametrize("std", [0.5, 2.0, 6.0])
+def test_spec_verify_many_sequences(std):
+    vi = I.verify_inputs(int(std * 10), 64, 7, 5003, std)        # V not a multiple of 4
+    _, _, near = _verify_case(vi, True)
+    assert near <= 1
+    vi = I.verify_inputs(int(std * 10) + 1, 16, 7, 151552, std)
+    _, _, near = _verify_case(vi, True)
+    assert near <= 1
+
+
+def test_spec_verify_special_cases():
+    rng = np.random.default_rng(3)
+    B, G, V = 8, 7, 2048
+    tl = (rng.standard_normal((B, G + 1, V)) * 2).astype(np.float32)
+    # p == q: everything accepted, bonus from p_G
+    vi = I.VerifyInputs(tl, tl[:, :G].copy(), rng.integers(0, V, (B, G)).astype(np.int32), 9, 0)
+    n, em, _ = _verify_case(vi, True)
+    assert np.all(n == G)
+    # draft mass only where target is -inf: always rejected at the first position
+    tl2 = tl.copy()
+    tl2[:, :, V // 2:] = -np.inf
+    dl2 = np.full((B, G, V), -np.inf, np.float32)
+    dl2[:, :, V // 2:] = 0.0
+    dr = rng.integers(V // 2, V, (B, G)).astype(np.int32)
+    n, em, _ = _verify_case(I.VerifyInputs(tl2, dl2, dr, 10, 0), True)
+    assert np.all(n == 0) and np.all(em[:, 0] < V // 2)

@@ -1,0 +1,269 @@
+"""Benchmark of the DSA draft-and-verify hot path on one MI355X.
+
+One step = the whole path over one batch of synthetic input:
+  indexer scores (draft step 1) -> top-k -> sparse attention for the G = 7
+  draft steps reusing the step-1 indices (IndexShare) -> rejection-sampling
+  verification of the drafted chain over the vocabulary.
+
+Default workload: single-sequence decode at context 32,768 (indexer 64 heads
+x 128 bf16, one shared index key per position; top-k 2048; attention 64
+heads x 128 bf16 per-head KV; 7 draft steps; verification of 7 drafts + bonus
+over a 151,552-token vocabulary with target logits N(0, 2^2) and draft =
+target + N(0, 1)).  Inputs are seeded synthetic data already resident in HBM.
+
+Prints one JSON line: value = draft-step sparse-attention context tokens/s
+(G * context / step time), plus a roofline object for the dominant kernel
+(sparse attention, HBM-bound) and the CPU oracle timed on the host cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode_32k", choices=["decode_32k"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 256 MiB device copy (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def calibrate_copy():
+    import torch
+    n = 256 * 1024 * 1024
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_each_way": n, "launches": 5}), flush=True)
+
+
+def build_workload(name):
+    from dsa_inputs import device as DI
+    if name == "decode_32k":
+        d = DI.draft_inputs(1, [32768], H_I=64, D_I=128, H_q=64, H_kv=64, D_qk=128, D_v=128, k=2048, G=7)
+        v = DI.verify_inputs(101, 1, 7, 151552, 2.0)
+        return d, v
+    raise ValueError(name)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path).", file=sys.stderr)
+        sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+    import numpy as np
+    import torch
+
+    import dsa_sparse_attention_lightning_amd as dsa
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    d, v = build_workload(args.workload)
+    B, G, k = d.B, d.G, d.k
+    stream = torch.cuda.current_stream()
+
+    # persistent outputs and workspaces (no allocation inside the timed loop)
+    scores = torch.empty((B, 1, d.ld), dtype=torch.float32, device=dev)
+    idx = torch.empty((B, 1, k), dtype=torch.int32, device=dev)
+    topk_ws = torch.empty(max(1, dsa.topk_workspace_size(B, 1, d.ld, k)), dtype=torch.uint8, device=dev)
+    outs = torch.empty((G, B, 1, d.H_q, d.D_v), dtype=torch.float32, device=dev)
+    lses = torch.empty((G, B, 1, d.H_q), dtype=torch.float32, device=dev)
+    attn_ws = torch.zeros(max(1, dsa.sparse_attn_workspace_size(B, 1, d.H_q, d.H_kv, d.D_qk, d.D_v, k)),
+                          dtype=torch.uint8, device=dev)
+    Bv, Gv, V = v.draft_logits.shape
+    acc_len = torch.empty(Bv, dtype=torch.int32, device=dev)
+    emitted = torch.empty((Bv, Gv + 1), dtype=torch.int32, device=dev)
+    ver_ws = torch.empty(max(1, dsa.spec_verify_workspace_size(Bv, Gv, V)), dtype=torch.uint8, device=dev)
+
+    # The step is captured as three HIP graphs replayed back to back:
+    #   draft_first = indexer + top-k (draft step 1), attn = the G sparse-
+    #   attention launches (IndexShare), verify = rejection sampling.
+    # Events between the replays time each phase on the launch stream.
+    def draft_first():
+        dsa.index_scores(d.q_index, d.w, d.kidx, d.block_table, d.row_len, page=d.page, out=scores)
+        dsa.topk(scores, d.row_len, k, out=idx, workspace=topk_ws)
+
+    def attn_steps():
+        for j in range(G):
+            dsa.sparse_attn(d.q[j][:, None], d.k_cache, d.v_cache, d.block_table, idx[:, 0], page=d.page,
+                            D_v=d.D_v, sm_scale=d.sm_scale, out=outs[j], lse=lses[j], workspace=attn_ws)
+
+    def verify():
+        dsa.spec_verify(v.target_logits, v.draft_logits, v.drafts, seed=v.seed, offset=v.offset,
+                        accepted_len=acc_len, emitted=emitted, workspace=ver_ws)
+
+    phases = [("draft_first", draft_first), ("attn", attn_steps), ("verify", verify)]
+    for _, fn in phases:          # eager warm-up (loads code objects, checks arguments)
+        fn()
+    torch.cuda.synchronize()
+    graphs = []
+    cap = torch.cuda.Stream()
+    for _, fn in phases:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            fn()
+        graphs.append(g)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        for i, g in enumerate(graphs):
+            if ev is not None:
+                ev[i].record(stream)
+            g.replay()
+        if ev is not None:
+            ev[len(graphs)].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    names = [n for n, _ in phases]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    per = {n: [] for n in names}
+    for s in range(args.steps):
+        for i, n in enumerate(names):
+            per[n].append(evs[s][i].elapsed_time(evs[s][i + 1]))
+    kern_us = {n: 1e3 * float(np.mean(x)) for n, x in per.items()}
+    attn_us = kern_us["attn"] / G
+
+    L_total = sum(d.lens)
+    n_sel = sum(min(k, L) for L in d.lens)
+    # algorithmic bytes per launch
+    attn_bytes = (n_sel * d.H_kv * (d.D_qk + d.D_v) * 2 + B * d.H_q * d.D_qk * 2 + B * k * 4
+                  + B * d.H_q * d.D_v * 4 + B * d.H_q * 4)
+    idx_bytes = L_total * d.D_I * 2 + L_total * 4 + B * d.H_I * (d.D_I * 2 + 4)
+    idx_flops = 2.0 * L_total * d.H_I * d.D_I
+    topk_bytes = L_total * 4 + B * k * 4
+    ver_bytes = Bv * (2 * Gv + 1) * V * 4
+    achieved = attn_bytes / (attn_us * 1e-6) / 1e9
+
+    value = G * L_total / (ms_per_step * 1e-3)
+    result = {
+        "metric": "draft-step sparse-attn context tokens/s + verified positions/s; % of HBM roofline",
+        "value": value,
+        "unit": "context tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode_32k: 1 sequence, context 32768, indexer 64x128, top-k 2048, "
+                               "MHA 64x128 paged 64, 7 draft steps (IndexShare), verify 7+1 x vocab 151552",
+                   "global_batch": B, "seq_len": L_total, "parallelism": "none (1 GPU)"},
+        "verified_positions_per_s": Bv * (Gv + 1) / (ms_per_step * 1e-3),
+        "roofline": {"bound": "hbm", "kernel": "mha_attn_kernel (dsa_sparse_attn)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "bytes_per_launch": attn_bytes, "avg_launch_us": attn_us,
+                     "timing": "HIP events around the graph of the G attention launches in each timed step, "
+                               "divided by G (includes the split-k combine kernel)"},
+        "phases_us": kern_us,
+        "phases_roofline": {
+            "draft_first (indexer + top-k)": {"bytes": idx_bytes + topk_bytes,
+                                              "GBps": (idx_bytes + topk_bytes) / kern_us["draft_first"] / 1e3},
+            "verify": {"bytes": ver_bytes, "GBps": ver_bytes / kern_us["verify"] / 1e3},
+        },
+        "graph": "each step replays three HIP graphs (draft_first, attn, verify) on one stream",
+        "accepted_len": acc_len.cpu().tolist(),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(d, v, scores, idx, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(d, v, scores, idx, budget_s):
+    """Times the float64 CPU oracle on one full step of the same workload
+    (draft block + verification of the same sequence), repeated until the
+    time budget is spent; same unit as the GPU value."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+
+    from oracle import dsa_oracle as O
+    import dsa_inputs as I
+
+    def f64(t):
+        return t.float().cpu().numpy().astype(np.float64)
+
+    L = d.lens[0]
+    t_prep = time.perf_counter()
+    pages = d.block_table[0].cpu().numpy()
+    order = pages[: (L + d.G + d.page - 1) // d.page]
+    keys = f64(d.kidx[order].reshape(-1, d.D_I))
+    K = f64(d.k_cache[order].reshape(-1, d.H_kv, d.D_qk))
+    V = f64(d.v_cache[order].reshape(-1, d.H_kv, d.D_v))
+    q_idx = f64(d.q_index[0, 0])
+    w = d.w[0, 0].double().cpu().numpy()
+    q = f64(d.q[:, 0])
+    tl = v.target_logits[0].cpu().numpy()
+    dl = v.draft_logits[0].cpu().numpy()
+    dr = v.drafts[0].cpu().numpy()
+    ua, us = I.verify_uniforms(v.seed, v.offset, 1, d.G)
+    prep = time.perf_counter() - t_prep
+
+    threads = sum(p.get("num_threads", 0) for p in threadpool_info() if p.get("user_api") == "blas") or 1
+    reps, spent = 0, 0.0
+    while spent < budget_s and reps < 50:
+        t0 = time.perf_counter()
+        O.draft_block(q_idx, w, keys, L, d.k, q, K, V, d.sm_scale)
+        O.spec_verify_seq(tl, dl, dr, ua[0], us[0])
+        spent += time.perf_counter() - t0
+        reps += 1
+    per_step = spent / reps
+    return {"value": d.G * L / per_step, "unit": "context tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} full steps of the same workload (1 sequence, context {L}: indexer, top-k, "
+                      f"{d.G} attention steps, verify over vocab {v.draft_logits.shape[-1]}); "
+                      f"float64 NumPy, {per_step:.3f} s/step, input conversion {prep:.1f} s not timed",
+            "cpu_model": _cpu_model()}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+if __name__ == "__main__":
+    main()

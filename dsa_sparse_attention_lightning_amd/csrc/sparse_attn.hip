@@ -28,6 +28,18 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 
+// Split-k plan: aim for about kTargetGroups workgroups, each with at least
+// kMinTokens selected tokens (tunable at build time).
+#ifndef DSA_ATTN_TARGET_WGS
+#define DSA_ATTN_TARGET_WGS 1024
+#endif
+#ifndef DSA_ATTN_MIN_TOKENS
+#define DSA_ATTN_MIN_TOKENS 32
+#endif
+#ifndef DSA_ATTN_UNROLL
+#define DSA_ATTN_UNROLL 8
+#endif
+
 struct AttnArgs {
   const uint16_t* q;
   const uint16_t* kc;
@@ -46,37 +58,99 @@ struct AttnArgs {
   int tok_per_split;
 };
 
+constexpr int kMaxTokPerSplit = 1024;
+
 // ---------------------------------------------------------------------------
 // Per-head KV gather kernel
 // ---------------------------------------------------------------------------
+// Loads of U tokens' K and V pieces.  Loads are unconditional (invalid
+// tokens and padding heads read row 0 / the last head, and are ignored by
+// consume) so that the compiler keeps all of them in flight at once.
+template <int D, int GQ, int U>
+__device__ __forceinline__ void issue_loads(const AttnArgs& a, const int64_t* s_off, int i, int ntok,
+                                            size_t lane_off, uint4 (&kr)[U], uint4 (&vr)[U]) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int li = min(i + u * kWaves, ntok - 1);
+    const int64_t off = max(s_off[li], (int64_t)0);
+    kr[u] = *reinterpret_cast<const uint4*>(a.kc + off + lane_off);
+    vr[u] = *reinterpret_cast<const uint4*>(a.vc + off + lane_off);
+  }
+}
+
+template <int D, int GQ, int U>
+__device__ __forceinline__ void consume(const int64_t* s_off, int i, int ntok, float scale_log2,
+                                        const float (&qv)[GQ][8], float (&m)[GQ], float (&l)[GQ],
+                                        float (&acc)[GQ][8], const uint4 (&kr)[U], const uint4 (&vr)[U]) {
+  constexpr int SLOT = D / 8;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int li = i + u * kWaves;
+    if (li >= ntok || s_off[li] < 0) continue;   // wave-uniform
+    float kf[8], vf[8];
+    kf[0] = bf16_lo(kr[u].x); kf[1] = bf16_hi(kr[u].x);
+    kf[2] = bf16_lo(kr[u].y); kf[3] = bf16_hi(kr[u].y);
+    kf[4] = bf16_lo(kr[u].z); kf[5] = bf16_hi(kr[u].z);
+    kf[6] = bf16_lo(kr[u].w); kf[7] = bf16_hi(kr[u].w);
+    vf[0] = bf16_lo(vr[u].x); vf[1] = bf16_hi(vr[u].x);
+    vf[2] = bf16_lo(vr[u].y); vf[3] = bf16_hi(vr[u].y);
+    vf[4] = bf16_lo(vr[u].z); vf[5] = bf16_hi(vr[u].z);
+    vf[6] = bf16_lo(vr[u].w); vf[7] = bf16_hi(vr[u].w);
+#pragma unroll
+    for (int j = 0; j < GQ; ++j) {
+      float dt = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dt = fmaf(qv[j][e], kf[e], dt);
+      dt = group_sum_dpp<SLOT>(dt);
+      const float sc = dt * scale_log2;
+      const float mn = fmaxf(m[j], sc);
+      const float corr = fast_exp2(m[j] - mn);
+      const float p = fast_exp2(sc - mn);
+      l[j] = l[j] * corr + p;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[j][e] = fmaf(p, vf[e], acc[j][e] * corr);
+      m[j] = mn;
+    }
+  }
+}
+
 template <int D, int GQ, int U>
 __global__ __launch_bounds__(kThreads) void mha_attn_kernel(AttnArgs a) {
   constexpr int SLOT = D / 8;            // lanes per KV row
   constexpr int NSLOT = 64 / SLOT;       // KV heads per wave
-  __shared__ float s_ml[kWaves][NSLOT * GQ][2];
-  __shared__ float s_o[kWaves][NSLOT * GQ][D];
+  constexpr int NH = NSLOT * GQ;         // query heads per workgroup
+  __shared__ int64_t s_off[kMaxTokPerSplit];
+  __shared__ float s_ml[kWaves][NH][2];
+  __shared__ float s_o[kWaves][NH][D];
 
   const int split = blockIdx.x;
   const int hg = blockIdx.y;                         // KV head group
   const int bs = blockIdx.z;                         // b * S_q + s
   const int b = bs / a.S_q;
   const int s = bs % a.S_q;
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
   const int slot = lane / SLOT;
   const int sub = lane % SLOT;
   const int g = hg * NSLOT + slot;                   // KV head of this lane
   const bool head_ok = g < a.H_kv;
 
-  // query values: 8 dims x GQ heads
+  // Row offsets of this split's tokens, resolved through the page table once.
+  const int32_t* idx = a.idx + ((size_t)b * a.idx_rows + (a.idx_rows > 1 ? s : 0)) * a.k;
+  const int32_t* bt = a.bt + (size_t)b * a.max_pages;
+  const int t_lo = split * a.tok_per_split;
+  const int ntok = min(a.tok_per_split, a.k - t_lo);
+  for (int i = tid; i < ntok; i += kThreads) {
+    const int t = idx[t_lo + i];
+    s_off[i] = t >= 0 ? (int64_t)bt[t / a.page] * a.page_stride + (int64_t)(t % a.page) * a.row_stride : -1;
+  }
+
   float qv[GQ][8];
 #pragma unroll
   for (int j = 0; j < GQ; ++j) {
     uint4 raw = make_uint4(0, 0, 0, 0);
-    if (head_ok) {
-      const int h = g * GQ + j;
-      raw = *reinterpret_cast<const uint4*>(a.q + ((size_t)bs * a.H_q + h) * D + sub * 8);
-    }
+    if (head_ok) raw = *reinterpret_cast<const uint4*>(a.q + ((size_t)bs * a.H_q + g * GQ + j) * D + sub * 8);
     qv[j][0] = bf16_lo(raw.x); qv[j][1] = bf16_hi(raw.x);
     qv[j][2] = bf16_lo(raw.y); qv[j][3] = bf16_hi(raw.y);
     qv[j][4] = bf16_lo(raw.z); qv[j][5] = bf16_hi(raw.z);
@@ -90,58 +164,23 @@ __global__ __launch_bounds__(kThreads) void mha_attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
   }
+  __syncthreads();
 
-  const int32_t* idx = a.idx + ((size_t)b * a.idx_rows + (a.idx_rows > 1 ? s : 0)) * a.k;
-  const int32_t* bt = a.bt + (size_t)b * a.max_pages;
-  const int t_lo = split * a.tok_per_split;
-  const int t_hi = min(t_lo + a.tok_per_split, a.k);
-  const size_t lane_off = (size_t)g * a.head_stride + sub * 8;
-
-  for (int i0 = t_lo + wave; i0 < t_hi; i0 += kWaves * U) {
-    uint4 kr[U], vr[U];
-    bool ok[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = i0 + u * kWaves;
-      const int t = i < t_hi ? idx[i] : -1;
-      ok[u] = t >= 0;
-      kr[u] = make_uint4(0, 0, 0, 0);
-      vr[u] = make_uint4(0, 0, 0, 0);
-      if (ok[u] && head_ok) {
-        const size_t row = (size_t)bt[t / a.page] * a.page_stride + (size_t)(t % a.page) * a.row_stride;
-        kr[u] = *reinterpret_cast<const uint4*>(a.kc + row + lane_off);
-        vr[u] = *reinterpret_cast<const uint4*>(a.vc + row + lane_off);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (!ok[u]) continue;   // wave-uniform
-      float kf[8], vf[8];
-      kf[0] = bf16_lo(kr[u].x); kf[1] = bf16_hi(kr[u].x);
-      kf[2] = bf16_lo(kr[u].y); kf[3] = bf16_hi(kr[u].y);
-      kf[4] = bf16_lo(kr[u].z); kf[5] = bf16_hi(kr[u].z);
-      kf[6] = bf16_lo(kr[u].w); kf[7] = bf16_hi(kr[u].w);
-      vf[0] = bf16_lo(vr[u].x); vf[1] = bf16_hi(vr[u].x);
-      vf[2] = bf16_lo(vr[u].y); vf[3] = bf16_hi(vr[u].y);
-      vf[4] = bf16_lo(vr[u].z); vf[5] = bf16_hi(vr[u].z);
-      vf[6] = bf16_lo(vr[u].w); vf[7] = bf16_hi(vr[u].w);
-#pragma unroll
-      for (int j = 0; j < GQ; ++j) {
-        float d = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) d = fmaf(qv[j][e], kf[e], d);
-#pragma unroll
-        for (int o = SLOT / 2; o >= 1; o >>= 1) d += __shfl_xor(d, o, 64);
-        const float sc = d * a.scale_log2;
-        const float mn = fmaxf(m[j], sc);
-        const float corr = fast_exp2(m[j] - mn);
-        const float p = fast_exp2(sc - mn);
-        l[j] = l[j] * corr + p;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[j][e] = fmaf(p, vf[e], acc[j][e] * corr);
-        m[j] = mn;
-      }
-    }
+  // Wave w takes local tokens w, w+4, ...; loads run one U-token stage ahead.
+  // padding heads (g >= H_kv) read the last real head; their results are dropped
+  const size_t lane_off = (size_t)min(g, a.H_kv - 1) * a.head_stride + sub * 8;
+  constexpr int STEP = kWaves * U;
+  uint4 kA[U], vA[U], kB[U], vB[U];
+  int i = wave;
+  issue_loads<D, GQ, U>(a, s_off, i, ntok, lane_off, kA, vA);
+  while (i < ntok) {
+    issue_loads<D, GQ, U>(a, s_off, i + STEP, ntok, lane_off, kB, vB);
+    consume<D, GQ, U>(s_off, i, ntok, a.scale_log2, qv, m, l, acc, kA, vA);
+    i += STEP;
+    if (i >= ntok) break;
+    issue_loads<D, GQ, U>(a, s_off, i + STEP, ntok, lane_off, kA, vA);
+    consume<D, GQ, U>(s_off, i, ntok, a.scale_log2, qv, m, l, acc, kB, vB);
+    i += STEP;
   }
 
   // merge the four waves (fixed order)
@@ -155,8 +194,7 @@ __global__ __launch_bounds__(kThreads) void mha_attn_kernel(AttnArgs a) {
     for (int e = 0; e < 8; ++e) s_o[wave][slot * GQ + j][sub * 8 + e] = acc[j][e];
   }
   __syncthreads();
-  // thread -> (head-in-group, dim) pairs
-  for (int p = threadIdx.x; p < NSLOT * GQ * D; p += kThreads) {
+  for (int p = tid; p < NH * D; p += kThreads) {
     const int hj = p / D;
     const int d = p % D;
     const int gg = hg * NSLOT + hj / GQ;
@@ -188,27 +226,61 @@ __global__ __launch_bounds__(kThreads) void mha_attn_kernel(AttnArgs a) {
   }
 }
 
-// Folds split partials in split order.  One wave per (b, s, h) row.
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part_o,
-                                                      const float* __restrict__ part_ml, int rows,
-                                                      int nsplit, int D, float* __restrict__ out,
-                                                      float* __restrict__ lse) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= rows) return;
+// Folds split partials in split order: one workgroup per (b, s, h) row.
+// Every thread issues all of its loads at once (one memory round trip); the
+// output dims are spread over threads and the splits over kCombineThreads/D
+// thread groups whose sums are added in group order.
+constexpr int kCombineThreads = 512;
+constexpr int kCombineMaxSplits = 128;
+
+template <int D>
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* __restrict__ part_o,
+                                                                  const float* __restrict__ part_ml,
+                                                                  int nsplit, float* __restrict__ out,
+                                                                  float* __restrict__ lse) {
+  constexpr int NG = kCombineThreads / D;
+  constexpr int PER = kCombineMaxSplits / NG;     // splits per thread group
+  __shared__ float s_m[kCombineMaxSplits], s_l[kCombineMaxSplits];
+  __shared__ float s_part[NG][D];
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int d = tid % D;
+  const int g = tid / D;
   const float* ml = part_ml + (size_t)row * nsplit * 2;
-  float M = -INFINITY;
-  for (int i = 0; i < nsplit; ++i) M = fmaxf(M, ml[2 * i]);
-  float Lsum = 0.f;
-  if (M != -INFINITY)
-    for (int i = 0; i < nsplit; ++i) Lsum += fast_exp2(ml[2 * i] - M) * ml[2 * i + 1];
-  for (int d = lane; d < D; d += 64) {
-    float O = 0.f;
-    if (M != -INFINITY)
-      for (int i = 0; i < nsplit; ++i) O += fast_exp2(ml[2 * i] - M) * part_o[((size_t)row * nsplit + i) * D + d];
-    out[(size_t)row * D + d] = M == -INFINITY ? 0.f : O / Lsum;
+  const float* po = part_o + (size_t)row * nsplit * D + d;
+  float ov[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int sp = g + u * NG;
+    ov[u] = sp < nsplit ? po[(size_t)sp * D] : 0.f;
   }
-  if (lane == 0 && lse) lse[row] = M == -INFINITY ? -INFINITY : (M + __log2f(Lsum)) * kLn2;
+  if (tid < nsplit) {
+    s_m[tid] = ml[2 * tid];
+    s_l[tid] = ml[2 * tid + 1];
+  }
+  __syncthreads();
+  float M = -INFINITY;
+  for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, s_m[sp]);
+  float O = 0.f;
+  if (M != -INFINITY) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int sp = g + u * NG;
+      if (sp < nsplit) O += fast_exp2(s_m[sp] - M) * ov[u];
+    }
+  }
+  s_part[g][d] = O;
+  __syncthreads();
+  if (g == 0) {
+    float Ot = 0.f;
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg) Ot += s_part[gg][d];
+    float Lsum = 0.f;
+    if (M != -INFINITY)
+      for (int sp = 0; sp < nsplit; ++sp) Lsum += fast_exp2(s_m[sp] - M) * s_l[sp];
+    out[(size_t)row * D + d] = M == -INFINITY ? 0.f : Ot / Lsum;
+    if (d == 0 && lse) lse[row] = M == -INFINITY ? -INFINITY : (M + __log2f(Lsum)) * kLn2;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -227,17 +299,20 @@ Plan make_plan(int B, int S_q, int H_q, int H_kv, int D_qk, int D_v, int k) {
   const int nslot = 64 / (D_qk / 8);
   p.head_groups = (H_kv + nslot - 1) / nslot;
   const long long base = (long long)B * S_q * p.head_groups;
-  constexpr int kMinTok = 32;
-  int ns = (int)((1024 + base - 1) / base);
+  constexpr int kMinTok = DSA_ATTN_MIN_TOKENS;
+  int ns = (int)((DSA_ATTN_TARGET_WGS + base - 1) / base);
   const int max_ns = (k + kMinTok - 1) / kMinTok;
   if (ns > max_ns) ns = max_ns;
+  const int min_ns = (k + kMaxTokPerSplit - 1) / kMaxTokPerSplit;
+  if (ns < min_ns) ns = min_ns;
+  if (ns > kCombineMaxSplits) ns = kCombineMaxSplits;
   if (ns < 1) ns = 1;
   p.tok_per_split = (k + ns - 1) / ns;
   p.nsplit = (k + p.tok_per_split - 1) / p.tok_per_split;
   const size_t rows = (size_t)B * S_q * H_q;
   if (p.nsplit > 1) {
     p.part_o_off = 0;
-    p.part_ml_off = align_up(rows * p.nsplit * D_v * sizeof(float), 256);
+    p.part_ml_off = p.part_o_off + align_up(rows * p.nsplit * D_v * sizeof(float), 256);
     p.ws_bytes = p.part_ml_off + align_up(rows * p.nsplit * 2 * sizeof(float), 256);
   }
   return p;
@@ -246,7 +321,7 @@ Plan make_plan(int B, int S_q, int H_q, int H_kv, int D_qk, int D_v, int k) {
 template <int D, int GQ>
 void launch_mha(const AttnArgs& a, const Plan& p, int B, hipStream_t s) {
   dim3 grid(p.nsplit, p.head_groups, B * a.S_q);
-  hipLaunchKernelGGL((mha_attn_kernel<D, GQ, 8>), grid, dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((mha_attn_kernel<D, GQ, DSA_ATTN_UNROLL>), grid, dim3(kThreads), 0, s, a);
 }
 
 }  // namespace
@@ -325,7 +400,11 @@ extern "C" dsa_status dsa_sparse_attn(const void* q, const void* k_cache, const 
   dsa_status st = launch_status("dsa_sparse_attn");
   if (st != DSA_OK || p.nsplit == 1) return st;
   const int rows = B * S_q * H_q;
-  hipLaunchKernelGGL(combine_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, a.part_o, a.part_ml, rows, p.nsplit,
-                     D_v, out, lse);
+  if (D_v == 64)
+    hipLaunchKernelGGL(combine_kernel<64>, dim3(rows), dim3(kCombineThreads), 0, s, a.part_o, a.part_ml, p.nsplit,
+                       out, lse);
+  else
+    hipLaunchKernelGGL(combine_kernel<128>, dim3(rows), dim3(kCombineThreads), 0, s, a.part_o, a.part_ml,
+                       p.nsplit, out, lse);
   return launch_status("dsa_sparse_attn(combine)");
 }

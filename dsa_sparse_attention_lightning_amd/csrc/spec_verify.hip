@@ -28,8 +28,6 @@ namespace {
 
 constexpr int kStatThreads = 256;
 constexpr int kChunk = 16384;        // logits per stats workgroup
-constexpr int kDecThreads = 512;
-constexpr int kDecWaves = kDecThreads / 64;
 constexpr int kTile = 256;           // logits per wave step (64 lanes x 4)
 constexpr int kMaxV = 1 << 20;
 constexpr int kMaxTiles = kMaxV / kTile;
@@ -112,19 +110,35 @@ __global__ __launch_bounds__(kStatThreads) void verify_stats_kernel(VerifyArgs a
   const int e0 = c * kChunk;
   const int e1 = min(e0 + kChunk, a.V);
   float m = -INFINITY, s = 0.f;
-  for (int e = e0 + threadIdx.x * 4; e < e1; e += kStatThreads * 4) {
-    const float4 x = load4(row, e, e1, a.vec);
-    const float m4 = fmaxf(fmaxf(x.x, x.y), fmaxf(x.z, x.w));
-    const float M = fmaxf(m, m4);
-    if (M == -INFINITY) continue;   // nothing but -inf logits so far
-    const float ML = M * kLog2e;
-    float t = s * fast_exp2(m * kLog2e - ML);
-    t += fast_exp2(x.x * kLog2e - ML);
-    t += fast_exp2(x.y * kLog2e - ML);
-    t += fast_exp2(x.z * kLog2e - ML);
-    t += fast_exp2(x.w * kLog2e - ML);
-    s = t;
-    m = M;
+  constexpr int kBatch = 4;                         // float4 loads in flight per thread
+  constexpr int kStride = kStatThreads * 4;
+  for (int e = e0 + threadIdx.x * 4; e < e1; e += kBatch * kStride) {
+    float4 x[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int ee = e + u * kStride;
+      if (a.vec) {
+        // unconditional aligned load (clamped inside the chunk), masked after
+        const float4 v = *reinterpret_cast<const float4*>(row + ((min(ee, e1 - 1)) & ~3));
+        x[u] = ee < e1 ? v : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+      } else {
+        x[u] = ee < e1 ? load4(row, ee, e1, false) : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const float m4 = fmaxf(fmaxf(x[u].x, x[u].y), fmaxf(x[u].z, x[u].w));
+      const float M = fmaxf(m, m4);
+      if (M == -INFINITY) continue;   // nothing but -inf logits so far
+      const float ML = M * kLog2e;
+      float t = s * fast_exp2(m * kLog2e - ML);
+      t += fast_exp2(x[u].x * kLog2e - ML);
+      t += fast_exp2(x[u].y * kLog2e - ML);
+      t += fast_exp2(x[u].z * kLog2e - ML);
+      t += fast_exp2(x[u].w * kLog2e - ML);
+      s = t;
+      m = M;
+    }
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
@@ -155,187 +169,308 @@ struct RowWeights {
   }
 };
 
+__device__ __forceinline__ float wave_incl_scan(float v) { return wave_incl_scan_dpp(v); }
+
+__device__ __forceinline__ void weights4(const RowWeights& rw, const float4& tv, const float4& dv, int e, int V,
+                                         float wv[4]) {
+  wv[0] = e + 0 < V ? rw.w(tv.x, dv.x) : 0.f;
+  wv[1] = e + 1 < V ? rw.w(tv.y, dv.y) : 0.f;
+  wv[2] = e + 2 < V ? rw.w(tv.z, dv.z) : 0.f;
+  wv[3] = e + 3 < V ? rw.w(tv.w, dv.w) : 0.f;
+}
+
 // Per-lane weights of 4 consecutive logits and their wave inclusive scan.
 __device__ __forceinline__ void tile_weights(const RowWeights& rw, int e, int V, bool vec, float wv[4],
                                              float& lane_incl) {
   const float4 tv = load4(rw.t, e, V, vec);
   float4 dv = make_float4(0.f, 0.f, 0.f, 0.f);
   if (rw.d) dv = load4(rw.d, e, V, vec);
-  wv[0] = e + 0 < V ? rw.w(tv.x, dv.x) : 0.f;
-  wv[1] = e + 1 < V ? rw.w(tv.y, dv.y) : 0.f;
-  wv[2] = e + 2 < V ? rw.w(tv.z, dv.z) : 0.f;
-  wv[3] = e + 3 < V ? rw.w(tv.w, dv.w) : 0.f;
-  float v = ((wv[0] + wv[1]) + wv[2]) + wv[3];
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const float u = __shfl_up(v, o, 64);
-    if (lane >= o) v += u;
-  }
-  lane_incl = v;
+  weights4(rw, tv, dv, e, V, wv);
+  lane_incl = wave_incl_scan(((wv[0] + wv[1]) + wv[2]) + wv[3]);
 }
 
-__global__ __launch_bounds__(kDecThreads) void verify_decide_kernel(VerifyArgs a) {
-  __shared__ float s_m[2 * kMaxG + 1], s_z[2 * kMaxG + 1];
-  __shared__ float s_tile[kMaxTiles];
-  __shared__ int s_jstar;
-  __shared__ float s_us;
-  __shared__ float s_W;
-  __shared__ int s_tile_pick;
-  __shared__ float s_x;
-  __shared__ int s_token;
+// Per-sequence decision record written by the chunk-0 workgroup of the mass
+// kernel: accepted length, sampling uniform and the sampled rows' softmax
+// statistics.
+struct Decision {
+  int jstar;
+  float us;
+  float mt, inv_zt, md, inv_zd;
+  int pad0, pad1;
+};
 
-  const int b = blockIdx.x;
+constexpr int kThreads2 = 256;
+constexpr int kWaves2 = kThreads2 / 64;
+constexpr int kMassChunk = 4096;              // logits per residual-mass workgroup
+constexpr int kChunkTiles = kMassChunk / kTile;   // 16
+constexpr int kMaxMassChunks = kMaxV / kMassChunk;
+
+struct VerifyWs {
+  float2* part;      // [B][2G+1][nchunks]
+  Decision* dec;     // [B]
+  float* cmass;      // [B][nmass]
+  int nmass;
+};
+
+// Folds chunk partials (chunk order) and runs the accept tests for sequence
+// b; results in shared memory.  Every workgroup of the sequence computes the
+// same values from the same inputs.
+__device__ void decide(const VerifyArgs& a, const VerifyWs& ws, int b, float* s_m, float* s_z, int* s_jstar,
+                       float* s_us, bool write_diag) {
   const int G = a.G, V = a.V;
   const int nrows = 2 * G + 1;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-
-  // 1. fold chunk partials in chunk order
   if (tid < nrows) {
-    const float2* p = a.part + ((size_t)b * nrows + tid) * a.nchunks;
+    const float2* p = ws.part + ((size_t)b * nrows + tid) * a.nchunks;
     float M = p[0].x, S = p[0].y;
     for (int c = 1; c < a.nchunks; ++c) ms_merge(M, S, p[c].x, p[c].y);
     s_m[tid] = M;
     s_z[tid] = S;
   }
   __syncthreads();
-
-  // 2. accept tests, one lane per draft position
-  if (wave == 0) {
+  if (tid < 64) {
     bool reject = false;
+    float p = NAN, q = NAN, ua = NAN;
     if (lane < G) {
       const int d = a.drafts[(size_t)b * G + lane];
       const float tv = a.tl[((size_t)b * (G + 1) + lane) * V + d];
       const float dv = a.dl[((size_t)b * G + lane) * V + d];
-      const float p = expf(tv - s_m[lane]) / s_z[lane];
-      const float q = expf(dv - s_m[G + 1 + lane]) / s_z[G + 1 + lane];
-      const float ua = a.uniforms ? a.uniforms[((size_t)b * (G + 1) + lane) * 2 + 0]
-                                  : philox_uniform(a.seed, a.offset, b, lane, 0);
+      p = expf(tv - s_m[lane]) / s_z[lane];
+      q = expf(dv - s_m[G + 1 + lane]) / s_z[G + 1 + lane];
+      ua = a.uniforms ? a.uniforms[((size_t)b * (G + 1) + lane) * 2 + 0] : philox_uniform(a.seed, a.offset, b, lane, 0);
       reject = !(ua * q < p);
-      if (a.diag) {
-        float* dg = a.diag + ((size_t)b * (G + 1) + lane) * 4;
-        dg[0] = p;
-        dg[1] = q;
-        dg[2] = ua;
-      }
     }
     const uint64_t rm = __ballot(reject);
     const int jstar = rm ? (__ffsll((long long)rm) - 1) : G;
+    const float us = a.uniforms ? a.uniforms[((size_t)b * (G + 1) + jstar) * 2 + 1]
+                                : philox_uniform(a.seed, a.offset, b, jstar, 1);
     if (lane == 0) {
-      s_jstar = jstar;
-      s_us = a.uniforms ? a.uniforms[((size_t)b * (G + 1) + jstar) * 2 + 1]
-                        : philox_uniform(a.seed, a.offset, b, jstar, 1);
+      *s_jstar = jstar;
+      *s_us = us;
     }
-    if (a.diag && lane <= G) {
+    if (write_diag && a.diag && lane <= G) {
       float* dg = a.diag + ((size_t)b * (G + 1) + lane) * 4;
-      if (lane > jstar || lane == G) {
-        dg[0] = NAN;
-        dg[1] = NAN;
-        dg[2] = NAN;
-      }
-      dg[3] = lane == jstar ? (a.uniforms ? a.uniforms[((size_t)b * (G + 1) + jstar) * 2 + 1]
-                                          : philox_uniform(a.seed, a.offset, b, jstar, 1))
-                            : NAN;
+      const bool used = lane <= jstar && lane < G;
+      dg[0] = used ? p : NAN;
+      dg[1] = used ? q : NAN;
+      dg[2] = used ? ua : NAN;
+      dg[3] = lane == jstar ? us : NAN;
     }
   }
   __syncthreads();
-  const int jstar = s_jstar;
+}
 
-  // 3. inverse-CDF draw from the residual (or bonus) row
+__device__ __forceinline__ RowWeights sampled_row(const VerifyArgs& a, int b, int jstar, const float* s_m,
+                                                  const float* s_z) {
   RowWeights rw;
-  rw.t = a.tl + ((size_t)b * (G + 1) + jstar) * V;
+  rw.t = a.tl + ((size_t)b * (a.G + 1) + jstar) * a.V;
   rw.mt = s_m[jstar];
   rw.inv_zt = 1.f / s_z[jstar];
   rw.d = nullptr;
   rw.md = 0.f;
   rw.inv_zd = 0.f;
-  if (jstar < G) {
-    rw.d = a.dl + ((size_t)b * G + jstar) * V;
-    rw.md = s_m[G + 1 + jstar];
-    rw.inv_zd = 1.f / s_z[G + 1 + jstar];
+  if (jstar < a.G) {
+    rw.d = a.dl + ((size_t)b * a.G + jstar) * a.V;
+    rw.md = s_m[a.G + 1 + jstar];
+    rw.inv_zd = 1.f / s_z[a.G + 1 + jstar];
   }
-  const int ntiles = (V + kTile - 1) / kTile;
-  for (int pass = 0; pass < 2; ++pass) {
-    for (int t = wave; t < ntiles; t += kDecWaves) {
-      float wv[4], incl;
-      tile_weights(rw, t * kTile + lane * 4, V, a.vec, wv, incl);
-      if (lane == 63) s_tile[t] = incl;
-    }
-    __syncthreads();
-    // scan of tile masses by wave 0, lanes own contiguous tile ranges
-    if (wave == 0) {
-      const int per = (ntiles + 63) / 64;
-      const int t0 = min(lane * per, ntiles);
-      const int t1 = min(t0 + per, ntiles);
-      float sum = 0.f;
-      for (int t = t0; t < t1; ++t) sum += s_tile[t];
-      float incl = sum;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const float u = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += u;
-      }
-      const float W = __shfl(incl, 63, 64);
-      const float x = s_us * W;
-      float run = incl - sum;
-      int pick = -1, last_pos = -1;
-      float pick_run = 0.f;
-      for (int t = t0; t < t1; ++t) {
-        const float ts = s_tile[t];
-        if (pick < 0 && run + ts > x) {
-          pick = t;
-          pick_run = run;
-        }
-        if (ts > 0.f) last_pos = t;
-        run += ts;
-      }
-      const uint64_t found = __ballot(pick >= 0);
-      if (found) {
-        const int src = __ffsll((long long)found) - 1;
-        const int tp = __shfl(pick, src, 64);
-        const float pr = __shfl(pick_run, src, 64);
-        if (lane == 0) {
-          s_tile_pick = tp;
-          s_x = x - pr;
-        }
-      } else {
-        // rounding left u*W beyond the last cumulative sum: take the last tile with mass
-        const uint64_t has = __ballot(last_pos >= 0);
-        const int src = has ? 63 - __clzll((long long)has) : 0;
-        const int tp = __shfl(last_pos, src, 64);
-        if (lane == 0) {
-          s_tile_pick = tp;
-          s_x = INFINITY;
-        }
-      }
-      if (lane == 0) s_W = W;
-    }
-    __syncthreads();
-    if (s_W > 0.f || pass == 1 || rw.d == nullptr) break;
-    // residual without mass (only reachable through rounding): draw from p
-    rw.d = nullptr;
-    __syncthreads();
-  }
+  return rw;
+}
 
-  // 4. locate the token inside the picked tile
-  if (wave == 0) {
+// Tile masses (wave inclusive-scan totals) of tiles [t0, t1) of a row into
+// s_tile[0 .. t1-t0).  Tiles go round-robin to the waves; each wave issues
+// the loads of up to kTilesPerWave tiles before weighting any of them.
+constexpr int kTilesPerWave = 4;
+
+__device__ void tile_masses(const RowWeights& rw, int V, bool vec, int t0, int t1, float* s_tile) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  for (int tb = t0; tb < t1; tb += nw * kTilesPerWave) {
+    float4 tv[kTilesPerWave], dv[kTilesPerWave];
+#pragma unroll
+    for (int i = 0; i < kTilesPerWave; ++i) {
+      const int t = tb + wave + i * nw;
+      const int e = t * kTile + lane * 4;
+      tv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      dv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (t < t1) {
+        tv[i] = load4(rw.t, e, V, vec);
+        if (rw.d) dv[i] = load4(rw.d, e, V, vec);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kTilesPerWave; ++i) {
+      const int t = tb + wave + i * nw;
+      if (t >= t1) continue;   // wave-uniform
+      float wv[4];
+      weights4(rw, tv[i], dv[i], t * kTile + lane * 4, V, wv);
+      const float incl = wave_incl_scan(((wv[0] + wv[1]) + wv[2]) + wv[3]);
+      if (lane == 63) s_tile[t - t0] = incl;
+    }
+  }
+}
+
+// First index in [0, n) whose running sum of v[] exceeds x, computed by one
+// wave (lanes own contiguous index ranges; fixed order).  Returns the running
+// sum before it in *before.  If rounding leaves x at or beyond the total,
+// returns the last index with v > 0 and *before = +inf (-1 if none).
+__device__ int wave_first_crossing(const float* v, int n, float x, float* before) {
+  const int lane = threadIdx.x & 63;
+  const int per = (n + 63) / 64;
+  const int i0 = min(lane * per, n), i1 = min(i0 + per, n);
+  float sum = 0.f;
+  int last_pos = -1;
+  for (int i = i0; i < i1; ++i) {
+    sum += v[i];
+    if (v[i] > 0.f) last_pos = i;
+  }
+  const float incl = wave_incl_scan(sum);
+  float run = incl - sum;
+  int pick = -1;
+  float pick_before = 0.f;
+  for (int i = i0; i < i1; ++i) {
+    if (pick < 0 && run + v[i] > x) {
+      pick = i;
+      pick_before = run;
+    }
+    run += v[i];
+  }
+  const uint64_t found = __ballot(pick >= 0);
+  if (found) {
+    const int src = __ffsll((long long)found) - 1;
+    *before = __shfl(pick_before, src, 64);
+    return __shfl(pick, src, 64);
+  }
+  const uint64_t has = __ballot(last_pos >= 0);
+  *before = INFINITY;
+  return has ? __shfl(last_pos, 63 - __clzll((long long)has), 64) : -1;
+}
+
+// Kernel 2: decisions, then the mass of one 16K-logit chunk of the sampled
+// row (sum of its tile masses in tile order).
+__global__ __launch_bounds__(kThreads2) void verify_mass_kernel(VerifyArgs a, VerifyWs ws) {
+  __shared__ float s_m[2 * kMaxG + 1], s_z[2 * kMaxG + 1];
+  __shared__ float s_tile[kChunkTiles];
+  __shared__ int s_jstar;
+  __shared__ float s_us;
+  const int c = blockIdx.x;
+  const int b = blockIdx.y;
+  decide(a, ws, b, s_m, s_z, &s_jstar, &s_us, c == 0);
+  const int jstar = s_jstar;
+  const RowWeights rw = sampled_row(a, b, jstar, s_m, s_z);
+  const int ntiles = (a.V + kTile - 1) / kTile;
+  const int t0 = c * kChunkTiles;   // c indexes 4K-logit mass chunks
+  const int t1 = min(t0 + kChunkTiles, ntiles);
+  tile_masses(rw, a.V, a.vec, t0, t1, s_tile);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float m = 0.f;
+    for (int t = 0; t < t1 - t0; ++t) m += s_tile[t];
+    ws.cmass[(size_t)b * ws.nmass + c] = m;
+    if (c == 0) {
+      Decision dd;
+      dd.jstar = jstar;
+      dd.us = s_us;
+      dd.mt = rw.mt;
+      dd.inv_zt = rw.inv_zt;
+      dd.md = rw.md;
+      dd.inv_zd = rw.inv_zd;
+      dd.pad0 = dd.pad1 = 0;
+      ws.dec[b] = dd;
+    }
+  }
+}
+
+// Kernel 3: one workgroup per sequence picks the emitted token: chunk by the
+// chunk masses, tile by the chunk's tile masses, token by a rescan of the
+// tile.  Writes emitted tokens and accepted lengths.
+__global__ __launch_bounds__(kThreads2) void verify_pick_kernel(VerifyArgs a, VerifyWs ws) {
+  __shared__ float s_tile[kMaxTiles];
+  __shared__ float s_cm[kMaxMassChunks];
+  __shared__ int s_tile_pick;
+  __shared__ float s_x;
+  __shared__ float s_W;
+  __shared__ int s_token;
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int G = a.G, V = a.V;
+  const Decision dd = ws.dec[b];
+  const int jstar = dd.jstar;
+  RowWeights rw;
+  rw.t = a.tl + ((size_t)b * (G + 1) + jstar) * V;
+  rw.mt = dd.mt;
+  rw.inv_zt = dd.inv_zt;
+  rw.d = jstar < G ? a.dl + ((size_t)b * G + jstar) * V : nullptr;
+  rw.md = dd.md;
+  rw.inv_zd = dd.inv_zd;
+  const int ntiles = (V + kTile - 1) / kTile;
+  const int nmass = ws.nmass;
+  for (int i = tid; i < nmass; i += kThreads2) s_cm[i] = ws.cmass[(size_t)b * nmass + i];
+  __syncthreads();
+  // total mass and the chunk holding u * W (wave 0)
+  if (tid < 64) {
+    float sum = 0.f;
+    for (int i = lane; i < nmass; i += 64) sum += s_cm[i];
+    sum = wave_sum(sum);
+    float before;
+    const int c = wave_first_crossing(s_cm, nmass, dd.us * sum, &before);
+    if (lane == 0) {
+      s_W = sum;
+      s_tile_pick = c < 0 ? 0 : c;
+      s_x = dd.us * sum - before;
+    }
+  }
+  __syncthreads();
+  int t0, t1;
+  bool full_row = false;
+  if (s_W > 0.f || rw.d == nullptr) {
+    t0 = s_tile_pick * kChunkTiles;
+    t1 = min(t0 + kChunkTiles, ntiles);
+  } else {
+    // residual without mass (reachable only through rounding): draw from p
+    rw.d = nullptr;
+    t0 = 0;
+    t1 = ntiles;
+    full_row = true;
+  }
+  float x = s_x;
+  __syncthreads();
+  tile_masses(rw, V, a.vec, t0, t1, s_tile);
+  __syncthreads();
+  if (tid < 64) {
+    if (full_row) {
+      float sum = 0.f;
+      for (int i = lane; i < t1 - t0; i += 64) sum += s_tile[i];
+      x = dd.us * wave_sum(sum);
+    }
+    float before;
+    const int t = wave_first_crossing(s_tile, t1 - t0, x, &before);
+    if (lane == 0) {
+      s_tile_pick = t < 0 ? -1 : t0 + t;
+      s_x = x - before;
+    }
+  }
+  __syncthreads();
+  // token inside the picked tile (wave 0)
+  if (tid < 64) {
     const int tp = s_tile_pick;
     int token = -1;
     if (tp >= 0) {
       float wv[4], incl;
       const int e = tp * kTile + lane * 4;
       tile_weights(rw, e, V, a.vec, wv, incl);
-      const float x = s_x;
+      const float xx = s_x;
       const float lane_sum = ((wv[0] + wv[1]) + wv[2]) + wv[3];
       const float excl = incl - lane_sum;
       int pick = -1;
-      if (incl > x) {
+      if (incl > xx) {
         float run = excl;
         for (int i = 0; i < 4; ++i) {
           run += wv[i];
-          if (run > x && wv[i] > 0.f) {
+          if (run > xx && wv[i] > 0.f) {
             pick = e + i;
             break;
           }
@@ -373,10 +508,20 @@ __global__ __launch_bounds__(kDecThreads) void verify_decide_kernel(VerifyArgs a
   if (tid == 0) a.acc_len[b] = jstar;
 }
 
-size_t verify_ws(int B, int G, int V, int* nchunks) {
+size_t verify_ws(int B, int G, int V, int* nchunks, VerifyWs* out, char* base) {
   const int nc = (V + kChunk - 1) / kChunk;
+  const int nm = (V + kMassChunk - 1) / kMassChunk;
   if (nchunks) *nchunks = nc;
-  return align_up((size_t)B * (2 * G + 1) * nc * sizeof(float2), 256);
+  const size_t part = align_up((size_t)B * (2 * G + 1) * nc * sizeof(float2), 256);
+  const size_t dec = align_up((size_t)B * sizeof(Decision), 256);
+  const size_t cm = align_up((size_t)B * nm * sizeof(float), 256);
+  if (out) {
+    out->part = reinterpret_cast<float2*>(base);
+    out->dec = reinterpret_cast<Decision*>(base + part);
+    out->cmass = reinterpret_cast<float*>(base + part + dec);
+    out->nmass = nm;
+  }
+  return part + dec + cm;
 }
 
 }  // namespace
@@ -384,7 +529,7 @@ size_t verify_ws(int B, int G, int V, int* nchunks) {
 
 extern "C" size_t spec_verify_workspace_size(int B, int G, int V) {
   if (B < 1 || G < 1 || V < 1) return 0;
-  return dsa::verify_ws(B, G, V, nullptr);
+  return dsa::verify_ws(B, G, V, nullptr, nullptr, nullptr);
 }
 
 extern "C" dsa_status spec_verify(const float* target_logits, const float* draft_logits,
@@ -402,7 +547,7 @@ extern "C" dsa_status spec_verify(const float* target_logits, const float* draft
   DSA_REQUIRE((int64_t)B * (2 * G + 1) <= 65535, DSA_ERR_UNSUPPORTED, "spec_verify: B*(2G+1)=%lld rows > 65535",
               (long long)B * (2 * G + 1));
   int nchunks = 0;
-  const size_t need = verify_ws(B, G, V, &nchunks);
+  const size_t need = verify_ws(B, G, V, &nchunks, nullptr, nullptr);
   DSA_REQUIRE(workspace && workspace_bytes >= need, DSA_ERR_WORKSPACE,
               "spec_verify: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
   VerifyArgs a{};
@@ -419,12 +564,17 @@ extern "C" dsa_status spec_verify(const float* target_logits, const float* draft
   a.acc_len = accepted_len;
   a.emitted = emitted;
   a.diag = diag;
-  a.part = static_cast<float2*>(workspace);
+  VerifyWs ws;
+  verify_ws(B, G, V, nullptr, &ws, static_cast<char*>(workspace));
+  a.part = ws.part;
   a.vec = (V % 4 == 0) && aligned16(target_logits) && aligned16(draft_logits);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipLaunchKernelGGL(verify_stats_kernel, dim3(nchunks, B * (2 * G + 1)), dim3(kStatThreads), 0, s, a);
   dsa_status st = launch_status("spec_verify(stats)");
   if (st != DSA_OK) return st;
-  hipLaunchKernelGGL(verify_decide_kernel, dim3(B), dim3(kDecThreads), 0, s, a);
-  return launch_status("spec_verify(decide)");
+  hipLaunchKernelGGL(verify_mass_kernel, dim3(ws.nmass, B), dim3(kThreads2), 0, s, a, ws);
+  st = launch_status("spec_verify(mass)");
+  if (st != DSA_OK) return st;
+  hipLaunchKernelGGL(verify_pick_kernel, dim3(B), dim3(kThreads2), 0, s, a, ws);
+  return launch_status("spec_verify(pick)");
 }

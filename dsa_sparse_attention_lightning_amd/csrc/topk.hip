@@ -110,12 +110,7 @@ __device__ void find_threshold_4096(const uint32_t* hist, uint32_t need, uint32_
     tot += c[j];
   }
   // inclusive scan over threads (descending bin order)
-  uint32_t inc = tot;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t v = __shfl_up(inc, o, 64);
-    if (lane_id() >= o) inc += v;
-  }
+  const uint32_t inc = wave_incl_scan_dpp(tot);
   const int wave = tid >> 6;
   if (lane_id() == 63) s_wave[wave] = inc;
   __syncthreads();
@@ -252,11 +247,7 @@ __device__ void select_candidates(const uint2* cand_g, const uint64_t* cand_l, i
         c4[j] = hist[255 - 4 * tid - j];
         tot += c4[j];
       }
-      uint32_t inc = tot;
-      for (int o = 1; o < 64; o <<= 1) {
-        uint32_t v = __shfl_up(inc, o, 64);
-        if (tid >= o) inc += v;
-      }
+      const uint32_t inc = wave_incl_scan_dpp(tot);
       uint32_t run = inc - tot;
       for (int j = 0; j < 4; ++j) {
         if (run < m_rem && run + c4[j] >= m_rem) {
@@ -342,11 +333,222 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const int32_t*
   for (int i = tid; i < k; i += kFinThreads) dst[i] = list[i];
 }
 
+// ---------------------------------------------------------------------------
+// One-workgroup path for rows up to kOneMaxLd positions: a single launch.
+// The row's keys stay in LDS when they fit (else each pass re-reads the
+// scores).  Radix select on 12/12/8-bit digits finds the k-th largest key
+// prefix; the output is an ordered compaction over positions (each wave owns
+// a contiguous position range, ballots give in-order ranks), so equal keys
+// are taken lowest position first and no sort is needed.
+// ---------------------------------------------------------------------------
+constexpr int kOneThreads = 1024;
+constexpr int kOneWaves = kOneThreads / 64;
+constexpr int kOneMaxLd = 131072;
+constexpr int kOneLdsKeys = 35840;       // 140 KiB of keys
+
+struct OneShared {
+  uint32_t hist[kBins];
+  uint32_t wave_tot[kOneWaves];
+  uint32_t wave_gt[kOneWaves], wave_eq[kOneWaves];
+  int bin;
+  uint32_t above, count;
+};
+
+// Bin T of an nbins histogram (scanning from the top) with
+// above(T) < need <= above(T) + hist[T]; all kOneThreads threads call it.
+__device__ void one_find_bin(OneShared& sh, int nbins, uint32_t need) {
+  const int tid = threadIdx.x;
+  const int per = nbins >= kOneThreads ? nbins / kOneThreads : 1;
+  const bool owns = tid * per < nbins;
+  const int hi = nbins - 1 - tid * per;
+  uint32_t tot = 0;
+  if (owns)
+    for (int j = 0; j < per; ++j) tot += sh.hist[hi - j];
+  const uint32_t inc = wave_incl_scan_dpp(tot);
+  const int wave = tid >> 6;
+  if (lane_id() == 63) sh.wave_tot[wave] = inc;
+  __syncthreads();
+  uint32_t run = inc - tot;
+  for (int w = 0; w < wave; ++w) run += sh.wave_tot[w];
+  if (owns)
+    for (int j = 0; j < per; ++j) {
+      const uint32_t c = sh.hist[hi - j];
+      if (run < need && run + c >= need) {
+        sh.bin = hi - j;
+        sh.above = run;
+        sh.count = c;
+      }
+      run += c;
+    }
+  __syncthreads();
+}
+
+template <bool kLds>
+__global__ __launch_bounds__(kOneThreads) void topk_one_kernel(const float* __restrict__ scores,
+                                                               const int32_t* __restrict__ row_len, int64_t ld,
+                                                               int k, int32_t* __restrict__ idx) {
+  extern __shared__ __align__(16) unsigned char one_smem[];
+  OneShared& sh = *reinterpret_cast<OneShared*>(one_smem);
+  uint32_t* keys = reinterpret_cast<uint32_t*>(one_smem + align_up(sizeof(OneShared), 16));
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int L = (int)min((int64_t)row_len[row], ld);   // row_len <= ld is a precondition
+  int32_t* dst = idx + (size_t)row * k;
+  if (L <= k) {
+    for (int i = tid; i < k; i += kOneThreads) dst[i] = i < L ? i : -1;
+    return;
+  }
+  const float* s = scores + (size_t)row * ld;
+  constexpr int kU = 8;   // loads in flight per thread
+  if (kLds) {
+    for (int t0 = tid; t0 < L; t0 += kU * kOneThreads) {
+      float v[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) v[u] = s[min(t0 + u * kOneThreads, L - 1)];
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+        if (t0 + u * kOneThreads < L) keys[t0 + u * kOneThreads] = order_key(v[u]);
+    }
+  }
+  auto key_at = [&](int t) -> uint32_t { return kLds ? keys[t] : order_key(s[t]); };
+
+  // Key range first: the bits that every key shares are resolved for free,
+  // so the first digit spreads over the range the scores actually occupy
+  // (indexer scores sit in a few octaves; a fixed top-bits digit would put
+  // most of the row into a handful of bins).
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+  __syncthreads();
+  for (int t0 = tid; t0 < L; t0 += kU * kOneThreads) {
+    uint32_t kv[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) kv[u] = key_at(min(t0 + u * kOneThreads, L - 1));
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      kmin = min(kmin, kv[u]);
+      kmax = max(kmax, kv[u]);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
+  }
+  if (lane == 0) {
+    sh.wave_gt[wave] = kmin;
+    sh.wave_eq[wave] = kmax;
+  }
+  __syncthreads();
+  kmin = sh.wave_gt[0];
+  kmax = sh.wave_eq[0];
+  for (int w = 1; w < kOneWaves; ++w) {
+    kmin = min(kmin, sh.wave_gt[w]);
+    kmax = max(kmax, sh.wave_eq[w]);
+  }
+  __syncthreads();
+  const int common = (kmin ^ kmax) ? __clz(kmin ^ kmax) : 32;
+  // radix select: resolved key bits are [31 .. shift]
+  int shift = 32 - common;
+  uint32_t prefix = shift >= 32 ? 0u : (kmin >> shift) << shift;
+  uint32_t need = (uint32_t)k;
+  while (shift > 0) {
+    const int nb = min(12, shift);
+    const int nshift = shift - nb;
+    const uint32_t mask = (1u << nb) - 1u;
+    for (int i = tid; i < (1 << nb); i += kOneThreads) sh.hist[i] = 0;
+    __syncthreads();
+    for (int tb = 0; tb < L; tb += kU * kOneThreads) {
+      uint32_t kv[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) kv[u] = key_at(min(tb + u * kOneThreads + tid, L - 1));
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int t = tb + u * kOneThreads + tid;
+        const uint32_t key = kv[u];
+        const bool hit = t < L && (shift >= 32 || (key >> shift) == (prefix >> shift));
+        const uint32_t bin = (key >> nshift) & mask;
+        // whole-wave same-bin case takes one atomic (all-equal rows)
+        const uint64_t hm = __ballot(hit);
+        const uint32_t b0 = (uint32_t)__builtin_amdgcn_readlane((int)bin, hm ? (__ffsll((long long)hm) - 1) : 0);
+        const uint64_t same = __ballot(hit && bin == b0);
+        if (same == hm) {
+          if (hm && lane == __ffsll((long long)hm) - 1) atomicAdd(&sh.hist[b0], (uint32_t)__popcll(hm));
+        } else if (hit) {
+          atomicAdd(&sh.hist[bin], 1u);
+        }
+      }
+    }
+    __syncthreads();
+    one_find_bin(sh, 1 << nb, need);
+    need -= sh.above;
+    prefix |= (uint32_t)sh.bin << nshift;
+    shift = nshift;
+    const bool done = sh.count == need;
+    __syncthreads();
+    if (done) break;
+  }
+
+  // ordered compaction: wave w owns positions [w*span, (w+1)*span)
+  const int span = ((L + kOneWaves - 1) / kOneWaves + 63) / 64 * 64;
+  const int p0 = min(wave * span, L), p1 = min(p0 + span, L);
+  const uint32_t P = shift >= 32 ? 0u : (prefix >> shift);
+  uint32_t n_gt = 0, n_eq = 0;
+  for (int tb = p0; tb < p1; tb += kU * 64) {
+    uint32_t kv[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) kv[u] = key_at(min(tb + u * 64 + lane, L - 1));
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int t = tb + u * 64 + lane;
+      const uint32_t kp = kv[u] >> shift;
+      n_gt += __popcll(__ballot(t < p1 && kp > P));
+      n_eq += __popcll(__ballot(t < p1 && kp == P));
+    }
+  }
+  if (lane == 0) {
+    sh.wave_gt[wave] = n_gt;
+    sh.wave_eq[wave] = n_eq;
+  }
+  __syncthreads();
+  uint32_t base_gt = 0, base_eq = 0;
+  for (int w = 0; w < wave; ++w) {
+    base_gt += sh.wave_gt[w];
+    base_eq += sh.wave_eq[w];
+  }
+  uint32_t eq_seen = base_eq;
+  uint32_t out_pos = base_gt + min(base_eq, need);
+  for (int tb = p0; tb < p1; tb += kU * 64) {
+    uint32_t kv[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) kv[u] = key_at(min(tb + u * 64 + lane, L - 1));
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int t = tb + u * 64 + lane;
+      const uint32_t kp = kv[u] >> shift;
+      const bool gt = t < p1 && kp > P;
+      const bool eq = t < p1 && kp == P;
+      const uint64_t eqm = __ballot(eq);
+      const bool take = gt || (eq && eq_seen + mask_rank(eqm) < need);
+      const uint64_t tm = __ballot(take);
+      if (take) dst[out_pos + mask_rank(tm)] = t;
+      out_pos += __popcll(tm);
+      eq_seen += __popcll(eqm);
+    }
+  }
+  // no padding needed: L > k means exactly k positions were written
+}
+
+size_t one_lds_bytes(bool in_lds) {
+  return align_up(sizeof(OneShared), 16) + (in_lds ? (size_t)kOneLdsKeys * 4 : 0);
+}
+
 }  // namespace
 }  // namespace dsa
 
 extern "C" size_t dsa_topk_workspace_size(int B, int R, int64_t ld, int k) {
   if (B < 1 || R < 1 || ld < 1 || k < 1) return 0;
+  if (ld <= dsa::kOneMaxLd) return 0;
   return dsa::ws_bytes(B * R, ld, k, nullptr, nullptr);
 }
 
@@ -360,12 +562,25 @@ extern "C" dsa_status dsa_topk(const float* scores, const int32_t* row_len, int 
   DSA_REQUIRE(k <= kMaxK, DSA_ERR_UNSUPPORTED, "dsa_topk: k=%d > %d", k, kMaxK);
   DSA_REQUIRE(ld <= ((int64_t)1 << 31) - 1, DSA_ERR_UNSUPPORTED, "dsa_topk: ld too large");
   const int rows = B * R;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (ld <= kOneMaxLd) {
+    // one launch, no workspace
+    const bool in_lds = ld <= kOneLdsKeys;
+    const size_t lds = one_lds_bytes(in_lds);
+    auto kern = in_lds ? topk_one_kernel<true> : topk_one_kernel<false>;
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)lds) != hipSuccess) {
+      set_error("dsa_topk: %zu bytes of LDS not available", lds);
+      return DSA_ERR_HIP;
+    }
+    hipLaunchKernelGGL(kern, dim3(rows), dim3(kOneThreads), lds, s, scores, row_len, ld, k, idx);
+    return launch_status("dsa_topk");
+  }
   const size_t need = ws_bytes(rows, ld, k, nullptr, nullptr);
   DSA_REQUIRE(workspace && workspace_bytes >= need, DSA_ERR_WORKSPACE,
               "dsa_topk: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
   RowWs ws;
   ws_bytes(rows, ld, k, &ws, static_cast<char*>(workspace));
-  hipStream_t s = static_cast<hipStream_t>(stream);
   const unsigned chunks = (unsigned)((ld + kChunk - 1) / kChunk);
   hipLaunchKernelGGL(topk_zero_kernel, dim3(rows), dim3(kHistThreads), 0, s, ws);
   hipLaunchKernelGGL(topk_hist1_kernel, dim3(chunks, rows), dim3(kHistThreads), 0, s, scores, row_len, ld, k, ws);

@@ -122,6 +122,8 @@ dsa_status dsa_topk(const float* scores, const int32_t* row_len, int B, int R,
  *   idx      int32 [B, idx_rows, k], idx_rows = 1 (shared by every query
  *            row) or S_q (one set per row); -1 entries are ignored
  *   lse      fp32 [B, S_q, H_q] or NULL
+ * workspace: dsa_sparse_attn_workspace_size() bytes (0: none needed) for
+ *   split-k partial results; no initialisation required.
  * Supported: (H_q == H_kv or H_q/H_kv in {2, 4}) with D_qk == D_v in
  * {64, 128}; or H_kv == 1, H_q in {16, 32, 64}, D_qk == 576, D_v == 512
  * (latent MQA).  Rows/heads/base pointers 16-byte aligned.

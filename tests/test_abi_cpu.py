@@ -58,14 +58,15 @@ def test_index_scores_validation():
 
 
 def test_topk_validation():
-    ws = lib.dsa_topk_workspace_size(2, 1, 1000, 64)
+    assert lib.dsa_topk_workspace_size(2, 1, 1000, 64) == 0          # one-workgroup path: none
+    ws = lib.dsa_topk_workspace_size(2, 1, 200000, 64)
     assert ws > 0
     assert lib.dsa_topk_workspace_size(0, 1, 1000, 64) == 0
     assert lib.dsa_topk(None, FAKE, 1, 1, 100, 8, FAKE, FAKE, ws, None) == _lib.DSA_ERR_INVALID_ARG
     assert lib.dsa_topk(FAKE, FAKE, 1, 1, 100, 0, FAKE, FAKE, ws, None) == _lib.DSA_ERR_INVALID_ARG
     assert lib.dsa_topk(FAKE, FAKE, 1, 1, 100, 9000, FAKE, FAKE, ws, None) == _lib.DSA_ERR_UNSUPPORTED
-    assert lib.dsa_topk(FAKE, FAKE, 2, 1, 1000, 64, FAKE, FAKE, ws - 1, None) == _lib.DSA_ERR_WORKSPACE
-    assert lib.dsa_topk(FAKE, FAKE, 2, 1, 1000, 64, FAKE, None, ws, None) == _lib.DSA_ERR_WORKSPACE
+    assert lib.dsa_topk(FAKE, FAKE, 2, 1, 200000, 64, FAKE, FAKE, ws - 1, None) == _lib.DSA_ERR_WORKSPACE
+    assert lib.dsa_topk(FAKE, FAKE, 2, 1, 200000, 64, FAKE, None, ws, None) == _lib.DSA_ERR_WORKSPACE
 
 
 def _attn_call(**over):

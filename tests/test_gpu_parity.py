@@ -86,39 +86,54 @@ def _topk_case(scores, lens, k):
         np.testing.assert_array_equal(got[b], ref, err_msg=f"row {b} L={lens[b]} k={k}")
 
 
-@pytest.mark.parametrize("name", ["normal", "ties", "allequal", "zeros_signed", "small_L", "k_ge_L",
-                                  "negative", "wide_range"])
-def test_topk_exact(name):
-    rng = np.random.default_rng(abs(hash(name)) % 2**32)
+# Row lengths exercising the three top-k paths: keys resident in LDS (ld up to
+# 35,840), one workgroup re-reading scores (up to 131,072), multi-workgroup
+# histogram pipeline (beyond).
+TOPK_LENS = {
+    "lds": [20000, 9000, 4097, 2048, 2049, 1, 0, 35000],
+    "one": [130000, 36000, 4097, 2049, 0],
+    "multi": [300000, 140000, 2049, 5],
+}
+
+
+@pytest.mark.parametrize("path", ["lds", "one", "multi"])
+@pytest.mark.parametrize("name", ["normal", "ties", "allequal", "zeros_signed", "negative", "wide_range"])
+def test_topk_exact(name, path):
+    rng = np.random.default_rng(abs(hash((name, path))) % 2**32)
     k = 2048
-    lens = [20000, 9000, 4097, 2048, 2049, 1, 0, 130000]
+    lens = TOPK_LENS[path]
     ld = max(lens) + 3
-    s = rng.standard_normal((len(lens), ld)).astype(np.float32)
+    shape = (len(lens), ld)
+    s = rng.standard_normal(shape).astype(np.float32)
     if name == "ties":
-        s = rng.integers(-20, 20, (len(lens), ld)).astype(np.float32)
+        s = rng.integers(-20, 20, shape).astype(np.float32)
     elif name == "allequal":
         s[:] = 1.5
     elif name == "zeros_signed":
-        s = np.where(rng.random((len(lens), ld)) < 0.5, np.float32(0.0), np.float32(-0.0))
+        s = np.where(rng.random(shape) < 0.5, np.float32(0.0), np.float32(-0.0))
         s[:, ::7] = 1.0
-    elif name == "small_L":
-        lens = [5, 64, 100, 2047]
-        k = 64
-    elif name == "k_ge_L":
-        lens = [2048, 100, 1000]
     elif name == "negative":
         s = -np.abs(s) - 1.0
     elif name == "wide_range":
-        s = (rng.standard_normal((len(lens), ld)) * 10.0 ** rng.integers(-30, 30, (len(lens), ld))).astype(np.float32)
-    log("topk", name, lens, k)
-    _topk_case(s[: len(lens)], lens, k)
+        s = (rng.standard_normal(shape) * 10.0 ** rng.integers(-30, 30, shape)).astype(np.float32)
+    log("topk", name, path, lens, k)
+    _topk_case(s, lens, k)
+
+
+@pytest.mark.parametrize("ld", [1000, 30000, 100000, 200000])
+def test_topk_small_k_and_k_ge_L(ld):
+    rng = np.random.default_rng(ld)
+    s = rng.standard_normal((3, ld)).astype(np.float32)
+    _topk_case(s, [min(ld, 5), min(ld, 64), min(ld, 100)], 64)     # k >= L rows
+    _topk_case(s, [ld, ld - 1, ld // 2], 1)                          # k = 1
 
 
 @pytest.mark.parametrize("k", [1, 7, 64, 2048, 8192])
-def test_topk_various_k(k):
+@pytest.mark.parametrize("ld", [30000, 50000, 180000])
+def test_topk_various_k(k, ld):
     rng = np.random.default_rng(k)
-    lens = [50000, 8191, 300]
-    s = rng.integers(0, 1000, (3, 50000)).astype(np.float32)
+    lens = [ld, 8191, 300]
+    s = rng.integers(0, 1000, (3, ld)).astype(np.float32)
     _topk_case(s, lens, k)
 
 
@@ -307,3 +322,48 @@ def test_spec_verify_special_cases():
     dr = rng.integers(V // 2, V, (B, G)).astype(np.int32)
     n, em, _ = _verify_case(I.VerifyInputs(tl2, dl2, dr, 10, 0), True)
     assert np.all(n == 0) and np.all(em[:, 0] < V // 2)
+
+
+# ----------------------------------------------------------------------------
+# HIP graph capture of the draft block: every replay matches the eager result
+# ----------------------------------------------------------------------------
+def test_draft_block_graph_replays():
+    d = I.draft_inputs(21, [3000], H_I=64, D_I=128, H_q=16, H_kv=16, D_qk=128, D_v=128, k=512, G=3)
+    dd = DraftDev(d)
+    scores = torch.empty((1, 1, dd.ld), device=DEV)
+    idx = torch.empty((1, 1, d.k), dtype=torch.int32, device=DEV)
+    outs = torch.empty((d.G, 1, 1, d.H_q, d.D_v), device=DEV)
+    lses = torch.empty((d.G, 1, 1, d.H_q), device=DEV)
+    ws = torch.empty(max(1, dsa.sparse_attn_workspace_size(1, 1, d.H_q, d.H_kv, d.D_qk, d.D_v, d.k)),
+                     dtype=torch.uint8, device=DEV)
+    vi = I.verify_inputs(22, 4, 7, 3000, 2.0)
+    tl, dl, dr = to_dev(vi.target_logits), to_dev(vi.draft_logits), to_dev(vi.drafts)
+    n = torch.empty(4, dtype=torch.int32, device=DEV)
+    em = torch.empty((4, 8), dtype=torch.int32, device=DEV)
+    vws = torch.empty(dsa.spec_verify_workspace_size(4, 7, 3000), dtype=torch.uint8, device=DEV)
+
+    def block():
+        dsa.index_scores(dd.q_index, dd.w, dd.kidx, dd.bt, dd.row_len, page=d.page, out=scores)
+        dsa.topk(scores, dd.row_len, d.k, out=idx)
+        for j in range(d.G):
+            dsa.sparse_attn(dd.q[j][:, None], dd.k, dd.v, dd.bt, idx[:, 0], page=d.page, sm_scale=d.sm_scale,
+                            out=outs[j], lse=lses[j], workspace=ws)
+        dsa.spec_verify(tl, dl, dr, seed=5, offset=1, accepted_len=n, emitted=em, workspace=vws)
+
+    block()
+    torch.cuda.synchronize()
+    ref = [x.clone() for x in (scores, idx, outs, lses, n, em)]
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=cap):
+        block()
+    L = int(d.lens[0])
+    for rep in range(4):
+        for x in (scores, idx, outs, lses, n, em):
+            x.zero_()                    # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(scores[..., :L], ref[0][..., :L]), f"replay {rep}: scores differ"
+        for a, b in zip((idx, outs, lses, n, em), ref[1:]):
+            assert torch.equal(a, b), f"replay {rep} differs"

@@ -232,15 +232,16 @@ __global__ __launch_bounds__(kThreads) void mha_attn_kernel(AttnArgs a) {
 // thread groups whose sums are added in group order.
 constexpr int kCombineThreads = 512;
 constexpr int kCombineMaxSplits = 128;
+constexpr int kLatentMaxSplits = 32;
 
-template <int D>
+template <int D, int MAXSPLIT>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* __restrict__ part_o,
                                                                   const float* __restrict__ part_ml,
                                                                   int nsplit, float* __restrict__ out,
                                                                   float* __restrict__ lse) {
-  constexpr int NG = kCombineThreads / D;
-  constexpr int PER = kCombineMaxSplits / NG;     // splits per thread group
-  __shared__ float s_m[kCombineMaxSplits], s_l[kCombineMaxSplits];
+  constexpr int NG = kCombineThreads / D > 0 ? kCombineThreads / D : 1;
+  constexpr int PER = MAXSPLIT / NG;              // splits per thread group
+  __shared__ float s_m[MAXSPLIT], s_l[MAXSPLIT];
   __shared__ float s_part[NG][D];
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
@@ -284,6 +285,217 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* _
 }
 
 // ---------------------------------------------------------------------------
+// Latent MQA kernel: one KV head of D_qk = 576 (K = whole row, V = its first
+// 512 dims) shared by NW*16 query heads.  Per 32-token tile:
+//   * the tile's rows go to LDS twice: row-major (K, B operand of QK^T) and
+//     transposed in the first 512 dims (V, B operand of PV), so every MFMA
+//     operand is one 16-byte LDS read;
+//   * wave w computes S = Q[16w..16w+15] K^T (18 K-steps x 2 N-blocks of
+//     v_mfma_f32_16x16x32_bf16), runs the online softmax for its 16 heads
+//     (16-lane DPP max/sum) and publishes P (bf16) and the rescale factors;
+//   * wave w then accumulates O[all heads][its 512/NW value dims] += P V.
+// Split-k partials (unnormalised O, m, l) go to the combine kernel as in the
+// per-head kernel.
+// ---------------------------------------------------------------------------
+constexpr int kLatD = 576;
+constexpr int kLatDv = 512;
+constexpr int kLatTile = 32;
+constexpr int kLatKRow = kLatD * 2 + 16;          // bytes per K row in LDS (padded)
+constexpr int kLatVRow = kLatTile * 2 + 16;       // bytes per transposed V row in LDS (padded)
+constexpr int kLatChunks = kLatD / 8;             // 16-byte chunks per row (72)
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_max_step(float v) {
+  return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, 0xf, 0xf, false)));
+}
+__device__ __forceinline__ float group_max16(float v) {
+  v = dpp_max_step<0xB1>(v);
+  v = dpp_max_step<0x4E>(v);
+  v = dpp_max_step<0x141>(v);
+  v = dpp_max_step<0x140>(v);
+  return v;
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rn(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);   // round to nearest even (finite inputs)
+  return (uint16_t)(u >> 16);
+}
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void latent_attn_kernel(AttnArgs a) {
+  constexpr int NT = NW * 64;
+  constexpr int H = NW * 16;
+  constexpr int DV_W = kLatDv / NW;               // value dims per wave
+  constexpr int NBV = DV_W / 16;                   // N-blocks of PV per wave
+  constexpr int KS = kLatD / 32;                   // 18 K-steps of QK
+  constexpr int PER_T = kLatTile * kLatChunks / NT;  // 16-byte chunks per thread per tile
+  __shared__ int64_t s_off[kMaxTokPerSplit];
+  __shared__ __align__(16) unsigned char s_k[kLatTile * kLatKRow];
+  __shared__ __align__(16) unsigned char s_vt[kLatDv * kLatVRow];
+  __shared__ __align__(16) uint16_t s_p[H][kLatTile + 8];
+  __shared__ float s_corr[H], s_lfin[H];
+
+  const int split = blockIdx.x;
+  const int bs = blockIdx.z;
+  const int b = bs / a.S_q;
+  const int s = bs % a.S_q;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int r16 = lane & 15;
+  const int grp = lane >> 4;
+
+  const int32_t* idx = a.idx + ((size_t)b * a.idx_rows + (a.idx_rows > 1 ? s : 0)) * a.k;
+  const int32_t* bt = a.bt + (size_t)b * a.max_pages;
+  const int t_lo = split * a.tok_per_split;
+  const int ntok = min(a.tok_per_split, a.k - t_lo);
+  for (int i = tid; i < ntok; i += NT) {
+    const int t = idx[t_lo + i];
+    s_off[i] = t >= 0 ? (int64_t)bt[t / a.page] * a.page_stride + (int64_t)(t % a.page) * a.row_stride : -1;
+  }
+  // Q fragments of this wave's 16 heads: A operand, lane holds head 16w + l%16,
+  // dims ks*32 + (l/16)*8 .. +8
+  bf16x8_t qa[KS];
+  {
+    const uint16_t* qrow = a.q + ((size_t)bs * a.H_q + wave * 16 + r16) * kLatD + grp * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qa[ks] = *reinterpret_cast<const bf16x8_t*>(qrow + ks * 32);
+  }
+  f32x4_t o[NW][NBV];
+#pragma unroll
+  for (int mb = 0; mb < NW; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NBV; ++nb) o[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run[4], l_run[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m_run[i] = -INFINITY;
+    l_run[i] = 0.f;
+  }
+  __syncthreads();
+
+  const int ntiles = (ntok + kLatTile - 1) / kLatTile;
+  uint4 pre[PER_T];
+  auto fetch = [&](int tile) {
+#pragma unroll
+    for (int j = 0; j < PER_T; ++j) {
+      const int c = tid + j * NT;
+      const int tt = min(tile * kLatTile + c / kLatChunks, ntok - 1);
+      const int64_t off = max(s_off[tt], (int64_t)0);
+      pre[j] = *reinterpret_cast<const uint4*>(a.kc + off + (c % kLatChunks) * 8);
+    }
+  };
+  fetch(0);
+  for (int tile = 0; tile < ntiles; ++tile) {
+    // stage the tile: K row-major, V transposed
+#pragma unroll
+    for (int j = 0; j < PER_T; ++j) {
+      const int c = tid + j * NT;
+      const int tt = c / kLatChunks;
+      const int ch = c % kLatChunks;
+      *reinterpret_cast<uint4*>(s_k + tt * kLatKRow + ch * 16) = pre[j];
+      if (ch < kLatDv / 8) {
+        const uint32_t w4[4] = {pre[j].x, pre[j].y, pre[j].z, pre[j].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint16_t v = (uint16_t)(e & 1 ? (w4[e >> 1] >> 16) : (w4[e >> 1] & 0xffffu));
+          *reinterpret_cast<uint16_t*>(s_vt + (ch * 8 + e) * kLatVRow + tt * 2) = v;
+        }
+      }
+    }
+    __syncthreads();
+    if (tile + 1 < ntiles) fetch(tile + 1);   // next tile's loads overlap this tile's math
+
+    // S = Q K^T for this wave's heads: C layout, lane holds heads
+    // 16w + (l/16)*4 + i, token nb*16 + l%16
+    f32x4_t sacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const bf16x8_t kb = *reinterpret_cast<const bf16x8_t*>(s_k + (nb * 16 + r16) * kLatKRow + ks * 64 + grp * 16);
+        sacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], kb, sacc[nb], 0, 0, 0);
+      }
+    }
+    // online softmax over the tile's tokens (exp2 domain)
+    bool valid[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int li = tile * kLatTile + nb * 16 + r16;
+      valid[nb] = li < ntok && s_off[li] >= 0;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float s0 = valid[0] ? sacc[0][i] * a.scale_log2 : -INFINITY;
+      const float s1 = valid[1] ? sacc[1][i] * a.scale_log2 : -INFINITY;
+      const float tmax = group_max16(fmaxf(s0, s1));
+      const float mn = fmaxf(m_run[i], tmax);
+      const float corr = mn == -INFINITY ? 1.f : fast_exp2(m_run[i] - mn);
+      const uint16_t p0 = f32_to_bf16_rn(mn == -INFINITY ? 0.f : fast_exp2(s0 - mn));
+      const uint16_t p1 = f32_to_bf16_rn(mn == -INFINITY ? 0.f : fast_exp2(s1 - mn));
+      // the row sum uses the bf16-rounded weights that PV multiplies
+      const float psum = group_sum_dpp<16>(__uint_as_float((uint32_t)p0 << 16) + __uint_as_float((uint32_t)p1 << 16));
+      l_run[i] = l_run[i] * corr + psum;
+      m_run[i] = mn;
+      const int h = wave * 16 + grp * 4 + i;
+      s_p[h][r16] = p0;
+      s_p[h][16 + r16] = p1;
+      if (r16 == 0) s_corr[h] = corr;
+    }
+    __syncthreads();
+    // O[all heads][this wave's value dims] = O * corr + P V
+#pragma unroll
+    for (int mb = 0; mb < NW; ++mb) {
+      const bf16x8_t pa = *reinterpret_cast<const bf16x8_t*>(&s_p[mb * 16 + r16][grp * 8]);
+      float c4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) c4[i] = s_corr[mb * 16 + grp * 4 + i];
+#pragma unroll
+      for (int nb = 0; nb < NBV; ++nb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[mb][nb][i] *= c4[i];
+        const int dv = wave * DV_W + nb * 16 + r16;
+        const bf16x8_t vb = *reinterpret_cast<const bf16x8_t*>(s_vt + dv * kLatVRow + grp * 16);
+        o[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o[mb][nb], 0, 0, 0);
+      }
+    }
+    __syncthreads();   // the next tile overwrites s_k, s_vt, s_p
+  }
+
+  // per-head statistics: owned by the wave that ran the head's softmax
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = wave * 16 + grp * 4 + i;
+    const size_t row = (size_t)bs * a.H_q + h;
+    if (r16 == 0) {
+      s_lfin[h] = l_run[i];
+      if (a.nsplit == 1) {
+        if (a.lse) a.lse[row] = m_run[i] == -INFINITY ? -INFINITY : (m_run[i] + __log2f(l_run[i])) * kLn2;
+      } else {
+        a.part_ml[(row * a.nsplit + split) * 2 + 0] = m_run[i];
+        a.part_ml[(row * a.nsplit + split) * 2 + 1] = l_run[i];
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int mb = 0; mb < NW; ++mb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = mb * 16 + grp * 4 + i;
+      const size_t row = (size_t)bs * a.H_q + h;
+      const float inv = s_lfin[h] > 0.f ? 1.f / s_lfin[h] : 0.f;
+#pragma unroll
+      for (int nb = 0; nb < NBV; ++nb) {
+        const int dv = wave * DV_W + nb * 16 + r16;
+        if (a.nsplit == 1) a.out[row * kLatDv + dv] = o[mb][nb][i] * inv;
+        else a.part_o[(row * a.nsplit + split) * kLatDv + dv] = o[mb][nb][i];
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Launch planning (shared by the workspace query and the call)
 // ---------------------------------------------------------------------------
 struct Plan {
@@ -294,18 +506,26 @@ struct Plan {
   size_t part_o_off, part_ml_off;
 };
 
+// The latent kernel is instantiated for 64 query heads (4 waves); fewer
+// heads would leave its per-wave register tiles spilling.
+bool is_latent(int H_q, int H_kv, int D_qk, int D_v) {
+  return H_kv == 1 && D_qk == kLatD && D_v == kLatDv && H_q == 64;
+}
+
 Plan make_plan(int B, int S_q, int H_q, int H_kv, int D_qk, int D_v, int k) {
   Plan p{};
-  const int nslot = 64 / (D_qk / 8);
-  p.head_groups = (H_kv + nslot - 1) / nslot;
+  const bool latent = is_latent(H_q, H_kv, D_qk, D_v);
+  const int nslot = latent ? 1 : 64 / (D_qk / 8);
+  p.head_groups = latent ? 1 : (H_kv + nslot - 1) / nslot;
   const long long base = (long long)B * S_q * p.head_groups;
-  constexpr int kMinTok = DSA_ATTN_MIN_TOKENS;
+  const int min_tok = latent ? 4 * kLatTile : DSA_ATTN_MIN_TOKENS;
+  const int max_split = latent ? kLatentMaxSplits : kCombineMaxSplits;
   int ns = (int)((DSA_ATTN_TARGET_WGS + base - 1) / base);
-  const int max_ns = (k + kMinTok - 1) / kMinTok;
+  const int max_ns = (k + min_tok - 1) / min_tok;
   if (ns > max_ns) ns = max_ns;
   const int min_ns = (k + kMaxTokPerSplit - 1) / kMaxTokPerSplit;
   if (ns < min_ns) ns = min_ns;
-  if (ns > kCombineMaxSplits) ns = kCombineMaxSplits;
+  if (ns > max_split) ns = max_split;
   if (ns < 1) ns = 1;
   p.tok_per_split = (k + ns - 1) / ns;
   p.nsplit = (k + p.tok_per_split - 1) / p.tok_per_split;
@@ -329,7 +549,7 @@ void launch_mha(const AttnArgs& a, const Plan& p, int B, hipStream_t s) {
 
 extern "C" size_t dsa_sparse_attn_workspace_size(int B, int S_q, int H_q, int H_kv, int D_qk, int D_v, int k) {
   if (B < 1 || S_q < 1 || H_q < 1 || H_kv < 1 || D_qk < 8 || D_v < 1 || k < 1) return 0;
-  if (D_qk != 64 && D_qk != 128) return 0;
+  if (D_qk != 64 && D_qk != 128 && !dsa::is_latent(H_q, H_kv, D_qk, D_v)) return 0;
   return dsa::make_plan(B, S_q, H_q, H_kv, D_qk, D_v, k).ws_bytes;
 }
 
@@ -353,9 +573,14 @@ extern "C" dsa_status dsa_sparse_attn(const void* q, const void* k_cache, const 
   DSA_REQUIRE(H_q % H_kv == 0, DSA_ERR_INVALID_ARG, "dsa_sparse_attn: H_q=%d not a multiple of H_kv=%d", H_q, H_kv);
   DSA_REQUIRE(std::isfinite(sm_scale), DSA_ERR_INVALID_ARG, "dsa_sparse_attn: sm_scale not finite");
   const int gq = H_q / H_kv;
-  DSA_REQUIRE((D_qk == 64 || D_qk == 128) && D_v == D_qk && (gq == 1 || gq == 2 || gq == 4),
+  const bool latent = is_latent(H_q, H_kv, D_qk, D_v);
+  DSA_REQUIRE(latent || ((D_qk == 64 || D_qk == 128) && D_v == D_qk && (gq == 1 || gq == 2 || gq == 4)),
               DSA_ERR_UNSUPPORTED, "dsa_sparse_attn: (H_q=%d, H_kv=%d, D_qk=%d, D_v=%d) not supported",
               H_q, H_kv, D_qk, D_v);
+  DSA_REQUIRE(!latent || v_cache == k_cache, DSA_ERR_UNSUPPORTED,
+              "dsa_sparse_attn: the latent path reads V from the key rows (pass v_cache == k_cache)");
+  DSA_REQUIRE(k <= (latent ? kLatentMaxSplits : kCombineMaxSplits) * kMaxTokPerSplit, DSA_ERR_UNSUPPORTED,
+              "dsa_sparse_attn: k=%d too large", k);
   DSA_REQUIRE(aligned16(q) && aligned16(k_cache) && aligned16(v_cache) && kv_page_stride % 8 == 0 &&
                   kv_row_stride % 8 == 0 && kv_head_stride % 8 == 0,
               DSA_ERR_INVALID_ARG, "dsa_sparse_attn: q/K/V rows must be 16-byte aligned");
@@ -388,6 +613,15 @@ extern "C" dsa_status dsa_sparse_attn(const void* q, const void* k_cache, const 
     a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.part_ml_off);
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (latent) {
+    dim3 grid(p.nsplit, 1, B * S_q);
+    hipLaunchKernelGGL(latent_attn_kernel<4>, grid, dim3(256), 0, s, a);
+    dsa_status st = launch_status("dsa_sparse_attn(latent)");
+    if (st != DSA_OK || p.nsplit == 1) return st;
+    hipLaunchKernelGGL((combine_kernel<kLatDv, kLatentMaxSplits>), dim3(B * S_q * H_q), dim3(kCombineThreads), 0, s,
+                       a.part_o, a.part_ml, p.nsplit, out, lse);
+    return launch_status("dsa_sparse_attn(combine)");
+  }
   if (D_qk == 64) {
     if (gq == 1) launch_mha<64, 1>(a, p, B, s);
     else if (gq == 2) launch_mha<64, 2>(a, p, B, s);
@@ -401,10 +635,10 @@ extern "C" dsa_status dsa_sparse_attn(const void* q, const void* k_cache, const 
   if (st != DSA_OK || p.nsplit == 1) return st;
   const int rows = B * S_q * H_q;
   if (D_v == 64)
-    hipLaunchKernelGGL(combine_kernel<64>, dim3(rows), dim3(kCombineThreads), 0, s, a.part_o, a.part_ml, p.nsplit,
-                       out, lse);
+    hipLaunchKernelGGL((combine_kernel<64, kCombineMaxSplits>), dim3(rows), dim3(kCombineThreads), 0, s, a.part_o,
+                       a.part_ml, p.nsplit, out, lse);
   else
-    hipLaunchKernelGGL(combine_kernel<128>, dim3(rows), dim3(kCombineThreads), 0, s, a.part_o, a.part_ml,
-                       p.nsplit, out, lse);
+    hipLaunchKernelGGL((combine_kernel<128, kCombineMaxSplits>), dim3(rows), dim3(kCombineThreads), 0, s, a.part_o,
+                       a.part_ml, p.nsplit, out, lse);
   return launch_status("dsa_sparse_attn(combine)");
 }

@@ -125,8 +125,10 @@ dsa_status dsa_topk(const float* scores, const int32_t* row_len, int B, int R,
  * workspace: dsa_sparse_attn_workspace_size() bytes (0: none needed) for
  *   split-k partial results; no initialisation required.
  * Supported: (H_q == H_kv or H_q/H_kv in {2, 4}) with D_qk == D_v in
- * {64, 128}; or H_kv == 1, H_q in {16, 32, 64}, D_qk == 576, D_v == 512
- * (latent MQA).  Rows/heads/base pointers 16-byte aligned.
+ * {64, 128}; or H_kv == 1, H_q == 64, D_qk == 576, D_v == 512 with
+ * v_cache == k_cache (latent MQA; QK^T and PV on bf16 MFMA, P rounded to
+ * bf16).  k <= 131072 (latent: k <= 32768).  Rows/heads/base pointers
+ * 16-byte aligned.
  */
 size_t dsa_sparse_attn_workspace_size(int B, int S_q, int H_q, int H_kv,
                                       int D_qk, int D_v, int k);

@@ -367,3 +367,71 @@ def test_draft_block_graph_replays():
         assert torch.equal(scores[..., :L], ref[0][..., :L]), f"replay {rep}: scores differ"
         for a, b in zip((idx, outs, lses, n, em), ref[1:]):
             assert torch.equal(a, b), f"replay {rep} differs"
+
+
+# ----------------------------------------------------------------------------
+# latent MQA attention (one 576-d KV row shared by 64 heads, V = first 512)
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("case", [
+    dict(lens=[3000, 1500], k=2048, shuffle=True),      # split-k, ragged, one row with -1 padding
+    dict(lens=[200], k=64, shuffle=False),              # single split, k < L
+    dict(lens=[100], k=128, shuffle=False),             # k > L: padding inside the split
+])
+def test_latent_attn_matches_oracle(case):
+    log("latent", case)
+    d = I.draft_inputs(31, case["lens"], H_I=4, D_I=32, H_q=64, D_qk=576, D_v=512, k=case["k"], G=2,
+                       latent=True, shuffle_pages=case["shuffle"])
+    dd = DraftDev(d)
+    rng = np.random.default_rng(7)
+    idx = np.full((d.B, d.k), -1, np.int64)
+    for b in range(d.B):
+        n = min(d.k, int(d.lens[b]))
+        idx[b, :n] = np.sort(rng.choice(int(d.lens[b]), n, replace=False))
+    _, _, err = _attn_vs_oracle(d, dd, idx)
+    log(f"  latent max err {err:.2e}")
+    idx2 = idx.copy()
+    for b in range(d.B):
+        rng.shuffle(idx2[b])
+    _attn_vs_oracle(d, dd, idx2)
+
+
+def test_latent_attn_dense_and_empty():
+    d = I.draft_inputs(32, [700], H_I=4, D_I=32, H_q=64, D_qk=576, D_v=512, k=1024, G=1, latent=True)
+    dd = DraftDev(d)
+    idx = np.full((1, d.k), -1, np.int64)
+    idx[0, :700] = np.arange(700)
+    out, lse, _ = _attn_vs_oracle(d, dd, idx)
+    o_dense, l_dense = O.dense_attn(d.q[0, 0], d.K[0], d.V[0], 700, d.sm_scale)
+    assert np.abs(out[0] - o_dense).max() <= ATTN_TOL
+    idx[:] = -1
+    o, l = dsa.sparse_attn(dd.q[0][:, None], dd.k, dd.v, dd.bt, to_dev(idx.astype(np.int32)), page=d.page,
+                           D_v=512, sm_scale=d.sm_scale)
+    assert torch.all(o == 0) and torch.all(torch.isneginf(l))
+
+
+# ----------------------------------------------------------------------------
+# verify-pass shape: 8 query rows, row r sees [0, L + r + 1), one index set per row
+# ----------------------------------------------------------------------------
+def test_verify_pass_rows():
+    G = 7
+    R = G + 1
+    d = I.draft_inputs(41, [5000], H_I=64, D_I=128, H_q=16, H_kv=16, D_qk=128, D_v=128, k=512, G=G + 1,
+                       R=R, integer_indexer=True)
+    L = int(d.lens[0])
+    row_len = np.array([[L + r + 1 for r in range(R)]], np.int32)     # causal rows over the drafted chain
+    dd = DraftDev(d)
+    rl = to_dev(row_len)
+    scores = dsa.index_scores(dd.q_index, dd.w, dd.kidx, dd.bt, rl, page=d.page, ld=L + R + 1)
+    idx = dsa.topk(scores, rl, d.k)                                     # [1, R, k]
+    ref_s = O.index_scores(d.q_index[0], d.w[0].astype(np.float64), d.keys[0], row_len[0])
+    got_s = scores.cpu().numpy()[0]
+    for r in range(R):
+        np.testing.assert_array_equal(got_s[r, : row_len[0, r]], ref_s[r, : row_len[0, r]].astype(np.float32))
+        np.testing.assert_array_equal(idx.cpu().numpy()[0, r], O.topk(ref_s[r], row_len[0, r], d.k))
+    # 8 query rows, each with its own index set
+    q = torch.stack([dd.q[j][0] for j in range(R)])[None]              # [1, R, H, D]
+    out, lse = dsa.sparse_attn(q.contiguous(), dd.k, dd.v, dd.bt, idx, page=d.page, sm_scale=d.sm_scale)
+    out = out.cpu().numpy()[0]
+    for r in range(R):
+        o_ref, _ = O.sparse_attn(d.q[r, 0], d.K[0], d.V[0], idx.cpu().numpy()[0, r], d.sm_scale)
+        assert np.abs(out[r] - o_ref).max() <= ATTN_TOL

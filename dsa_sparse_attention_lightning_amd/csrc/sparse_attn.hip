@@ -25,8 +25,11 @@
 namespace dsa {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
+#ifndef DSA_ATTN_WAVES
+#define DSA_ATTN_WAVES 4
+#endif
+constexpr int kWaves = DSA_ATTN_WAVES;      // waves per per-head-KV workgroup
+constexpr int kThreads = kWaves * 64;
 
 // Split-k plan: aim for about kTargetGroups workgroups, each with at least
 // kMinTokens selected tokens (tunable at build time).
@@ -34,10 +37,10 @@ constexpr int kWaves = kThreads / 64;
 #define DSA_ATTN_TARGET_WGS 1024
 #endif
 #ifndef DSA_ATTN_MIN_TOKENS
-#define DSA_ATTN_MIN_TOKENS 32
+#define DSA_ATTN_MIN_TOKENS 128
 #endif
 #ifndef DSA_ATTN_UNROLL
-#define DSA_ATTN_UNROLL 8
+#define DSA_ATTN_UNROLL 2
 #endif
 
 struct AttnArgs {
@@ -78,39 +81,65 @@ __device__ __forceinline__ void issue_loads(const AttnArgs& a, const int64_t* s_
   }
 }
 
+// Online-softmax update with one stage of U tokens: the U dot products and
+// their DPP reductions are independent (they overlap), then the running max,
+// sum and accumulator are rescaled once for the whole stage.
 template <int D, int GQ, int U>
 __device__ __forceinline__ void consume(const int64_t* s_off, int i, int ntok, float scale_log2,
                                         const float (&qv)[GQ][8], float (&m)[GQ], float (&l)[GQ],
                                         float (&acc)[GQ][8], const uint4 (&kr)[U], const uint4 (&vr)[U]) {
   constexpr int SLOT = D / 8;
+  bool ok[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int li = i + u * kWaves;
-    if (li >= ntok || s_off[li] < 0) continue;   // wave-uniform
-    float kf[8], vf[8];
-    kf[0] = bf16_lo(kr[u].x); kf[1] = bf16_hi(kr[u].x);
-    kf[2] = bf16_lo(kr[u].y); kf[3] = bf16_hi(kr[u].y);
-    kf[4] = bf16_lo(kr[u].z); kf[5] = bf16_hi(kr[u].z);
-    kf[6] = bf16_lo(kr[u].w); kf[7] = bf16_hi(kr[u].w);
-    vf[0] = bf16_lo(vr[u].x); vf[1] = bf16_hi(vr[u].x);
-    vf[2] = bf16_lo(vr[u].y); vf[3] = bf16_hi(vr[u].y);
-    vf[4] = bf16_lo(vr[u].z); vf[5] = bf16_hi(vr[u].z);
-    vf[6] = bf16_lo(vr[u].w); vf[7] = bf16_hi(vr[u].w);
+    ok[u] = li < ntok && s_off[li] >= 0;   // wave-uniform
+  }
 #pragma unroll
-    for (int j = 0; j < GQ; ++j) {
-      float dt = 0.f;
+  for (int j = 0; j < GQ; ++j) {
+    float sc[U];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) dt = fmaf(qv[j][e], kf[e], dt);
-      dt = group_sum_dpp<SLOT>(dt);
-      const float sc = dt * scale_log2;
-      const float mn = fmaxf(m[j], sc);
-      const float corr = fast_exp2(m[j] - mn);
-      const float p = fast_exp2(sc - mn);
-      l[j] = l[j] * corr + p;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[j][e] = fmaf(p, vf[e], acc[j][e] * corr);
-      m[j] = mn;
+    for (int u = 0; u < U; ++u) {
+      const float k0 = bf16_lo(kr[u].x), k1 = bf16_hi(kr[u].x), k2 = bf16_lo(kr[u].y), k3 = bf16_hi(kr[u].y);
+      const float k4 = bf16_lo(kr[u].z), k5 = bf16_hi(kr[u].z), k6 = bf16_lo(kr[u].w), k7 = bf16_hi(kr[u].w);
+      float d0 = qv[j][0] * k0;
+      float d1 = qv[j][1] * k1;
+      d0 = fmaf(qv[j][2], k2, d0);
+      d1 = fmaf(qv[j][3], k3, d1);
+      d0 = fmaf(qv[j][4], k4, d0);
+      d1 = fmaf(qv[j][5], k5, d1);
+      d0 = fmaf(qv[j][6], k6, d0);
+      d1 = fmaf(qv[j][7], k7, d1);
+      sc[u] = group_sum_dpp<SLOT>(d0 + d1) * scale_log2;
     }
+    float smax = m[j];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (ok[u]) smax = fmaxf(smax, sc[u]);
+    if (smax == -INFINITY) continue;   // nothing valid yet (wave-uniform)
+    const float corr = fast_exp2(m[j] - smax);
+    float lsum = l[j] * corr;
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = acc[j][e] * corr;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (!ok[u]) continue;
+      const float p = fast_exp2(sc[u] - smax);
+      lsum += p;
+      o[0] = fmaf(p, bf16_lo(vr[u].x), o[0]);
+      o[1] = fmaf(p, bf16_hi(vr[u].x), o[1]);
+      o[2] = fmaf(p, bf16_lo(vr[u].y), o[2]);
+      o[3] = fmaf(p, bf16_hi(vr[u].y), o[3]);
+      o[4] = fmaf(p, bf16_lo(vr[u].z), o[4]);
+      o[5] = fmaf(p, bf16_hi(vr[u].z), o[5]);
+      o[6] = fmaf(p, bf16_lo(vr[u].w), o[6]);
+      o[7] = fmaf(p, bf16_hi(vr[u].w), o[7]);
+    }
+    l[j] = lsum;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[j][e] = o[e];
+    m[j] = smax;
   }
 }
 
@@ -226,62 +255,60 @@ __global__ __launch_bounds__(kThreads) void mha_attn_kernel(AttnArgs a) {
   }
 }
 
-// Folds split partials in split order: one workgroup per (b, s, h) row.
-// Every thread issues all of its loads at once (one memory round trip); the
-// output dims are spread over threads and the splits over kCombineThreads/D
-// thread groups whose sums are added in group order.
-constexpr int kCombineThreads = 512;
+// Folds split partials in split order: one workgroup of D threads per
+// (b, s, h) row, one output dim per thread.  The split statistics (m, l) are
+// the same for every thread of the row (scalar loads); each thread issues the
+// loads of all its split partials at once, so the fold is one memory round
+// trip with no barrier.
 constexpr int kCombineMaxSplits = 128;
 constexpr int kLatentMaxSplits = 32;
 
 template <int D, int MAXSPLIT>
-__global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* __restrict__ part_o,
-                                                                  const float* __restrict__ part_ml,
-                                                                  int nsplit, float* __restrict__ out,
-                                                                  float* __restrict__ lse) {
-  constexpr int NG = kCombineThreads / D > 0 ? kCombineThreads / D : 1;
-  constexpr int PER = MAXSPLIT / NG;              // splits per thread group
-  __shared__ float s_m[MAXSPLIT], s_l[MAXSPLIT];
-  __shared__ float s_part[NG][D];
+__global__ __launch_bounds__(D) void combine_kernel(const float* __restrict__ part_o,
+                                                    const float* __restrict__ part_ml, int nsplit,
+                                                    float* __restrict__ out, float* __restrict__ lse) {
   const int row = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int d = tid % D;
-  const int g = tid / D;
+  const int d = threadIdx.x;
   const float* ml = part_ml + (size_t)row * nsplit * 2;
   const float* po = part_o + (size_t)row * nsplit * D + d;
-  float ov[PER];
+  float ov[MAXSPLIT], mv[MAXSPLIT], lv[MAXSPLIT];
 #pragma unroll
-  for (int u = 0; u < PER; ++u) {
-    const int sp = g + u * NG;
-    ov[u] = sp < nsplit ? po[(size_t)sp * D] : 0.f;
+  for (int sp = 0; sp < MAXSPLIT; ++sp) {
+    const int c = min(sp, nsplit - 1);
+    ov[sp] = po[(size_t)c * D];
+    mv[sp] = ml[2 * c];
+    lv[sp] = ml[2 * c + 1];
   }
-  if (tid < nsplit) {
-    s_m[tid] = ml[2 * tid];
-    s_l[tid] = ml[2 * tid + 1];
-  }
-  __syncthreads();
   float M = -INFINITY;
-  for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, s_m[sp]);
-  float O = 0.f;
+#pragma unroll
+  for (int sp = 0; sp < MAXSPLIT; ++sp)
+    if (sp < nsplit) M = fmaxf(M, mv[sp]);
+  float O = 0.f, Lsum = 0.f;
   if (M != -INFINITY) {
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int sp = g + u * NG;
-      if (sp < nsplit) O += fast_exp2(s_m[sp] - M) * ov[u];
+    for (int sp = 0; sp < MAXSPLIT; ++sp) {
+      if (sp < nsplit) {
+        const float c = fast_exp2(mv[sp] - M);
+        O += c * ov[sp];
+        Lsum += c * lv[sp];
+      }
     }
   }
-  s_part[g][d] = O;
-  __syncthreads();
-  if (g == 0) {
-    float Ot = 0.f;
-#pragma unroll
-    for (int gg = 0; gg < NG; ++gg) Ot += s_part[gg][d];
-    float Lsum = 0.f;
-    if (M != -INFINITY)
-      for (int sp = 0; sp < nsplit; ++sp) Lsum += fast_exp2(s_m[sp] - M) * s_l[sp];
-    out[(size_t)row * D + d] = M == -INFINITY ? 0.f : Ot / Lsum;
-    if (d == 0 && lse) lse[row] = M == -INFINITY ? -INFINITY : (M + __log2f(Lsum)) * kLn2;
-  }
+  out[(size_t)row * D + d] = M == -INFINITY ? 0.f : O / Lsum;
+  if (d == 0 && lse) lse[row] = M == -INFINITY ? -INFINITY : (M + __log2f(Lsum)) * kLn2;
+}
+
+template <int D>
+void launch_combine(const float* part_o, const float* part_ml, int rows, int nsplit, float* out, float* lse,
+                    hipStream_t s) {
+  if (nsplit <= 16)
+    hipLaunchKernelGGL((combine_kernel<D, 16>), dim3(rows), dim3(D), 0, s, part_o, part_ml, nsplit, out, lse);
+  else if (nsplit <= 32)
+    hipLaunchKernelGGL((combine_kernel<D, 32>), dim3(rows), dim3(D), 0, s, part_o, part_ml, nsplit, out, lse);
+  else if (nsplit <= 64)
+    hipLaunchKernelGGL((combine_kernel<D, 64>), dim3(rows), dim3(D), 0, s, part_o, part_ml, nsplit, out, lse);
+  else
+    hipLaunchKernelGGL((combine_kernel<D, 128>), dim3(rows), dim3(D), 0, s, part_o, part_ml, nsplit, out, lse);
 }
 
 // ---------------------------------------------------------------------------
@@ -618,8 +645,7 @@ extern "C" dsa_status dsa_sparse_attn(const void* q, const void* k_cache, const 
     hipLaunchKernelGGL(latent_attn_kernel<4>, grid, dim3(256), 0, s, a);
     dsa_status st = launch_status("dsa_sparse_attn(latent)");
     if (st != DSA_OK || p.nsplit == 1) return st;
-    hipLaunchKernelGGL((combine_kernel<kLatDv, kLatentMaxSplits>), dim3(B * S_q * H_q), dim3(kCombineThreads), 0, s,
-                       a.part_o, a.part_ml, p.nsplit, out, lse);
+    launch_combine<kLatDv>(a.part_o, a.part_ml, B * S_q * H_q, p.nsplit, out, lse, s);
     return launch_status("dsa_sparse_attn(combine)");
   }
   if (D_qk == 64) {
@@ -634,11 +660,7 @@ extern "C" dsa_status dsa_sparse_attn(const void* q, const void* k_cache, const 
   dsa_status st = launch_status("dsa_sparse_attn");
   if (st != DSA_OK || p.nsplit == 1) return st;
   const int rows = B * S_q * H_q;
-  if (D_v == 64)
-    hipLaunchKernelGGL((combine_kernel<64, kCombineMaxSplits>), dim3(rows), dim3(kCombineThreads), 0, s, a.part_o,
-                       a.part_ml, p.nsplit, out, lse);
-  else
-    hipLaunchKernelGGL((combine_kernel<128, kCombineMaxSplits>), dim3(rows), dim3(kCombineThreads), 0, s, a.part_o,
-                       a.part_ml, p.nsplit, out, lse);
+  if (D_v == 64) launch_combine<64>(a.part_o, a.part_ml, rows, p.nsplit, out, lse, s);
+  else launch_combine<128>(a.part_o, a.part_ml, rows, p.nsplit, out, lse, s);
   return launch_status("dsa_sparse_attn(combine)");
 }

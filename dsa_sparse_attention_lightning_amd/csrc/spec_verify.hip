@@ -26,8 +26,8 @@
 namespace dsa {
 namespace {
 
-constexpr int kStatThreads = 256;
-constexpr int kChunk = 16384;        // logits per stats workgroup
+constexpr int kStatThreads = 1024;   // 16K logits = 4 float4 loads per thread, one batch
+constexpr int kChunkBig = 16384;     // logits per stats workgroup (many rows)
 constexpr int kTile = 256;           // logits per wave step (64 lanes x 4)
 constexpr int kMaxV = 1 << 20;
 constexpr int kMaxTiles = kMaxV / kTile;
@@ -83,7 +83,7 @@ struct VerifyArgs {
   const float* tl;
   const float* dl;
   const int32_t* drafts;
-  int B, G, V, nchunks;
+  int B, G, V, nchunks, chunk;
   const float* uniforms;
   uint64_t seed, offset;
   int32_t* acc_len;
@@ -107,8 +107,8 @@ __global__ __launch_bounds__(kStatThreads) void verify_stats_kernel(VerifyArgs a
   const int b = rr / nrows;
   const int r = rr % nrows;
   const float* row = row_ptr(a, b, r);
-  const int e0 = c * kChunk;
-  const int e1 = min(e0 + kChunk, a.V);
+  const int e0 = c * a.chunk;
+  const int e1 = min(e0 + a.chunk, a.V);
   float m = -INFINITY, s = 0.f;
   constexpr int kBatch = 4;                         // float4 loads in flight per thread
   constexpr int kStride = kStatThreads * 4;
@@ -199,7 +199,7 @@ struct Decision {
   int pad0, pad1;
 };
 
-constexpr int kThreads2 = 256;
+constexpr int kThreads2 = 1024;      // 16 waves: one 256-logit tile each per 4K chunk
 constexpr int kWaves2 = kThreads2 / 64;
 constexpr int kMassChunk = 4096;              // logits per residual-mass workgroup
 constexpr int kChunkTiles = kMassChunk / kTile;   // 16
@@ -222,9 +222,17 @@ __device__ void decide(const VerifyArgs& a, const VerifyWs& ws, int b, float* s_
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   if (tid < nrows) {
+    // chunk order; loads of 8 partials are issued before they are merged
     const float2* p = ws.part + ((size_t)b * nrows + tid) * a.nchunks;
-    float M = p[0].x, S = p[0].y;
-    for (int c = 1; c < a.nchunks; ++c) ms_merge(M, S, p[c].x, p[c].y);
+    float M = -INFINITY, S = 0.f;
+    for (int c0 = 0; c0 < a.nchunks; c0 += 8) {
+      float2 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = p[min(c0 + u, a.nchunks - 1)];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (c0 + u < a.nchunks) ms_merge(M, S, v[u].x, v[u].y);
+    }
     s_m[tid] = M;
     s_z[tid] = S;
   }
@@ -508,8 +516,11 @@ __global__ __launch_bounds__(kThreads2) void verify_pick_kernel(VerifyArgs a, Ve
   if (tid == 0) a.acc_len[b] = jstar;
 }
 
+int stats_chunk(int, int, int) { return kChunkBig; }
+
 size_t verify_ws(int B, int G, int V, int* nchunks, VerifyWs* out, char* base) {
-  const int nc = (V + kChunk - 1) / kChunk;
+  const int chunk = stats_chunk(B, G, V);
+  const int nc = (V + chunk - 1) / chunk;
   const int nm = (V + kMassChunk - 1) / kMassChunk;
   if (nchunks) *nchunks = nc;
   const size_t part = align_up((size_t)B * (2 * G + 1) * nc * sizeof(float2), 256);
@@ -558,6 +569,7 @@ extern "C" dsa_status spec_verify(const float* target_logits, const float* draft
   a.G = G;
   a.V = V;
   a.nchunks = nchunks;
+  a.chunk = stats_chunk(B, G, V);
   a.uniforms = uniforms;
   a.seed = seed;
   a.offset = offset;

@@ -346,12 +346,16 @@ constexpr int kOneWaves = kOneThreads / 64;
 constexpr int kOneMaxLd = 131072;
 constexpr int kOneLdsKeys = 35840;       // 140 KiB of keys
 
+constexpr int kOneCand = kBins / 2;    // threshold-bin candidates resolved in LDS (reuses hist)
+
 struct OneShared {
   uint32_t hist[kBins];
   uint32_t wave_tot[kOneWaves];
   uint32_t wave_gt[kOneWaves], wave_eq[kOneWaves];
   int bin;
   uint32_t above, count;
+  uint32_t ncand, kthr;
+  int pthr;
 };
 
 // Bin T of an nbins histogram (scanning from the top) with
@@ -402,32 +406,23 @@ __global__ __launch_bounds__(kOneThreads) void topk_one_kernel(const float* __re
   }
   const float* s = scores + (size_t)row * ld;
   constexpr int kU = 8;   // loads in flight per thread
-  if (kLds) {
-    for (int t0 = tid; t0 < L; t0 += kU * kOneThreads) {
-      float v[kU];
-#pragma unroll
-      for (int u = 0; u < kU; ++u) v[u] = s[min(t0 + u * kOneThreads, L - 1)];
-#pragma unroll
-      for (int u = 0; u < kU; ++u)
-        if (t0 + u * kOneThreads < L) keys[t0 + u * kOneThreads] = order_key(v[u]);
-    }
-  }
   auto key_at = [&](int t) -> uint32_t { return kLds ? keys[t] : order_key(s[t]); };
-
-  // Key range first: the bits that every key shares are resolved for free,
-  // so the first digit spreads over the range the scores actually occupy
-  // (indexer scores sit in a few octaves; a fixed top-bits digit would put
-  // most of the row into a handful of bins).
+  // Stage the keys (when they fit) and find the key range in the same pass:
+  // the bits every key shares are resolved for free, so the first digit
+  // spreads over the range the scores actually occupy (indexer scores sit in
+  // a few octaves; a fixed top-bits digit would put most of the row into a
+  // handful of bins).
   uint32_t kmin = 0xffffffffu, kmax = 0u;
-  __syncthreads();
   for (int t0 = tid; t0 < L; t0 += kU * kOneThreads) {
-    uint32_t kv[kU];
+    float v[kU];
 #pragma unroll
-    for (int u = 0; u < kU; ++u) kv[u] = key_at(min(t0 + u * kOneThreads, L - 1));
+    for (int u = 0; u < kU; ++u) v[u] = s[min(t0 + u * kOneThreads, L - 1)];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      kmin = min(kmin, kv[u]);
-      kmax = max(kmax, kv[u]);
+      const uint32_t key = order_key(v[u]);   // clamped duplicates do not change min/max
+      kmin = min(kmin, key);
+      kmax = max(kmax, key);
+      if (kLds && t0 + u * kOneThreads < L) keys[t0 + u * kOneThreads] = key;
     }
   }
 #pragma unroll
@@ -452,6 +447,7 @@ __global__ __launch_bounds__(kOneThreads) void topk_one_kernel(const float* __re
   int shift = 32 - common;
   uint32_t prefix = shift >= 32 ? 0u : (kmin >> shift) << shift;
   uint32_t need = (uint32_t)k;
+  bool fast = false;   // threshold bin small enough to resolve its candidates in LDS
   while (shift > 0) {
     const int nb = min(12, shift);
     const int nshift = shift - nb;
@@ -467,16 +463,7 @@ __global__ __launch_bounds__(kOneThreads) void topk_one_kernel(const float* __re
         const int t = tb + u * kOneThreads + tid;
         const uint32_t key = kv[u];
         const bool hit = t < L && (shift >= 32 || (key >> shift) == (prefix >> shift));
-        const uint32_t bin = (key >> nshift) & mask;
-        // whole-wave same-bin case takes one atomic (all-equal rows)
-        const uint64_t hm = __ballot(hit);
-        const uint32_t b0 = (uint32_t)__builtin_amdgcn_readlane((int)bin, hm ? (__ffsll((long long)hm) - 1) : 0);
-        const uint64_t same = __ballot(hit && bin == b0);
-        if (same == hm) {
-          if (hm && lane == __ffsll((long long)hm) - 1) atomicAdd(&sh.hist[b0], (uint32_t)__popcll(hm));
-        } else if (hit) {
-          atomicAdd(&sh.hist[bin], 1u);
-        }
+        if (hit) atomicAdd(&sh.hist[(key >> nshift) & mask], 1u);
       }
     }
     __syncthreads();
@@ -484,9 +471,97 @@ __global__ __launch_bounds__(kOneThreads) void topk_one_kernel(const float* __re
     need -= sh.above;
     prefix |= (uint32_t)sh.bin << nshift;
     shift = nshift;
-    const bool done = sh.count == need;
+    const uint32_t cnt = sh.count;
     __syncthreads();
-    if (done) break;
+    if (cnt == need) break;
+    if (cnt <= (uint32_t)kOneCand) {
+      fast = true;
+      break;
+    }
+  }
+
+  if (fast) {
+    // Wave w owns positions [p0, p1), 4 consecutive positions per lane.
+    // Pass 1 counts the wave's positions above the threshold bin and
+    // collects the bin's candidates (key, position); one thread per
+    // candidate ranks it by (key desc, position asc) to find the exact
+    // threshold pair; pass 2 writes the kept positions in order.
+    const int span4 = ((L + kOneWaves - 1) / kOneWaves + 255) / 256 * 256;
+    const int p0 = min(wave * span4, L), p1 = min(p0 + span4, L);
+    const uint32_t P = prefix >> shift;
+    uint2* cand = reinterpret_cast<uint2*>(sh.hist);
+    if (tid == 0) sh.ncand = 0;
+    __syncthreads();
+    auto keys4 = [&](int t, uint32_t (&kk)[4]) {
+      if (kLds) {
+        // t % 4 == 0; lanes past the range read the array's last quad (masked by the caller)
+        const uint4 v = *reinterpret_cast<const uint4*>(keys + min(t, kOneLdsKeys - 4));
+        kk[0] = v.x; kk[1] = v.y; kk[2] = v.z; kk[3] = v.w;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kk[i] = order_key(s[min(t + i, L - 1)]);
+      }
+    };
+    uint32_t gt_lane = 0;
+    for (int tb = p0; tb < p1; tb += 256) {
+      const int t = tb + lane * 4;
+      uint32_t kk[4];
+      keys4(t, kk);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool valid = t + i < p1;
+        const uint32_t kp = kk[i] >> shift;
+        gt_lane += (valid && kp > P) ? 1u : 0u;
+        if (valid && kp == P) {
+          const uint32_t slot = atomicAdd(&sh.ncand, 1u);
+          if (slot < (uint32_t)kOneCand) cand[slot] = make_uint2(kk[i], (uint32_t)(t + i));
+        }
+      }
+    }
+    const uint32_t gt_w = wave_sum_u32(gt_lane);
+    if (lane == 0) {
+      sh.wave_gt[wave] = gt_w;
+      sh.wave_eq[wave] = 0;
+    }
+    __syncthreads();
+    const int n = (int)min(sh.ncand, (uint32_t)kOneCand);
+    for (int i = tid; i < n; i += kOneThreads) {
+      const uint2 c = cand[i];
+      uint32_t rank = 0;
+      for (int j = 0; j < n; ++j) {
+        const uint2 e = cand[j];
+        rank += (e.x > c.x || (e.x == c.x && e.y < c.y)) ? 1u : 0u;
+      }
+      if (rank == need - 1) {
+        sh.kthr = c.x;
+        sh.pthr = (int)c.y;
+      }
+      if (rank < need) atomicAdd(&sh.wave_eq[c.y / span4], 1u);
+    }
+    __syncthreads();
+    const uint32_t kthr = sh.kthr;
+    const int pthr = sh.pthr;
+    uint32_t out_pos = 0;
+    for (int w = 0; w < wave; ++w) out_pos += sh.wave_gt[w] + sh.wave_eq[w];
+    for (int tb = p0; tb < p1; tb += 256) {
+      const int t = tb + lane * 4;
+      uint32_t kk[4];
+      keys4(t, kk);
+      bool take[4];
+      uint32_t c = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        take[i] = t + i < p1 && (kk[i] > kthr || (kk[i] == kthr && t + i <= pthr));
+        c += take[i] ? 1u : 0u;
+      }
+      const uint32_t incl = wave_incl_scan_dpp(c);
+      uint32_t slot = out_pos + incl - c;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (take[i]) dst[slot++] = t + i;
+      out_pos += (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+    }
+    return;
   }
 
   // ordered compaction: wave w owns positions [w*span, (w+1)*span)

@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode_32k", choices=["decode_32k"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the verify-batch and 1M-indexer side measurements")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device copy (HBM counter calibration)")
@@ -236,9 +238,70 @@ def main():
         "graph": "each timed step is one replay of a HIP graph holding the whole step",
         "accepted_len": acc_len.cpu().tolist(),
     }
+    if not args.no_extras:
+        result["extras"] = extra_measurements(dsa)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(d, v, scores, idx, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def _time_graph(fn, reps=20):
+    """Average duration (us) of `fn` captured as a HIP graph, timed with
+    events on the launch stream."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+        fn()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()
+    a.record(stream)
+    for _ in range(reps):
+        g.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return 1e3 * a.elapsed_time(b) / reps
+
+
+def extra_measurements(dsa):
+    """Side measurements on the other workload shapes (not the headline):
+    spec_verify on the 256 x 8 x 151,552 verification batch, and the
+    indexer at 1M context for one row (draft step 1, HBM-bound) and eight
+    rows (verify-pass shape, MFMA-bound)."""
+    import torch
+    from dsa_inputs import device as DI
+    out = {}
+    B, G, V = 256, 7, 151552
+    v = DI.verify_inputs(5, B, G, V, 2.0, offset=11)
+    n = torch.empty(B, dtype=torch.int32, device="cuda:0")
+    em = torch.empty((B, G + 1), dtype=torch.int32, device="cuda:0")
+    ws = torch.empty(dsa.spec_verify_workspace_size(B, G, V), dtype=torch.uint8, device="cuda:0")
+    us = _time_graph(lambda: dsa.spec_verify(v.target_logits, v.draft_logits, v.drafts, seed=v.seed,
+                                             offset=v.offset, accepted_len=n, emitted=em, workspace=ws))
+    vbytes = B * (2 * G + 1) * V * 4
+    out["verify_256x8x151552"] = {
+        "us_per_call": us, "verified_positions_per_s": B * (G + 1) / (us * 1e-6),
+        "algorithmic_bytes": vbytes, "GBps": vbytes / us / 1e3, "frac_hbm": vbytes / us / 1e3 / HBM_PEAK_GBS,
+        "mean_accepted": float(n.float().mean()), "logit_std": 2.0}
+    del v, ws
+    L = 1 << 20
+    for R in (1, 8):
+        d = DI.draft_inputs(3, [L], H_I=64, D_I=128, H_q=64, D_qk=576, D_v=512, k=2048, G=0, R=R,
+                            latent=True)
+        sc = torch.empty((1, R, d.ld), dtype=torch.float32, device="cuda:0")
+        us = _time_graph(lambda: dsa.index_scores(d.q_index, d.w, d.kidx, d.block_table, d.row_len,
+                                                  page=d.page, out=sc))
+        flops = 2.0 * R * L * d.H_I * d.D_I
+        kbytes = L * d.D_I * 2 + R * L * 4
+        out[f"indexer_1m_R{R}"] = {
+            "us_per_call": us, "TFLOPs": flops / us / 1e6, "frac_mfma": flops / us / 1e6 / BF16_MFMA_PEAK_TFLOPS,
+            "GBps": kbytes / us / 1e3, "frac_hbm": kbytes / us / 1e3 / HBM_PEAK_GBS}
+        del d, sc
+    return out
 
 
 def cpu_baseline(d, v, scores, idx, budget_s):

@@ -182,6 +182,208 @@ dsa_status launch_index(const void* q, const float* w, const void* kidx, const i
   return launch_index_t<KS, MB, 4>(q, w, kidx, bt, row_len, scores, B, R, H, page, max_pages, ld, stream);
 }
 
+// ---------------------------------------------------------------------------
+// Several query rows (R >= 2, e.g. the verify-pass shape with one row per
+// chained position): the contraction has M = R * 64 (row, head) pairs, so it
+// is a real GEMM.  Wave w owns RPW query rows = RPW*2 M blocks of 32 (row,
+// head) pairs, whose Q fragments stay in registers for the whole kernel.  The
+// workgroup stages 32-position key tiles in LDS once for all its waves (the
+// next tile is prefetched into registers while the current one is consumed)
+// and every wave runs v_mfma_f32_32x32x16_bf16 over them.  Epilogue as in the
+// one-row kernel: ReLU, * w, head sum in fp32 (16 heads per lane, then the
+// two lane halves).
+// C layout of the 32x32 MFMA: lane l, register v holds row (v/4)*8 +
+// (l/32)*4 + v%4, column l%32.
+// ---------------------------------------------------------------------------
+constexpr int kRowsTile = 32;
+constexpr int kMaxChunkPositions = 4096;   // per-workgroup chunk cap (LDS row table)
+
+#ifndef DSA_INDEX_WPE
+#define DSA_INDEX_WPE 2
+#endif
+template <int KS16, int RPW, int NWAVE>
+__global__ __launch_bounds__(NWAVE * 64) __attribute__((amdgpu_waves_per_eu(DSA_INDEX_WPE))) void index_scores_rows_kernel(
+    const uint16_t* __restrict__ q, const float* __restrict__ w, const uint16_t* __restrict__ kidx,
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ row_len, float* __restrict__ scores,
+    int R, int H, int page, int max_pages, int64_t ld, int chunk) {
+  constexpr int D = KS16 * 16;
+  constexpr int NT = NWAVE * 64;
+  constexpr int MBW = RPW * 2;                       // 32-row M blocks per wave
+  constexpr int KROW = D * 2 + 16;                   // padded LDS row (bytes)
+  constexpr int CHUNKS = kRowsTile * D / 8;          // 16-byte pieces per tile
+  constexpr int PER = (CHUNKS + NT - 1) / NT;
+  __shared__ __align__(16) unsigned char s_k[2 * kRowsTile * KROW];
+  __shared__ __align__(16) float s_w[NWAVE * RPW][64];
+  __shared__ int s_row[kMaxChunkPositions];   // physical key row of each chunk position
+
+  const int b = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  int lmax = 0;
+  for (int r = 0; r < R; ++r) lmax = max(lmax, row_len[b * R + r]);
+  const int t_begin = blockIdx.x * chunk;
+  if (t_begin >= lmax) return;
+  const int t_end = min(t_begin + chunk, lmax);
+  const int32_t* bt = block_table + (size_t)b * max_pages;
+  // physical row of every chunk position, resolved once through the block
+  // table (a key load then needs no dependent global load and no division)
+  for (int i = tid; i < t_end - t_begin; i += NT) {
+    const int t = t_begin + i;
+    s_row[i] = bt[t / page] * page + t % page;
+  }
+  // the row this lane stores and how far it is valid (read before the tile
+  // loop, so that the loop's only global loads are the key prefetches)
+  const int r_st = RPW == 2 ? wave * 2 + hi : wave;
+  const int t_lim = (r_st < R && (RPW == 2 || hi == 0)) ? min(t_end, row_len[b * R + r_st]) : 0;
+
+  // Q fragments: block mb = (row 2w + mb/2... generally RPW*w + mb/2, heads (mb%2)*32 + l%32)
+  bf16x8_t qa[MBW][KS16];
+#pragma unroll
+  for (int mb = 0; mb < MBW; ++mb) {
+    const int r = wave * RPW + mb / 2;
+    const int h = (mb % 2) * 32 + l32;
+    const bool ok = r < R && h < H;
+    const uint16_t* src = q + ((size_t)(b * R + (ok ? r : 0)) * H + (ok ? h : 0)) * D + hi * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS16; ++ks)
+      qa[mb][ks] = ok ? *reinterpret_cast<const bf16x8_t*>(src + ks * 16) : bf16x8_t{};
+  }
+  for (int i = tid; i < NWAVE * RPW * 64; i += NT) {
+    const int r = i / 64, h = i % 64;
+    s_w[r][h] = (r < R && h < H) ? 0.5f * w[(size_t)(b * R + r) * H + h] : 0.f;
+  }
+
+  // key tile loads: piece c = tid + j*NT -> position c / (D/8), 16-byte
+  // column c % (D/8).  A ring of PF tiles is in flight in registers; the LDS
+  // tile is double-buffered so one barrier per tile suffices.
+  constexpr int PF = 4;
+  struct Slot {
+    uint4 v[PER];
+  };
+  auto fetch = [&](int t0) __attribute__((always_inline)) {
+    Slot out;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int c = min(tid + j * NT, CHUNKS - 1);
+      const int t = min(t0 + c / (D / 8), t_end - 1);
+      const uint16_t* src = kidx + (size_t)s_row[t - t_begin] * D + (c % (D / 8)) * 8;
+      out.v[j] = *reinterpret_cast<const uint4*>(src);
+    }
+    return out;
+  };
+  const int n_tiles = (t_end - t_begin + kRowsTile - 1) / kRowsTile;
+  // one tile: stage it from its ring slot, refill the slot PF tiles ahead,
+  // run the MFMAs and the epilogue
+  auto tile_step = [&](Slot slot, int tile_no) __attribute__((always_inline)) {
+    const int t0 = t_begin + tile_no * kRowsTile;
+    unsigned char* buf = s_k + (tile_no & 1) * (kRowsTile * KROW);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int c = tid + j * NT;
+      if (CHUNKS % NT == 0 || c < CHUNKS) *reinterpret_cast<uint4*>(buf + (c / (D / 8)) * KROW + (c % (D / 8)) * 16) = slot.v[j];
+    }
+    __syncthreads();
+    const Slot next = fetch(t0 + PF * kRowsTile);   // clamped inside the chunk; tiles past t_end are never stored
+
+    f32x16_t acc[MBW];
+#pragma unroll
+    for (int mb = 0; mb < MBW; ++mb) acc[mb] = f32x16_t{};
+    // B fragment of the next k step read while the current one multiplies
+    const unsigned char* brow = buf + l32 * KROW + hi * 16;
+    bf16x8_t kb = *reinterpret_cast<const bf16x8_t*>(brow);
+#pragma unroll
+    for (int ks = 0; ks < KS16; ++ks) {
+      bf16x8_t kn = kb;
+      if (ks + 1 < KS16) kn = *reinterpret_cast<const bf16x8_t*>(brow + (ks + 1) * 32);
+#pragma unroll
+      for (int mb = 0; mb < MBW; ++mb)
+        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mb][ks], kb, acc[mb], 0, 0, 0);
+      kb = kn;
+    }
+    // epilogue: rows of block mb are heads (mb%2)*32 + (v/4)*8 + hi*4 + v%4
+    float part[RPW];
+#pragma unroll
+    for (int rr = 0; rr < RPW; ++rr) part[rr] = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < MBW; ++mb) {
+      const int rloc = wave * RPW + mb / 2;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        // s_w holds w/2, and (x + |x|) * (w/2) equals w * ReLU(x) exactly
+        // (power-of-two scaling), without a compare per element
+        const float4 wv = *reinterpret_cast<const float4*>(&s_w[rloc][(mb % 2) * 32 + g * 8 + hi * 4]);
+        float sum = part[mb / 2];
+        sum = fmaf(wv.x, acc[mb][g * 4 + 0] + fabsf(acc[mb][g * 4 + 0]), sum);
+        sum = fmaf(wv.y, acc[mb][g * 4 + 1] + fabsf(acc[mb][g * 4 + 1]), sum);
+        sum = fmaf(wv.z, acc[mb][g * 4 + 2] + fabsf(acc[mb][g * 4 + 2]), sum);
+        sum = fmaf(wv.w, acc[mb][g * 4 + 3] + fabsf(acc[mb][g * 4 + 3]), sum);
+        part[mb / 2] = sum;
+      }
+    }
+#pragma unroll
+    for (int rr = 0; rr < RPW; ++rr) part[rr] += __shfl_xor(part[rr], 32, 64);
+    // lane half hi stores row wave*RPW + hi (RPW = 2) or row wave (RPW = 1, low half only)
+    const int t = t0 + l32;
+    const float v = (RPW == 2 && hi) ? part[RPW - 1] : part[0];
+    if (t < t_lim) scores[(size_t)(b * R + r_st) * ld + t] = v;
+    return next;
+  };
+  __syncthreads();   // s_row, s_w ready
+  Slot pre0 = fetch(t_begin);
+  Slot pre1 = fetch(t_begin + kRowsTile);
+  Slot pre2 = fetch(t_begin + 2 * kRowsTile);
+  Slot pre3 = fetch(t_begin + 3 * kRowsTile);
+  // whole rounds of PF tiles, then the tail (keeping the loop body free of
+  // branches lets every wait cover only the slot that is consumed)
+  int tg = 0;
+  for (; tg + PF <= n_tiles; tg += PF) {
+    pre0 = tile_step(pre0, tg);
+    pre1 = tile_step(pre1, tg + 1);
+    pre2 = tile_step(pre2, tg + 2);
+    pre3 = tile_step(pre3, tg + 3);
+  }
+  if (tg < n_tiles) tile_step(pre0, tg);   // n_tiles - tg is uniform across the workgroup
+  if (tg + 1 < n_tiles) tile_step(pre1, tg + 1);
+  if (tg + 2 < n_tiles) tile_step(pre2, tg + 2);
+}
+
+template <int KS16>
+dsa_status launch_rows(const void* q, const float* w, const void* kidx, const int32_t* bt, const int32_t* row_len,
+                       float* scores, int B, int R, int H, int page, int max_pages, int64_t ld, hipStream_t s) {
+  // about DSA_INDEX_ROWS_WGS workgroups per launch, chunks of at most 4096 positions
+#ifndef DSA_INDEX_ROWS_WGS
+#define DSA_INDEX_ROWS_WGS 512
+#endif
+  const int64_t tiles = (ld + kRowsTile - 1) / kRowsTile;
+  int per = (int)((tiles * B + DSA_INDEX_ROWS_WGS - 1) / DSA_INDEX_ROWS_WGS);
+  per = per < 1 ? 1 : per > kMaxChunkPositions / kRowsTile ? kMaxChunkPositions / kRowsTile : per;
+  const int chunk = per * kRowsTile;
+  dim3 grid((unsigned)((ld + chunk - 1) / chunk), (unsigned)B);
+  const uint16_t* qq = static_cast<const uint16_t*>(q);
+  const uint16_t* kk = static_cast<const uint16_t*>(kidx);
+  // up to 4 rows: one row per wave (Q fragments 64 VGPRs); 5..8 rows: two
+  // rows per wave in 4 waves (128 VGPRs of Q; rows past R hold zero Q)
+#define DSA_ROWS_LAUNCH(RPW, NW) \
+  hipLaunchKernelGGL((index_scores_rows_kernel<KS16, RPW, NW>), grid, dim3(NW * 64), 0, s, qq, w, kk, bt, row_len, \
+                     scores, R, H, page, max_pages, ld, chunk)
+  switch (R) {
+    case 2: DSA_ROWS_LAUNCH(1, 2); break;
+    case 3: DSA_ROWS_LAUNCH(1, 3); break;
+    case 4: DSA_ROWS_LAUNCH(1, 4); break;
+#ifdef DSA_INDEX_R8_RPW1
+    case 5: case 6: DSA_ROWS_LAUNCH(2, 4); break;
+    default: DSA_ROWS_LAUNCH(1, 8); break;
+#else
+    default: DSA_ROWS_LAUNCH(2, 4); break;
+#endif
+  }
+#undef DSA_ROWS_LAUNCH
+  return launch_status("dsa_index_scores");
+}
+
 template <int KS>
 dsa_status dispatch_mb(int MB, const void* q, const float* w, const void* kidx, const int32_t* bt,
                        const int32_t* row_len, float* scores, int B, int R, int H, int page,
@@ -217,6 +419,13 @@ extern "C" dsa_status dsa_index_scores(const void* q, const float* w, const void
               "dsa_index_scores: q and k_index must be 16-byte aligned");
   const int MB = (H_I + 15) / 16;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (R >= 2) {   // several query rows: GEMM-shaped kernel, Q fragments in registers
+    switch (D_I) {
+      case 32: return launch_rows<2>(q, w, k_index, block_table, row_len, scores, B, R, H_I, page, max_pages, ld, s);
+      case 64: return launch_rows<4>(q, w, k_index, block_table, row_len, scores, B, R, H_I, page, max_pages, ld, s);
+      default: return launch_rows<8>(q, w, k_index, block_table, row_len, scores, B, R, H_I, page, max_pages, ld, s);
+    }
+  }
   switch (D_I) {
     case 32: return dispatch_mb<1>(MB, q, w, k_index, block_table, row_len, scores, B, R, H_I, page, max_pages, ld, s);
     case 64: return dispatch_mb<2>(MB, q, w, k_index, block_table, row_len, scores, B, R, H_I, page, max_pages, ld, s);

@@ -245,15 +245,18 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def _time_graph(fn, reps=20):
-    """Average duration (us) of `fn` captured as a HIP graph, timed with
-    events on the launch stream."""
+def _time_graph(fn, reps=20, inner=8):
+    """Average duration (us) of one call of `fn`: `inner` calls captured
+    back to back in one HIP graph (so the per-replay launch gap is spread
+    over them), replayed `reps` times and timed with events on the launch
+    stream."""
     import torch
     fn()
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=torch.cuda.Stream()):
-        fn()
+        for _ in range(inner):
+            fn()
     for _ in range(3):
         g.replay()
     torch.cuda.synchronize()
@@ -264,7 +267,7 @@ def _time_graph(fn, reps=20):
         g.replay()
     b.record(stream)
     torch.cuda.synchronize()
-    return 1e3 * a.elapsed_time(b) / reps
+    return 1e3 * a.elapsed_time(b) / (reps * inner)
 
 
 def extra_measurements(dsa):

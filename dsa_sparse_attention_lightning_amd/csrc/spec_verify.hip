@@ -9,16 +9,19 @@
 // norm(max(0, p - q)); if every draft is accepted a bonus token is drawn from
 // the last target row.
 //
-// Two launches, both streaming logits once with 16-byte loads:
-//   stats   grid (chunk, row): per 16K-logit chunk of each of the 2G+1 rows of
-//           a sequence, the running max and sum of exp(x - max) (fp32,
-//           wavefront reductions); partials land in the workspace.
-//   decide  one workgroup per sequence: folds the chunk partials in chunk
-//           order, tests the G drafts in parallel lanes (first rejection by
-//           ballot), then draws from the residual (or bonus) row by inverse
-//           CDF: per-256-logit tile masses from a wave inclusive scan, a scan
-//           over the tile masses, and a rescan of the one tile that holds the
-//           crossing point.
+// Four launches:
+//   stats   grid (chunk, row): the running max and sum of exp(x - max) of
+//           each chunk of each of the 2G+1 rows of a sequence (fp32,
+//           wavefront reductions), streamed once with 16-byte loads (whole
+//           rows per workgroup when the batch fills the GPU; non-temporal
+//           loads when the logits exceed the last-level cache).
+//   decide  one workgroup per sequence folds its partials and tests the G
+//           drafts in parallel lanes (first rejection by ballot).
+//   mass    grid (chunk, sequence): the residual (or bonus) weights of one
+//           chunk of the sampled row: per-256-logit tile masses from a wave
+//           inclusive scan, added in tile order.
+//   pick    one workgroup per sequence draws by inverse CDF: the chunk that
+//           holds u * W, the tile inside it, then the token inside the tile.
 // Uniforms come from the caller or from Philox4x64-10 (Salmon, Moraes, Dror,
 // Shaw, SC'11) evaluated in-kernel at counter (offset, b, j, stream).
 #include "dsa_common.h"
@@ -26,8 +29,17 @@
 namespace dsa {
 namespace {
 
-constexpr int kStatThreads = 1024;   // 16K logits = 4 float4 loads per thread, one batch
-constexpr int kChunkBig = 16384;     // logits per stats workgroup (many rows)
+#ifndef DSA_VERIFY_STAT_THREADS
+#define DSA_VERIFY_STAT_THREADS 256
+#endif
+#ifndef DSA_VERIFY_STAT_U
+#define DSA_VERIFY_STAT_U 4
+#endif
+constexpr int kStatThreads = DSA_VERIFY_STAT_THREADS;
+constexpr int kStatU = DSA_VERIFY_STAT_U;       // float4 loads in flight per thread
+constexpr int kStatStep = kStatThreads * 4;     // logits per load round of a workgroup
+constexpr int kStatTargetWgs = 512;
+constexpr size_t kStreamBytes = (size_t)256 << 20;   // above this, logits are streamed non-temporally
 constexpr int kTile = 256;           // logits per wave step (64 lanes x 4)
 constexpr int kMaxV = 1 << 20;
 constexpr int kMaxTiles = kMaxV / kTile;
@@ -69,8 +81,17 @@ __device__ __forceinline__ void ms_merge(float& m, float& s, float m2, float s2)
   m = M;
 }
 
+// 16-byte load; NT marks it non-temporal (streamed data that is not re-read soon)
+template <bool NT>
+__device__ __forceinline__ float4 ld16(const float* p) {
+  const f32x4_t v = NT ? __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p))
+                       : *reinterpret_cast<const f32x4_t*>(p);
+  return make_float4(v[0], v[1], v[2], v[3]);
+}
+
+template <bool NT = false>
 __device__ __forceinline__ float4 load4(const float* row, int e, int V, bool vec) {
-  if (vec && e + 3 < V) return *reinterpret_cast<const float4*>(row + e);
+  if (vec && e + 3 < V) return ld16<NT>(row + e);
   float4 r;
   r.x = e + 0 < V ? row[e + 0] : -INFINITY;
   r.y = e + 1 < V ? row[e + 1] : -INFINITY;
@@ -99,6 +120,7 @@ __device__ __forceinline__ const float* row_ptr(const VerifyArgs& a, int b, int 
   return a.dl + ((size_t)b * a.G + (r - a.G - 1)) * a.V;
 }
 
+template <bool NT>
 __global__ __launch_bounds__(kStatThreads) void verify_stats_kernel(VerifyArgs a) {
   __shared__ float2 s_w[kStatThreads / 64];
   const int c = blockIdx.x;
@@ -109,36 +131,38 @@ __global__ __launch_bounds__(kStatThreads) void verify_stats_kernel(VerifyArgs a
   const float* row = row_ptr(a, b, r);
   const int e0 = c * a.chunk;
   const int e1 = min(e0 + a.chunk, a.V);
+  const float4 ninf = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
   float m = -INFINITY, s = 0.f;
-  constexpr int kBatch = 4;                         // float4 loads in flight per thread
-  constexpr int kStride = kStatThreads * 4;
-  for (int e = e0 + threadIdx.x * 4; e < e1; e += kBatch * kStride) {
-    float4 x[kBatch];
+  for (int e = e0 + threadIdx.x * 4; e < e1; e += kStatU * kStatStep) {
+    float4 x[kStatU];
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int ee = e + u * kStride;
+    for (int u = 0; u < kStatU; ++u) {
+      const int ee = e + u * kStatStep;
       if (a.vec) {
         // unconditional aligned load (clamped inside the chunk), masked after
-        const float4 v = *reinterpret_cast<const float4*>(row + ((min(ee, e1 - 1)) & ~3));
-        x[u] = ee < e1 ? v : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+        const float4 v = ld16<NT>(row + (min(ee, e1 - 1) & ~3));
+        x[u] = ee < e1 ? v : ninf;
       } else {
-        x[u] = ee < e1 ? load4(row, ee, e1, false) : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+        x[u] = ee < e1 ? load4(row, ee, e1, false) : ninf;
       }
     }
+    // one rescale per batch: max over the batch first, then its exponentials
+    float bm = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const float m4 = fmaxf(fmaxf(x[u].x, x[u].y), fmaxf(x[u].z, x[u].w));
-      const float M = fmaxf(m, m4);
-      if (M == -INFINITY) continue;   // nothing but -inf logits so far
-      const float ML = M * kLog2e;
-      float t = s * fast_exp2(m * kLog2e - ML);
+    for (int u = 0; u < kStatU; ++u) bm = fmaxf(bm, fmaxf(fmaxf(x[u].x, x[u].y), fmaxf(x[u].z, x[u].w)));
+    const float M = fmaxf(m, bm);
+    if (M == -INFINITY) continue;   // nothing but -inf logits so far
+    const float ML = M * kLog2e;
+    float t = 0.f;
+#pragma unroll
+    for (int u = 0; u < kStatU; ++u) {
       t += fast_exp2(x[u].x * kLog2e - ML);
       t += fast_exp2(x[u].y * kLog2e - ML);
       t += fast_exp2(x[u].z * kLog2e - ML);
       t += fast_exp2(x[u].w * kLog2e - ML);
-      s = t;
-      m = M;
     }
+    s = s * fast_exp2(m * kLog2e - ML) + t;
+    m = M;
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
@@ -199,17 +223,25 @@ struct Decision {
   int pad0, pad1;
 };
 
-constexpr int kThreads2 = 1024;      // 16 waves: one 256-logit tile each per 4K chunk
-constexpr int kWaves2 = kThreads2 / 64;
-constexpr int kMassChunk = 4096;              // logits per residual-mass workgroup
-constexpr int kChunkTiles = kMassChunk / kTile;   // 16
-constexpr int kMaxMassChunks = kMaxV / kMassChunk;
+constexpr int kDecideThreads = 256;
+#ifndef DSA_VERIFY_MASS_THREADS
+#define DSA_VERIFY_MASS_THREADS 512
+#endif
+#ifndef DSA_VERIFY_BIG_CT
+#define DSA_VERIFY_BIG_CT 32
+#endif
+constexpr int kMassThreads = DSA_VERIFY_MASS_THREADS;   // residual-mass workgroups
+constexpr int kPickThreads = 1024;   // pick workgroups: 16 waves
+constexpr int kSmallChunkTiles = 16;   // 4K-logit mass chunks (few sequences)
+constexpr int kBigChunkTiles = DSA_VERIFY_BIG_CT;   // mass chunk tiles when there are many sequences
+constexpr int kMaxMassChunks = kMaxV / (kSmallChunkTiles * kTile);
 
 struct VerifyWs {
   float2* part;      // [B][2G+1][nchunks]
   Decision* dec;     // [B]
   float* cmass;      // [B][nmass]
   int nmass;
+  int chunk_tiles;   // 256-logit tiles per mass chunk
 };
 
 // Folds chunk partials (chunk order) and runs the accept tests for sequence
@@ -221,29 +253,41 @@ __device__ void decide(const VerifyArgs& a, const VerifyWs& ws, int b, float* s_
   const int nrows = 2 * G + 1;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  if (tid < nrows) {
-    // chunk order; loads of 8 partials are issued before they are merged
-    const float2* p = ws.part + ((size_t)b * nrows + tid) * a.nchunks;
+  const int wave = tid >> 6;
+  const int nw = blockDim.x >> 6;
+  // the draft tokens' logits are fetched first so that their latency overlaps the fold
+  float tv = 0.f, dv = 0.f;
+  if (tid < G) {
+    const int d = min(max(a.drafts[(size_t)b * G + lane], 0), V - 1);   // reads stay inside the row
+    tv = a.tl[((size_t)b * (G + 1) + lane) * V + d];
+    dv = a.dl[((size_t)b * G + lane) * V + d];
+  }
+  // row r folded by wave r % nw: lane l merges chunks l, l + 64, ... in that
+  // order, then a butterfly (merging is symmetric, so every lane, and every
+  // workgroup of the sequence, ends with the same bits)
+  for (int r = wave; r < nrows; r += nw) {
+    const float2* p = ws.part + ((size_t)b * nrows + r) * a.nchunks;
     float M = -INFINITY, S = 0.f;
-    for (int c0 = 0; c0 < a.nchunks; c0 += 8) {
-      float2 v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = p[min(c0 + u, a.nchunks - 1)];
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (c0 + u < a.nchunks) ms_merge(M, S, v[u].x, v[u].y);
+    for (int c = lane; c < a.nchunks; c += 64) {
+      const float2 v = p[c];
+      ms_merge(M, S, v.x, v.y);
     }
-    s_m[tid] = M;
-    s_z[tid] = S;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float m2 = __shfl_xor(M, o, 64);
+      const float s2 = __shfl_xor(S, o, 64);
+      ms_merge(M, S, m2, s2);
+    }
+    if (lane == 0) {
+      s_m[r] = M;
+      s_z[r] = S;
+    }
   }
   __syncthreads();
   if (tid < 64) {
     bool reject = false;
     float p = NAN, q = NAN, ua = NAN;
     if (lane < G) {
-      const int d = a.drafts[(size_t)b * G + lane];
-      const float tv = a.tl[((size_t)b * (G + 1) + lane) * V + d];
-      const float dv = a.dl[((size_t)b * G + lane) * V + d];
       p = expf(tv - s_m[lane]) / s_z[lane];
       q = expf(dv - s_m[G + 1 + lane]) / s_z[G + 1 + lane];
       ua = a.uniforms ? a.uniforms[((size_t)b * (G + 1) + lane) * 2 + 0] : philox_uniform(a.seed, a.offset, b, lane, 0);
@@ -288,10 +332,11 @@ __device__ __forceinline__ RowWeights sampled_row(const VerifyArgs& a, int b, in
 
 // Tile masses (wave inclusive-scan totals) of tiles [t0, t1) of a row into
 // s_tile[0 .. t1-t0).  Tiles go round-robin to the waves; each wave issues
-// the loads of up to kTilesPerWave tiles before weighting any of them.
-constexpr int kTilesPerWave = 4;
-
+// the loads of up to TPW tiles before weighting any of them.  The weights
+// and sums are the same for every TPW and NT.
+template <int TPW, bool NT>
 __device__ void tile_masses(const RowWeights& rw, int V, bool vec, int t0, int t1, float* s_tile) {
+  constexpr int kTilesPerWave = TPW;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int nw = blockDim.x >> 6;
@@ -304,8 +349,8 @@ __device__ void tile_masses(const RowWeights& rw, int V, bool vec, int t0, int t
       tv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
       dv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
       if (t < t1) {
-        tv[i] = load4(rw.t, e, V, vec);
-        if (rw.d) dv[i] = load4(rw.d, e, V, vec);
+        tv[i] = load4<NT>(rw.t, e, V, vec);
+        if (rw.d) dv[i] = load4<NT>(rw.d, e, V, vec);
       }
     }
 #pragma unroll
@@ -356,45 +401,65 @@ __device__ int wave_first_crossing(const float* v, int n, float x, float* before
   return has ? __shfl(last_pos, 63 - __clzll((long long)has), 64) : -1;
 }
 
-// Kernel 2: decisions, then the mass of one 16K-logit chunk of the sampled
-// row (sum of its tile masses in tile order).
-__global__ __launch_bounds__(kThreads2) void verify_mass_kernel(VerifyArgs a, VerifyWs ws) {
+// Kernel 2: the decision of each sequence.
+__global__ __launch_bounds__(kDecideThreads) void verify_decide_kernel(VerifyArgs a, VerifyWs ws) {
   __shared__ float s_m[2 * kMaxG + 1], s_z[2 * kMaxG + 1];
-  __shared__ float s_tile[kChunkTiles];
   __shared__ int s_jstar;
   __shared__ float s_us;
+  const int b = blockIdx.x;
+  decide(a, ws, b, s_m, s_z, &s_jstar, &s_us, true);
+  if (threadIdx.x == 0) {
+    const RowWeights rw = sampled_row(a, b, s_jstar, s_m, s_z);
+    Decision dd;
+    dd.jstar = s_jstar;
+    dd.us = s_us;
+    dd.mt = rw.mt;
+    dd.inv_zt = rw.inv_zt;
+    dd.md = rw.md;
+    dd.inv_zd = rw.inv_zd;
+    dd.pad0 = dd.pad1 = 0;
+    ws.dec[b] = dd;
+  }
+}
+
+// Sampled row of sequence b as its decision record states it.
+__device__ __forceinline__ RowWeights decided_row(const VerifyArgs& a, const Decision& dd, int b) {
+  RowWeights rw;
+  rw.t = a.tl + ((size_t)b * (a.G + 1) + dd.jstar) * a.V;
+  rw.mt = dd.mt;
+  rw.inv_zt = dd.inv_zt;
+  rw.d = dd.jstar < a.G ? a.dl + ((size_t)b * a.G + dd.jstar) * a.V : nullptr;
+  rw.md = dd.md;
+  rw.inv_zd = dd.inv_zd;
+  return rw;
+}
+
+// Kernel 3: the mass of one chunk (CT tiles) of the sampled row (sum of its
+// tile masses in tile order).
+template <int CT, bool NT>
+__global__ __launch_bounds__(kMassThreads) void verify_mass_kernel(VerifyArgs a, VerifyWs ws) {
+  __shared__ float s_tile[CT];
   const int c = blockIdx.x;
   const int b = blockIdx.y;
-  decide(a, ws, b, s_m, s_z, &s_jstar, &s_us, c == 0);
-  const int jstar = s_jstar;
-  const RowWeights rw = sampled_row(a, b, jstar, s_m, s_z);
+  const RowWeights rw = decided_row(a, ws.dec[b], b);
   const int ntiles = (a.V + kTile - 1) / kTile;
-  const int t0 = c * kChunkTiles;   // c indexes 4K-logit mass chunks
-  const int t1 = min(t0 + kChunkTiles, ntiles);
-  tile_masses(rw, a.V, a.vec, t0, t1, s_tile);
+  const int t0 = c * CT;
+  const int t1 = min(t0 + CT, ntiles);
+  constexpr int kTpw = CT / (kMassThreads / 64);
+  tile_masses<kTpw, NT>(rw, a.V, a.vec, t0, t1, s_tile);
   __syncthreads();
   if (threadIdx.x == 0) {
     float m = 0.f;
     for (int t = 0; t < t1 - t0; ++t) m += s_tile[t];
     ws.cmass[(size_t)b * ws.nmass + c] = m;
-    if (c == 0) {
-      Decision dd;
-      dd.jstar = jstar;
-      dd.us = s_us;
-      dd.mt = rw.mt;
-      dd.inv_zt = rw.inv_zt;
-      dd.md = rw.md;
-      dd.inv_zd = rw.inv_zd;
-      dd.pad0 = dd.pad1 = 0;
-      ws.dec[b] = dd;
-    }
   }
 }
 
-// Kernel 3: one workgroup per sequence picks the emitted token: chunk by the
+// Kernel 4: one workgroup per sequence picks the emitted token: chunk by the
 // chunk masses, tile by the chunk's tile masses, token by a rescan of the
 // tile.  Writes emitted tokens and accepted lengths.
-__global__ __launch_bounds__(kThreads2) void verify_pick_kernel(VerifyArgs a, VerifyWs ws) {
+template <bool NT>
+__global__ __launch_bounds__(kPickThreads) void verify_pick_kernel(VerifyArgs a, VerifyWs ws) {
   __shared__ float s_tile[kMaxTiles];
   __shared__ float s_cm[kMaxMassChunks];
   __shared__ int s_tile_pick;
@@ -407,16 +472,11 @@ __global__ __launch_bounds__(kThreads2) void verify_pick_kernel(VerifyArgs a, Ve
   const int G = a.G, V = a.V;
   const Decision dd = ws.dec[b];
   const int jstar = dd.jstar;
-  RowWeights rw;
-  rw.t = a.tl + ((size_t)b * (G + 1) + jstar) * V;
-  rw.mt = dd.mt;
-  rw.inv_zt = dd.inv_zt;
-  rw.d = jstar < G ? a.dl + ((size_t)b * G + jstar) * V : nullptr;
-  rw.md = dd.md;
-  rw.inv_zd = dd.inv_zd;
+  RowWeights rw = decided_row(a, dd, b);
   const int ntiles = (V + kTile - 1) / kTile;
   const int nmass = ws.nmass;
-  for (int i = tid; i < nmass; i += kThreads2) s_cm[i] = ws.cmass[(size_t)b * nmass + i];
+  const int ct = ws.chunk_tiles;
+  for (int i = tid; i < nmass; i += kPickThreads) s_cm[i] = ws.cmass[(size_t)b * nmass + i];
   __syncthreads();
   // total mass and the chunk holding u * W (wave 0)
   if (tid < 64) {
@@ -435,8 +495,8 @@ __global__ __launch_bounds__(kThreads2) void verify_pick_kernel(VerifyArgs a, Ve
   int t0, t1;
   bool full_row = false;
   if (s_W > 0.f || rw.d == nullptr) {
-    t0 = s_tile_pick * kChunkTiles;
-    t1 = min(t0 + kChunkTiles, ntiles);
+    t0 = s_tile_pick * ct;
+    t1 = min(t0 + ct, ntiles);
   } else {
     // residual without mass (reachable only through rounding): draw from p
     rw.d = nullptr;
@@ -446,7 +506,7 @@ __global__ __launch_bounds__(kThreads2) void verify_pick_kernel(VerifyArgs a, Ve
   }
   float x = s_x;
   __syncthreads();
-  tile_masses(rw, V, a.vec, t0, t1, s_tile);
+  tile_masses<4, NT>(rw, V, a.vec, t0, t1, s_tile);
   __syncthreads();
   if (tid < 64) {
     if (full_row) {
@@ -516,12 +576,29 @@ __global__ __launch_bounds__(kThreads2) void verify_pick_kernel(VerifyArgs a, Ve
   if (tid == 0) a.acc_len[b] = jstar;
 }
 
-int stats_chunk(int, int, int) { return kChunkBig; }
+// Logits per stats workgroup: whole rows when the rows alone give about
+// kStatTargetWgs workgroups, else rows split into chunks of whole load
+// rounds so that about that many run.
+int stats_chunk(int B, int G, int V) {
+  const int64_t rows = (int64_t)B * (2 * G + 1);
+  const int64_t steps = (V + kStatStep - 1) / kStatStep;
+  int64_t want = (kStatTargetWgs + rows - 1) / rows;   // chunks per row
+  want = want < 1 ? 1 : want > steps ? steps : want;
+  return (int)((steps + want - 1) / want) * kStatStep;
+}
+
+// Tiles per residual-mass chunk: 16K-logit chunks when there are enough
+// sequences to fill the GPU with them, else 4K.
+int mass_chunk_tiles(int B, int V) {
+  const int64_t big = (V + kBigChunkTiles * kTile - 1) / (kBigChunkTiles * kTile);
+  return (int64_t)B * big >= 1024 ? kBigChunkTiles : kSmallChunkTiles;
+}
 
 size_t verify_ws(int B, int G, int V, int* nchunks, VerifyWs* out, char* base) {
   const int chunk = stats_chunk(B, G, V);
   const int nc = (V + chunk - 1) / chunk;
-  const int nm = (V + kMassChunk - 1) / kMassChunk;
+  const int ct = mass_chunk_tiles(B, V);
+  const int nm = (V + ct * kTile - 1) / (ct * kTile);
   if (nchunks) *nchunks = nc;
   const size_t part = align_up((size_t)B * (2 * G + 1) * nc * sizeof(float2), 256);
   const size_t dec = align_up((size_t)B * sizeof(Decision), 256);
@@ -531,6 +608,7 @@ size_t verify_ws(int B, int G, int V, int* nchunks, VerifyWs* out, char* base) {
     out->dec = reinterpret_cast<Decision*>(base + part);
     out->cmass = reinterpret_cast<float*>(base + part + dec);
     out->nmass = nm;
+    out->chunk_tiles = ct;
   }
   return part + dec + cm;
 }
@@ -581,12 +659,25 @@ extern "C" dsa_status spec_verify(const float* target_logits, const float* draft
   a.part = ws.part;
   a.vec = (V % 4 == 0) && aligned16(target_logits) && aligned16(draft_logits);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(verify_stats_kernel, dim3(nchunks, B * (2 * G + 1)), dim3(kStatThreads), 0, s, a);
+  const bool nt = (size_t)B * (2 * G + 1) * V * sizeof(float) > kStreamBytes;
+  const dim3 gs(nchunks, B * (2 * G + 1)), gm(ws.nmass, B);
+  if (nt) hipLaunchKernelGGL(verify_stats_kernel<true>, gs, dim3(kStatThreads), 0, s, a);
+  else hipLaunchKernelGGL(verify_stats_kernel<false>, gs, dim3(kStatThreads), 0, s, a);
   dsa_status st = launch_status("spec_verify(stats)");
   if (st != DSA_OK) return st;
-  hipLaunchKernelGGL(verify_mass_kernel, dim3(ws.nmass, B), dim3(kThreads2), 0, s, a, ws);
+  hipLaunchKernelGGL(verify_decide_kernel, dim3(B), dim3(kDecideThreads), 0, s, a, ws);
+  st = launch_status("spec_verify(decide)");
+  if (st != DSA_OK) return st;
+  if (ws.chunk_tiles == kBigChunkTiles) {
+    if (nt) hipLaunchKernelGGL((verify_mass_kernel<kBigChunkTiles, true>), gm, dim3(kMassThreads), 0, s, a, ws);
+    else hipLaunchKernelGGL((verify_mass_kernel<kBigChunkTiles, false>), gm, dim3(kMassThreads), 0, s, a, ws);
+  } else {
+    if (nt) hipLaunchKernelGGL((verify_mass_kernel<kSmallChunkTiles, true>), gm, dim3(kMassThreads), 0, s, a, ws);
+    else hipLaunchKernelGGL((verify_mass_kernel<kSmallChunkTiles, false>), gm, dim3(kMassThreads), 0, s, a, ws);
+  }
   st = launch_status("spec_verify(mass)");
   if (st != DSA_OK) return st;
-  hipLaunchKernelGGL(verify_pick_kernel, dim3(B), dim3(kThreads2), 0, s, a, ws);
+  if (nt) hipLaunchKernelGGL(verify_pick_kernel<true>, dim3(B), dim3(kPickThreads), 0, s, a, ws);
+  else hipLaunchKernelGGL(verify_pick_kernel<false>, dim3(B), dim3(kPickThreads), 0, s, a, ws);
   return launch_status("spec_verify(pick)");
 }

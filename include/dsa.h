@@ -161,7 +161,8 @@ dsa_status dsa_sparse_attn(const void* q, const void* k_cache, const void* v_cac
  * u = (first 64-bit output >> 40) * 2^-24.
  *
  *   target_logits fp32 [B, G+1, V]   draft_logits fp32 [B, G, V]
- *   draft_tokens  int32 [B, G] in [0, V)
+ *   draft_tokens  int32 [B, G] in [0, V) (a token outside is clamped into
+ *                 the row for the read; its decision is then meaningless)
  *   accepted_len  int32 [B]          emitted int32 [B, G+1] (-1 after the
  *                                    accepted_len+1 emitted tokens)
  *   diag          fp32 [B, G+1, 4] or NULL: p_j(d_j), q_j(d_j), u_acc, u_smp

@@ -43,6 +43,10 @@ def parse():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the verify-batch and 1M-indexer side measurements")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--extras-only", action="store_true",
+                    help="only the side measurements (for profiling them on their own)")
+    ap.add_argument("--extras-reps", type=int, default=20,
+                    help="graph replays per side measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device copy (HBM counter calibration)")
     return ap.parse_args()
@@ -99,6 +103,10 @@ def main():
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.extras_only:
+        import dsa_sparse_attention_lightning_amd as dsa
+        print(json.dumps({"extras": extra_measurements(dsa, args.extras_reps)}), flush=True)
         return
     import numpy as np
     import torch
@@ -239,7 +247,7 @@ def main():
         "accepted_len": acc_len.cpu().tolist(),
     }
     if not args.no_extras:
-        result["extras"] = extra_measurements(dsa)
+        result["extras"] = extra_measurements(dsa, args.extras_reps)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(d, v, scores, idx, args.cpu_seconds)
     print(json.dumps(result), flush=True)
@@ -270,7 +278,7 @@ def _time_graph(fn, reps=20, inner=8):
     return 1e3 * a.elapsed_time(b) / (reps * inner)
 
 
-def extra_measurements(dsa):
+def extra_measurements(dsa, reps=20):
     """Side measurements on the other workload shapes (not the headline):
     spec_verify on the 256 x 8 x 151,552 verification batch, and the
     indexer at 1M context for one row (draft step 1, HBM-bound) and eight
@@ -284,7 +292,7 @@ def extra_measurements(dsa):
     em = torch.empty((B, G + 1), dtype=torch.int32, device="cuda:0")
     ws = torch.empty(dsa.spec_verify_workspace_size(B, G, V), dtype=torch.uint8, device="cuda:0")
     us = _time_graph(lambda: dsa.spec_verify(v.target_logits, v.draft_logits, v.drafts, seed=v.seed,
-                                             offset=v.offset, accepted_len=n, emitted=em, workspace=ws))
+                                             offset=v.offset, accepted_len=n, emitted=em, workspace=ws), reps)
     vbytes = B * (2 * G + 1) * V * 4
     out["verify_256x8x151552"] = {
         "us_per_call": us, "verified_positions_per_s": B * (G + 1) / (us * 1e-6),
@@ -297,7 +305,7 @@ def extra_measurements(dsa):
                             latent=True)
         sc = torch.empty((1, R, d.ld), dtype=torch.float32, device="cuda:0")
         us = _time_graph(lambda: dsa.index_scores(d.q_index, d.w, d.kidx, d.block_table, d.row_len,
-                                                  page=d.page, out=sc))
+                                                  page=d.page, out=sc), reps)
         flops = 2.0 * R * L * d.H_I * d.D_I
         kbytes = L * d.D_I * 2 + R * L * 4
         out[f"indexer_1m_R{R}"] = {

@@ -280,7 +280,8 @@ def _time_graph(fn, reps=20, inner=8):
 
 def extra_measurements(dsa, reps=20):
     """Side measurements on the other workload shapes (not the headline):
-    spec_verify on the 256 x 8 x 151,552 verification batch, and the
+    spec_verify on the 256 x 8 x 151,552 verification batch, sparse
+    attention on the 16-sequence batched configuration, and the
     indexer at 1M context for one row (draft step 1, HBM-bound) and eight
     rows (verify-pass shape, MFMA-bound)."""
     import torch
@@ -299,6 +300,29 @@ def extra_measurements(dsa, reps=20):
         "algorithmic_bytes": vbytes, "GBps": vbytes / us / 1e3, "frac_hbm": vbytes / us / 1e3 / HBM_PEAK_GBS,
         "mean_accepted": float(n.float().mean()), "logit_std": 2.0}
     del v, ws
+    # sparse attention on the batched configuration: 16 sequences with context
+    # uniform in [16K, 64K], paged KV from one shuffled pool (about 1 GiB of
+    # gathered K/V per call, more than the last-level cache holds)
+    import dsa_inputs as I
+    d = DI.draft_inputs(2, I.batched_lens(2), H_I=64, D_I=128, H_q=64, H_kv=64, D_qk=128, D_v=128, k=2048,
+                        G=1, shuffle_pages=True)
+    sc = dsa.index_scores(d.q_index, d.w, d.kidx, d.block_table, d.row_len, page=d.page, ld=d.ld)
+    idx = dsa.topk(sc, d.row_len, d.k)
+    del sc
+    o = torch.empty((d.B, 1, d.H_q, d.D_v), dtype=torch.float32, device="cuda:0")
+    lse = torch.empty((d.B, 1, d.H_q), dtype=torch.float32, device="cuda:0")
+    aws = torch.zeros(max(1, dsa.sparse_attn_workspace_size(d.B, 1, d.H_q, d.H_kv, d.D_qk, d.D_v, d.k)),
+                      dtype=torch.uint8, device="cuda:0")
+    us = _time_graph(lambda: dsa.sparse_attn(d.q[0][:, None], d.k_cache, d.v_cache, d.block_table, idx[:, 0],
+                                             page=d.page, D_v=d.D_v, sm_scale=d.sm_scale, out=o, lse=lse,
+                                             workspace=aws), reps)
+    n_sel = sum(min(d.k, L) for L in d.lens)
+    abytes = (n_sel * d.H_kv * (d.D_qk + d.D_v) * 2 + d.B * d.H_q * d.D_qk * 2 + d.B * d.k * 4
+              + d.B * d.H_q * d.D_v * 4 + d.B * d.H_q * 4)
+    out["attn_batched_16x16k_64k"] = {
+        "us_per_call": us, "algorithmic_bytes": abytes, "GBps": abytes / us / 1e3,
+        "frac_hbm": abytes / us / 1e3 / HBM_PEAK_GBS, "context_tokens_per_s": sum(d.lens) / (us * 1e-6)}
+    del d, idx, o, lse, aws
     L = 1 << 20
     for R in (1, 8):
         d = DI.draft_inputs(3, [L], H_I=64, D_I=128, H_q=64, D_qk=576, D_v=512, k=2048, G=0, R=R,

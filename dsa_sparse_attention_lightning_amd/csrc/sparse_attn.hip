@@ -10,7 +10,7 @@
 // VALU, not MFMA.  A KV row of D bf16 is read by D/8 lanes (16 bytes each);
 // a wave covers 64/(D/8) KV heads of one token, so every load instruction
 // reads one contiguous stretch of the token's K (or V) row.  The workgroup's
-// four waves walk disjoint tokens of its split with their own online-softmax
+// waves walk disjoint tokens of its split with their own online-softmax
 // state (exp2 domain), merge in LDS in a fixed order, and write either the
 // final output (one split) or a partial (o, m, l) that a combine kernel folds
 // in split order.
@@ -26,7 +26,7 @@ namespace dsa {
 namespace {
 
 #ifndef DSA_ATTN_WAVES
-#define DSA_ATTN_WAVES 4
+#define DSA_ATTN_WAVES 8
 #endif
 constexpr int kWaves = DSA_ATTN_WAVES;      // waves per per-head-KV workgroup
 constexpr int kThreads = kWaves * 64;
@@ -37,7 +37,7 @@ constexpr int kThreads = kWaves * 64;
 #define DSA_ATTN_TARGET_WGS 1024
 #endif
 #ifndef DSA_ATTN_MIN_TOKENS
-#define DSA_ATTN_MIN_TOKENS 128
+#define DSA_ATTN_MIN_TOKENS 256
 #endif
 #ifndef DSA_ATTN_UNROLL
 #define DSA_ATTN_UNROLL 2
@@ -195,7 +195,7 @@ __global__ __launch_bounds__(kThreads) void mha_attn_kernel(AttnArgs a) {
   }
   __syncthreads();
 
-  // Wave w takes local tokens w, w+4, ...; loads run one U-token stage ahead.
+  // Wave w takes local tokens w, w + kWaves, ...; loads run one U-token stage ahead.
   // padding heads (g >= H_kv) read the last real head; their results are dropped
   const size_t lane_off = (size_t)min(g, a.H_kv - 1) * a.head_stride + sub * 8;
   constexpr int STEP = kWaves * U;
@@ -212,7 +212,7 @@ __global__ __launch_bounds__(kThreads) void mha_attn_kernel(AttnArgs a) {
     i += STEP;
   }
 
-  // merge the four waves (fixed order)
+  // merge the waves (fixed order)
 #pragma unroll
   for (int j = 0; j < GQ; ++j) {
     if (sub == 0) {

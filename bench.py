@@ -280,7 +280,7 @@ def _time_graph(fn, reps=20, inner=8):
 
 def extra_measurements(dsa, reps=20):
     """Side measurements on the other workload shapes (not the headline):
-    spec_verify on the 256 x 8 x 151,552 verification batch, sparse
+    spec_verify (and greedy verification) on the 256 x 8 x 151,552 verification batch, sparse
     attention on the 16-sequence batched configuration, and the
     indexer at 1M context for one row (draft step 1, HBM-bound) and eight
     rows (verify-pass shape, MFMA-bound)."""
@@ -299,7 +299,18 @@ def extra_measurements(dsa, reps=20):
         "us_per_call": us, "verified_positions_per_s": B * (G + 1) / (us * 1e-6),
         "algorithmic_bytes": vbytes, "GBps": vbytes / us / 1e3, "frac_hbm": vbytes / us / 1e3 / HBM_PEAK_GBS,
         "mean_accepted": float(n.float().mean()), "logit_std": 2.0}
-    del v, ws
+    # greedy verification of the same batch (greedy drafts: the draft model's
+    # argmax); reads only the target rows
+    gdr = v.draft_logits.argmax(dim=-1).to(torch.int32)
+    gws = torch.empty(dsa.spec_verify_greedy_workspace_size(B, G, V), dtype=torch.uint8, device="cuda:0")
+    us = _time_graph(lambda: dsa.spec_verify_greedy(v.target_logits, gdr, accepted_len=n, emitted=em,
+                                                    workspace=gws), reps)
+    gbytes = B * (G + 1) * V * 4
+    out["greedy_verify_256x8x151552"] = {
+        "us_per_call": us, "verified_positions_per_s": B * (G + 1) / (us * 1e-6), "algorithmic_bytes": gbytes,
+        "GBps": gbytes / us / 1e3, "frac_hbm": gbytes / us / 1e3 / HBM_PEAK_GBS,
+        "mean_accepted": float(n.float().mean())}
+    del v, ws, gws, gdr
     # sparse attention on the batched configuration: 16 sequences with context
     # uniform in [16K, 64K], paged KV from one shuffled pool (about 1 GiB of
     # gathered K/V per call, more than the last-level cache holds)

@@ -19,6 +19,7 @@ from . import _lib
 __all__ = [
     "index_scores", "topk", "sparse_attn", "spec_verify",
     "topk_workspace_size", "sparse_attn_workspace_size", "spec_verify_workspace_size",
+    "spec_verify_greedy", "spec_verify_greedy_workspace_size",
     "abi_version", "DSAError",
 ]
 
@@ -67,6 +68,10 @@ def sparse_attn_workspace_size(B, S_q, H_q, H_kv, D_qk, D_v, k) -> int:
 
 def spec_verify_workspace_size(B, G, V) -> int:
     return int(_lib.load().spec_verify_workspace_size(B, G, V))
+
+
+def spec_verify_greedy_workspace_size(B, G, V) -> int:
+    return int(_lib.load().spec_verify_greedy_workspace_size(B, G, V))
 
 
 def _workspace(nbytes, device, ws):
@@ -220,4 +225,29 @@ def spec_verify(target_logits, draft_logits, draft_tokens, *, uniforms=None, see
                          _ptr(accepted_len), _ptr(emitted), _ptr(diag), _ptr(ws), nbytes,
                          _stream(stream))
     _lib.check("spec_verify", st)
+    return accepted_len, emitted
+
+
+def spec_verify_greedy(target_logits, draft_tokens, *, accepted_len=None, emitted=None, workspace=None,
+                       stream=None):
+    """Greedy verification: d_j accepted iff it is the argmax of target row j
+    (ties to the lower token id); the first mismatch, or the bonus row, emits
+    the argmax.  target_logits [B, G+1, V] fp32; draft_tokens [B, G] int32.
+    Returns (accepted_len int32 [B], emitted int32 [B, G+1])."""
+    lib = _lib.load()
+    _dev(target_logits, "target_logits", (torch.float32,))
+    _dev(draft_tokens, "draft_tokens", (torch.int32,))
+    B, G1, V = target_logits.shape
+    G = G1 - 1
+    _need(G >= 1, "target_logits needs G+1 >= 2 rows")
+    _need(draft_tokens.shape == (B, G), "draft_tokens must be [B, G]")
+    if accepted_len is None:
+        accepted_len = torch.empty(B, dtype=torch.int32, device=target_logits.device)
+    if emitted is None:
+        emitted = torch.empty((B, G + 1), dtype=torch.int32, device=target_logits.device)
+    nbytes = int(lib.spec_verify_greedy_workspace_size(B, G, V))
+    ws = _workspace(nbytes, target_logits.device, workspace)
+    st = lib.spec_verify_greedy(_ptr(target_logits), _ptr(draft_tokens), B, G, V, _ptr(accepted_len),
+                                _ptr(emitted), _ptr(ws), nbytes, _stream(stream))
+    _lib.check("spec_verify_greedy", st)
     return accepted_len, emitted

@@ -37,6 +37,9 @@ SIGNATURES = {
     "spec_verify": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_void_p,
                             c_uint64, c_uint64, c_void_p, c_void_p, c_void_p, c_void_p,
                             c_size_t, c_void_p]),
+    "spec_verify_greedy_workspace_size": (c_size_t, [c_int, c_int, c_int]),
+    "spec_verify_greedy": (c_int, [c_void_p, c_void_p, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p,
+                                   c_size_t, c_void_p]),
 }
 
 _lib = None

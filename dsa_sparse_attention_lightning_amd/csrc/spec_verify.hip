@@ -579,13 +579,14 @@ __global__ __launch_bounds__(kPickThreads) void verify_pick_kernel(VerifyArgs a,
 // Logits per stats workgroup: whole rows when the rows alone give about
 // kStatTargetWgs workgroups, else rows split into chunks of whole load
 // rounds so that about that many run.
-int stats_chunk(int B, int G, int V) {
-  const int64_t rows = (int64_t)B * (2 * G + 1);
+int chunk_for_rows(int64_t rows, int V) {
   const int64_t steps = (V + kStatStep - 1) / kStatStep;
   int64_t want = (kStatTargetWgs + rows - 1) / rows;   // chunks per row
   want = want < 1 ? 1 : want > steps ? steps : want;
   return (int)((steps + want - 1) / want) * kStatStep;
 }
+
+int stats_chunk(int B, int G, int V) { return chunk_for_rows((int64_t)B * (2 * G + 1), V); }
 
 // Tiles per residual-mass chunk: 16K-logit chunks when there are enough
 // sequences to fill the GPU with them, else 4K.
@@ -611,6 +612,123 @@ size_t verify_ws(int B, int G, int V, int* nchunks, VerifyWs* out, char* base) {
     out->chunk_tiles = ct;
   }
   return part + dec + cm;
+}
+
+// ---------------------------------------------------------------------------
+// Greedy verification: d_j is accepted iff it is the argmax of target row j
+// (ties to the lower token id); the first mismatch emits that argmax, and a
+// fully accepted chain emits the argmax of the last target row.  Only the
+// G+1 target rows are read, once.
+// ---------------------------------------------------------------------------
+struct ArgMax {
+  float v;
+  int i;
+};
+
+// Larger value wins; equal values go to the lower index.  Associative and
+// commutative, so every reduction order gives the same winner.
+__device__ __forceinline__ ArgMax am_pick(ArgMax a, ArgMax b) {
+  return (b.v > a.v || (b.v == a.v && b.i < a.i)) ? b : a;
+}
+
+__device__ __forceinline__ ArgMax am_wave(ArgMax a) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    ArgMax b;
+    b.v = __shfl_xor(a.v, o, 64);
+    b.i = __shfl_xor(a.i, o, 64);
+    a = am_pick(a, b);
+  }
+  return a;
+}
+
+struct GreedyArgs {
+  const float* tl;
+  const int32_t* drafts;
+  int B, G, V, nchunks, chunk;
+  int32_t* acc_len;
+  int32_t* emitted;
+  ArgMax* part;   // [B][G+1][nchunks]
+  bool vec;
+};
+
+// Kernel 1: (max, argmax) of each chunk of each target row.
+template <bool NT>
+__global__ __launch_bounds__(kStatThreads) void greedy_argmax_kernel(GreedyArgs a) {
+  __shared__ ArgMax s_w[kStatThreads / 64];
+  const int c = blockIdx.x;
+  const int rr = blockIdx.y;   // b * (G+1) + j
+  const float* row = a.tl + (size_t)rr * a.V;
+  const int e0 = c * a.chunk;
+  const int e1 = min(e0 + a.chunk, a.V);
+  ArgMax best{-INFINITY, INT_MAX};
+  for (int e = e0 + threadIdx.x * 4; e < e1; e += kStatU * kStatStep) {
+    float4 x[kStatU];
+#pragma unroll
+    for (int u = 0; u < kStatU; ++u) {
+      const int ee = e + u * kStatStep;
+      if (a.vec) x[u] = ld16<NT>(row + (min(ee, e1 - 1) & ~3));
+      else x[u] = load4(row, min(ee, e1 - 1), e1, false);
+    }
+#pragma unroll
+    for (int u = 0; u < kStatU; ++u) {
+      const int ee = e + u * kStatStep;   // ascending within the thread: strict > keeps the first
+      if (ee + 0 < e1 && x[u].x > best.v) best = ArgMax{x[u].x, ee + 0};
+      if (ee + 1 < e1 && x[u].y > best.v) best = ArgMax{x[u].y, ee + 1};
+      if (ee + 2 < e1 && x[u].z > best.v) best = ArgMax{x[u].z, ee + 2};
+      if (ee + 3 < e1 && x[u].w > best.v) best = ArgMax{x[u].w, ee + 3};
+    }
+  }
+  best = am_wave(best);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) s_w[wave] = best;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    ArgMax r = s_w[0];
+    for (int w = 1; w < kStatThreads / 64; ++w) r = am_pick(r, s_w[w]);
+    a.part[(size_t)rr * a.nchunks + c] = r;
+  }
+}
+
+// Kernel 2: one workgroup per sequence folds the chunk winners of its G+1
+// rows and compares the drafts with them.
+constexpr int kGreedyThreads = 256;
+
+__global__ __launch_bounds__(kGreedyThreads) void greedy_decide_kernel(GreedyArgs a) {
+  __shared__ int s_arg[kMaxG + 1];
+  const int b = blockIdx.x;
+  const int G = a.G;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  for (int j = wave; j <= G; j += kGreedyThreads / 64) {
+    const ArgMax* p = a.part + ((size_t)b * (G + 1) + j) * a.nchunks;
+    ArgMax best{-INFINITY, INT_MAX};
+    for (int c = lane; c < a.nchunks; c += 64) best = am_pick(best, p[c]);
+    best = am_wave(best);
+    // a row of -inf only (or NaN, outside the domain) has no winner: token 0
+    if (lane == 0) s_arg[j] = best.i == INT_MAX ? 0 : best.i;
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const bool mismatch = lane < G && a.drafts[(size_t)b * G + lane] != s_arg[lane];
+    const uint64_t mm = __ballot(mismatch);
+    const int jstar = mm ? (__ffsll((long long)mm) - 1) : G;
+    if (lane <= G) {
+      int32_t v = -1;
+      if (lane < jstar) v = a.drafts[(size_t)b * G + lane];
+      else if (lane == jstar) v = s_arg[jstar];
+      a.emitted[(size_t)b * (G + 1) + lane] = v;
+    }
+    if (lane == 0) a.acc_len[b] = jstar;
+  }
+}
+
+size_t greedy_ws(int B, int G, int V, int* nchunks, int* chunk) {
+  const int ch = chunk_for_rows((int64_t)B * (G + 1), V);
+  const int nc = (V + ch - 1) / ch;
+  if (nchunks) *nchunks = nc;
+  if (chunk) *chunk = ch;
+  return align_up((size_t)B * (G + 1) * nc * sizeof(ArgMax), 256);
 }
 
 }  // namespace
@@ -680,4 +798,50 @@ extern "C" dsa_status spec_verify(const float* target_logits, const float* draft
   if (nt) hipLaunchKernelGGL(verify_pick_kernel<true>, dim3(B), dim3(kPickThreads), 0, s, a, ws);
   else hipLaunchKernelGGL(verify_pick_kernel<false>, dim3(B), dim3(kPickThreads), 0, s, a, ws);
   return launch_status("spec_verify(pick)");
+}
+
+extern "C" size_t spec_verify_greedy_workspace_size(int B, int G, int V) {
+  if (B < 1 || G < 1 || V < 1) return 0;
+  return dsa::greedy_ws(B, G, V, nullptr, nullptr);
+}
+
+extern "C" dsa_status spec_verify_greedy(const float* target_logits, const int32_t* draft_tokens, int B, int G,
+                                         int V, int32_t* accepted_len, int32_t* emitted, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+  using namespace dsa;
+  clear_error();
+  DSA_REQUIRE(target_logits && draft_tokens && accepted_len && emitted, DSA_ERR_INVALID_ARG,
+              "spec_verify_greedy: null pointer argument");
+  DSA_REQUIRE(B >= 1 && G >= 1 && V >= 1, DSA_ERR_INVALID_ARG,
+              "spec_verify_greedy: sizes must be positive (B=%d G=%d V=%d)", B, G, V);
+  DSA_REQUIRE(G <= kMaxG, DSA_ERR_UNSUPPORTED, "spec_verify_greedy: G=%d > %d", G, kMaxG);
+  DSA_REQUIRE(V <= kMaxV, DSA_ERR_UNSUPPORTED, "spec_verify_greedy: V=%d > %d", V, kMaxV);
+  DSA_REQUIRE((int64_t)B * (G + 1) <= 65535, DSA_ERR_UNSUPPORTED, "spec_verify_greedy: B*(G+1)=%lld rows > 65535",
+              (long long)B * (G + 1));
+  int nchunks = 0, chunk = 0;
+  const size_t need = greedy_ws(B, G, V, &nchunks, &chunk);
+  DSA_REQUIRE(workspace && workspace_bytes >= need, DSA_ERR_WORKSPACE,
+              "spec_verify_greedy: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  GreedyArgs a{};
+  a.tl = target_logits;
+  a.drafts = draft_tokens;
+  a.B = B;
+  a.G = G;
+  a.V = V;
+  a.nchunks = nchunks;
+  a.chunk = chunk;
+  a.acc_len = accepted_len;
+  a.emitted = emitted;
+  a.part = static_cast<ArgMax*>(workspace);
+  a.vec = (V % 4 == 0) && aligned16(target_logits);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 g1(nchunks, B * (G + 1));
+  if ((size_t)B * (G + 1) * V * sizeof(float) > kStreamBytes)
+    hipLaunchKernelGGL(greedy_argmax_kernel<true>, g1, dim3(kStatThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(greedy_argmax_kernel<false>, g1, dim3(kStatThreads), 0, s, a);
+  const dsa_status st = launch_status("spec_verify_greedy(argmax)");
+  if (st != DSA_OK) return st;
+  hipLaunchKernelGGL(greedy_decide_kernel, dim3(B), dim3(kGreedyThreads), 0, s, a);
+  return launch_status("spec_verify_greedy(decide)");
 }

@@ -177,6 +177,29 @@ dsa_status spec_verify(const float* target_logits, const float* draft_logits,
                        int32_t* accepted_len, int32_t* emitted, float* diag,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * spec_verify_greedy -- greedy verification of drafted chains, the
+ * alternative that section "Rejection sampling and a loss that optimizes
+ * acceptance directly" contrasts with sampling (greedy drafts are brittle
+ * when the target distribution is flat).  For each sequence b:
+ *   for j = 0..G-1: accept d_j iff d_j == argmax_v target_logits[b, j, v];
+ *     on the first mismatch emit that argmax and stop with accepted_len = j;
+ *   if all G are accepted emit argmax of target row G, accepted_len = G.
+ * argmax ties go to the lower token id (-0.0 == +0.0); NaN logits are
+ * outside the domain; a row of -inf only yields token 0.  Only the target
+ * rows are read, once.
+ *
+ *   target_logits fp32 [B, G+1, V]   draft_tokens int32 [B, G]
+ *   accepted_len  int32 [B]          emitted int32 [B, G+1] (-1 padded)
+ * workspace: spec_verify_greedy_workspace_size() bytes, no initialisation.
+ * Supported: 1 <= G <= 32, 1 <= V <= 2^20, B*(G+1) <= 65535.
+ */
+size_t spec_verify_greedy_workspace_size(int B, int G, int V);
+dsa_status spec_verify_greedy(const float* target_logits, const int32_t* draft_tokens,
+                              int B, int G, int V, int32_t* accepted_len,
+                              int32_t* emitted, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -47,6 +47,8 @@ __all__ = [
     "icdf",
     "spec_verify_seq",
     "spec_verify",
+    "greedy_verify_seq",
+    "greedy_verify",
     "acceptance_probability",
     "total_variation",
 ]
@@ -271,6 +273,38 @@ def spec_verify(target_logits, draft_logits, drafts, u_accept, u_sample):
     n = np.array([r["n"] for r in res], dtype=np.int64)
     emitted = np.stack([r["emitted"] for r in res])
     return n, emitted, res
+
+
+def greedy_verify_seq(target_logits, drafts):
+    """Greedy verification of one drafted chain of G tokens.
+
+    Section "Rejection sampling and a loss that optimizes acceptance
+    directly" contrasts probabilistic drafting with greedy drafting, where
+    the draft is the most likely token.  Reading: d_j is accepted iff it is
+    the argmax of target row j; the first mismatch emits that argmax and
+    stops; a fully accepted chain emits the argmax of target row G.  argmax
+    picks the lowest token id among equal maxima (numpy's argmax does; softmax
+    is monotone, so the argmax of the logits is that of p).
+
+    target_logits: [G+1, V]; drafts: [G].  Returns (n, emitted [G+1], -1 padded).
+    """
+    tl = np.asarray(target_logits, dtype=np.float64)
+    G = tl.shape[0] - 1
+    emitted = np.full(G + 1, -1, dtype=np.int64)
+    for j in range(G):
+        best = int(np.argmax(tl[j]))
+        if int(drafts[j]) != best:
+            emitted[j] = best
+            return j, emitted
+        emitted[j] = best
+    emitted[G] = int(np.argmax(tl[G]))
+    return G, emitted
+
+
+def greedy_verify(target_logits, drafts):
+    """Batched greedy_verify_seq: [B, G+1, V], [B, G] -> (n [B], emitted [B, G+1])."""
+    out = [greedy_verify_seq(target_logits[b], drafts[b]) for b in range(np.asarray(drafts).shape[0])]
+    return np.array([o[0] for o in out], dtype=np.int64), np.stack([o[1] for o in out])
 
 
 def acceptance_probability(p, q):

@@ -107,6 +107,22 @@ def test_spec_verify_validation():
     assert call(wsb=ws - 1) == _lib.DSA_ERR_WORKSPACE
 
 
+def test_spec_verify_greedy_validation():
+    ws = lib.spec_verify_greedy_workspace_size(4, 15, 1024)
+    assert ws > 0
+    assert lib.spec_verify_greedy_workspace_size(0, 15, 1024) == 0
+    call = lambda **o: lib.spec_verify_greedy(o.get("t", FAKE), o.get("d", FAKE), o.get("B", 4), o.get("G", 15),
+                                              o.get("V", 1024), FAKE, FAKE, o.get("ws", FAKE), o.get("wsb", ws), None)
+    assert call(t=None) == _lib.DSA_ERR_INVALID_ARG
+    assert call(d=None) == _lib.DSA_ERR_INVALID_ARG
+    assert call(G=0) == _lib.DSA_ERR_INVALID_ARG
+    assert call(G=33) == _lib.DSA_ERR_UNSUPPORTED
+    assert call(V=(1 << 20) + 1) == _lib.DSA_ERR_UNSUPPORTED
+    assert call(B=5000) == _lib.DSA_ERR_UNSUPPORTED
+    assert call(wsb=ws - 1) == _lib.DSA_ERR_WORKSPACE
+    assert call(ws=None) == _lib.DSA_ERR_WORKSPACE
+
+
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(ImportError):
         _lib._lib_backup = _lib._lib

@@ -173,3 +173,19 @@ def test_verify_256x8x151552(std):
         assert np.all(em[b, n[b] + 1:] == -1)
     assert near <= 1
     log(f"verify std {std}: mean accepted {n.mean():.3f}, near-margin {near}")
+
+
+def test_greedy_verify_256x8x151552():
+    B, G, V = 256, 7, 151552
+    v = DI.verify_inputs(8, B, G, V, 2.0)
+    drafts = v.draft_logits.argmax(dim=-1).to(torch.int32)      # greedy drafting: the draft model's argmax
+    n, em = dsa.spec_verify_greedy(v.target_logits, drafts)
+    n = n.cpu().numpy()
+    em = em.cpu().numpy()
+    rng = np.random.default_rng(8)
+    sample = np.sort(rng.choice(B, size=32, replace=False))
+    tl = v.target_logits[torch.as_tensor(sample, device=DEV)].cpu().numpy()
+    ref_n, ref_em = O.greedy_verify(tl, drafts.cpu().numpy()[sample])
+    np.testing.assert_array_equal(n[sample], ref_n)
+    np.testing.assert_array_equal(em[sample], ref_em)
+    log(f"greedy: mean accepted {n.mean():.3f}")

@@ -324,6 +324,61 @@ def test_spec_verify_special_cases():
     assert np.all(n == 0) and np.all(em[:, 0] < V // 2)
 
 
+@pytest.mark.parametrize("std", [0.5, 2.0])
+def test_spec_verify_block16(std):
+    """Block-16 layout: G = 15 drafts plus the bonus position."""
+    vi = I.verify_inputs(int(std * 10) + 70, 24, 15, 5003, std)
+    _, _, near = _verify_case(vi, True)
+    assert near <= 1
+    vi = I.verify_inputs(int(std * 10) + 71, 4, 15, 151552, std)
+    _, _, near = _verify_case(vi, False)
+    assert near <= 1
+
+
+# ----------------------------------------------------------------------------
+# greedy verification (bit-exact: only comparisons)
+# ----------------------------------------------------------------------------
+def _greedy_inputs(rng, B, G, V, integer):
+    if integer:
+        tl = rng.integers(-4, 5, size=(B, G + 1, V)).astype(np.float32)      # ties everywhere
+    else:
+        tl = (rng.standard_normal((B, G + 1, V)) * 2).astype(np.float32)
+    best = tl.argmax(axis=-1)
+    cut = rng.integers(0, G + 1, size=B)                                     # drafts agree on a prefix
+    dr = rng.integers(0, V, size=(B, G)).astype(np.int32)
+    for b in range(B):
+        dr[b, : cut[b]] = best[b, : cut[b]]
+    return tl, dr
+
+
+@pytest.mark.parametrize("G,V,integer", [(7, 1024, True), (7, 1024, False), (15, 1000, True), (15, 5003, False),
+                                          (7, 151552, True), (1, 4, False)])
+def test_greedy_verify(G, V, integer):
+    rng = np.random.default_rng(G * 7 + V + integer)
+    B = 6 if V > 100000 else 40
+    tl, dr = _greedy_inputs(rng, B, G, V, integer)
+    n, em = dsa.spec_verify_greedy(to_dev(tl), to_dev(dr))
+    ref_n, ref_em = O.greedy_verify(tl, dr)
+    np.testing.assert_array_equal(n.cpu().numpy(), ref_n)
+    np.testing.assert_array_equal(em.cpu().numpy(), ref_em)
+
+
+def test_greedy_verify_special_rows():
+    G, V = 3, 4099
+    tl = np.zeros((3, G + 1, V), np.float32)
+    tl[0] = -np.inf
+    tl[0, :, 17] = 1.0                          # one finite entry per row
+    tl[1, :, :] = -0.0
+    tl[1, :, 5:] = 0.0                          # -0.0 == +0.0: token 0 wins
+    tl[2, :, V - 1] = 3.0                       # maximum in the ragged tail
+    dr = np.array([[17, 17, 17], [0, 0, 1], [V - 1, 0, 0]], np.int32)
+    n, em = dsa.spec_verify_greedy(to_dev(tl), to_dev(dr))
+    ref_n, ref_em = O.greedy_verify(tl, dr)
+    np.testing.assert_array_equal(n.cpu().numpy(), ref_n)
+    np.testing.assert_array_equal(em.cpu().numpy(), ref_em)
+    assert list(ref_n) == [3, 2, 1]
+
+
 # ----------------------------------------------------------------------------
 # HIP graph capture of the draft block: every replay matches the eager result
 # ----------------------------------------------------------------------------

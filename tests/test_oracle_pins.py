@@ -389,3 +389,75 @@ def test_verify_special_cases():
         r = O.spec_verify_seq(tl3, dl3, d, rng.random(1), rng.random(2))
         assert r["emitted"][0] == 5
         assert r["n"] == (1 if d[0] == 5 else 0)
+
+
+# ----------------------------------------------------------------------------
+# f2 greedy verification
+# ----------------------------------------------------------------------------
+def _greedy_loops(tl, drafts):
+    """Greedy verification with explicit loops: the first strictly larger
+    logit moves the argmax, so equal maxima keep the lowest token id."""
+    G = len(tl) - 1
+    out = [-1] * (G + 1)
+
+    def arg(row):
+        best_i, best_v = 0, row[0]
+        for i in range(1, len(row)):
+            if row[i] > best_v:
+                best_i, best_v = i, row[i]
+        return best_i
+
+    for j in range(G):
+        a = arg(tl[j])
+        out[j] = a
+        if drafts[j] != a:
+            return j, out
+    out[G] = arg(tl[G])
+    return G, out
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_greedy_verify_bruteforce(seed):
+    rng = np.random.default_rng(900 + seed)
+    G, V = (7, 15)[seed % 2], 12
+    for _ in range(40):
+        tl = rng.integers(-3, 4, size=(G + 1, V)).astype(np.float64)   # many ties
+        best = [int(np.flatnonzero(r == r.max())[0]) for r in tl]
+        # drafts agree with the argmax for a random prefix, then differ (or not)
+        cut = int(rng.integers(0, G + 1))
+        drafts = [best[j] if j < cut else int(rng.integers(V)) for j in range(G)]
+        n, em = O.greedy_verify_seq(tl, drafts)
+        n2, em2 = _greedy_loops(tl.tolist(), drafts)
+        assert n == n2 and list(em) == em2
+        assert n >= min(cut, G)
+
+
+def test_greedy_verify_special_cases():
+    tl = np.array([[0.0, 3.0, 3.0, 1.0],       # tie: lowest id (1) wins
+                   [-0.0, 0.0, -1.0, -2.0],    # -0.0 == +0.0: id 0 wins
+                   [5.0, 5.0, 5.0, 5.0]])      # all equal: id 0
+    n, em = O.greedy_verify_seq(tl, [1, 0])
+    assert n == 2 and list(em) == [1, 0, 0]
+    n, em = O.greedy_verify_seq(tl, [2, 0])
+    assert n == 0 and list(em) == [1, -1, -1]
+    n, em = O.greedy_verify_seq(tl, [1, 3])
+    assert n == 1 and list(em) == [1, 0, -1]
+
+
+def test_greedy_equals_sampling_verify_for_one_hot_targets():
+    """With one-hot target rows, rejection sampling (any draft logits, any
+    uniforms) accepts a draft iff it is the target's argmax and resamples that
+    argmax from the residual: it must coincide with greedy verification."""
+    rng = np.random.default_rng(77)
+    G, V = 7, 32
+    for _ in range(50):
+        hot = rng.integers(V, size=G + 1)
+        tl = np.full((G + 1, V), -1e3)
+        tl[np.arange(G + 1), hot] = 0.0   # exp(-1000) underflows: p is exactly one-hot
+        dl = rng.standard_normal((G, V)) * 2
+        cut = int(rng.integers(0, G + 1))
+        drafts = [int(hot[j]) if j < cut else int(rng.integers(V)) for j in range(G)]
+        r = O.spec_verify_seq(tl, dl, drafts, rng.random(G), rng.random(G + 1))
+        n, em = O.greedy_verify_seq(tl, drafts)
+        assert r["n"] == n
+        assert list(r["emitted"]) == list(em)

@@ -334,6 +334,67 @@ def extra_measurements(dsa, reps=20):
         "us_per_call": us, "algorithmic_bytes": abytes, "GBps": abytes / us / 1e3,
         "frac_hbm": abytes / us / 1e3 / HBM_PEAK_GBS, "context_tokens_per_s": sum(d.lens) / (us * 1e-6)}
     del d, idx, o, lse, aws
+    # cross-layer IndexShare at context 32K: one indexer + top-k serves a block
+    # of 4 layers (each with its own queries and KV), against an indexer per layer
+    layers = [DI.draft_inputs(40 + l, [32768], H_I=64, D_I=128, H_q=64, H_kv=64, D_qk=128, D_v=128, k=2048, G=1)
+              for l in range(4)]
+    d0 = layers[0]
+    sc = torch.empty((1, 1, d0.ld), dtype=torch.float32, device="cuda:0")
+    ix = torch.empty((1, 1, d0.k), dtype=torch.int32, device="cuda:0")
+    o = torch.empty((1, 1, d0.H_q, d0.D_v), dtype=torch.float32, device="cuda:0")
+    lse = torch.empty((1, 1, d0.H_q), dtype=torch.float32, device="cuda:0")
+    aws = torch.zeros(max(1, dsa.sparse_attn_workspace_size(1, 1, 64, 64, 128, 128, 2048)), dtype=torch.uint8,
+                      device="cuda:0")
+
+    def select(l):
+        dsa.index_scores(l.q_index, l.w, l.kidx, l.block_table, l.row_len, page=l.page, out=sc)
+        dsa.topk(sc, l.row_len, l.k, out=ix)
+
+    def attend(l):
+        dsa.sparse_attn(l.q[0][:, None], l.k_cache, l.v_cache, l.block_table, ix[:, 0], page=l.page,
+                        sm_scale=l.sm_scale, out=o, lse=lse, workspace=aws)
+
+    def shared():
+        select(d0)
+        for l in layers:
+            attend(l)
+
+    def per_layer():
+        for l in layers:
+            select(l)
+            attend(l)
+
+    us_shared = _time_graph(shared, reps, inner=4)
+    us_per = _time_graph(per_layer, reps, inner=4)
+    out["cross_layer_indexshare_32k_4layers"] = {
+        "us_per_block_shared": us_shared, "us_per_block_indexer_each_layer": us_per,
+        "speedup": us_per / us_shared}
+    del layers, d0, sc, ix, o, lse, aws
+    # verify-pass DSA at context 32K: 8 chained rows (7 drafts + bonus), row r
+    # sees [0, L + r + 1); indexer at R = 8, per-row top-k, 8-row attention
+    # with per-row index sets
+    L, R = 32768, 8
+    d = DI.draft_inputs(45, [L], H_I=64, D_I=128, H_q=64, H_kv=64, D_qk=128, D_v=128, k=2048, G=R, R=R)
+    rl = torch.arange(L + 1, L + R + 1, dtype=torch.int32, device="cuda:0")[None].contiguous()
+    sc = torch.empty((1, R, L + R), dtype=torch.float32, device="cuda:0")
+    ix = torch.empty((1, R, d.k), dtype=torch.int32, device="cuda:0")
+    qv = d.q[:, 0][None].contiguous()                                   # [1, R, H, D]
+    o = torch.empty((1, R, d.H_q, d.D_v), dtype=torch.float32, device="cuda:0")
+    lse = torch.empty((1, R, d.H_q), dtype=torch.float32, device="cuda:0")
+    aws = torch.zeros(max(1, dsa.sparse_attn_workspace_size(1, R, 64, 64, 128, 128, d.k)), dtype=torch.uint8,
+                      device="cuda:0")
+    tws = torch.empty(max(1, dsa.topk_workspace_size(1, R, L + R, d.k)), dtype=torch.uint8, device="cuda:0")
+
+    def verify_pass():
+        dsa.index_scores(d.q_index, d.w, d.kidx, d.block_table, rl, page=d.page, out=sc)
+        dsa.topk(sc, rl, d.k, out=ix, workspace=tws)
+        dsa.sparse_attn(qv, d.k_cache, d.v_cache, d.block_table, ix, page=d.page, sm_scale=d.sm_scale, out=o,
+                        lse=lse, workspace=aws)
+
+    us = _time_graph(verify_pass, reps)
+    out["verify_pass_dsa_32k_8rows"] = {"us_per_call": us, "rows_per_s": R / (us * 1e-6),
+                                        "context_tokens_per_s": R * L / (us * 1e-6)}
+    del d, rl, sc, ix, qv, o, lse, aws, tws
     L = 1 << 20
     for R in (1, 8):
         d = DI.draft_inputs(3, [L], H_I=64, D_I=128, H_q=64, D_qk=576, D_v=512, k=2048, G=0, R=R,

@@ -43,6 +43,9 @@ __all__ = [
     "sparse_attn",
     "dense_attn",
     "draft_block",
+    "layer_block",
+    "mixed_kv_sets",
+    "mixed_kv_draft_block",
     "softmax",
     "icdf",
     "spec_verify_seq",
@@ -178,6 +181,53 @@ def draft_block(q_index, w, keys, L, k, q_steps, K, V, scale):
         outs.append(o)
         lses.append(lse)
     return idx, np.stack(outs), np.stack(lses)
+
+
+def layer_block(q_index, w, keys, L, k, q_layers, K_layers, V_layers, scale):
+    """Cross-layer IndexShare: one indexer serves a block of backbone layers.
+
+    Section "IndexShare and KVShare" (and the IndexShare glossary entry): one
+    indexer is shared across every four backbone layers; the first computes
+    which past tokens matter and the rest reuse its top-k.  Each layer keeps
+    its own queries and KV cache.  q_layers: [n, H_q, D_qk];
+    K_layers / V_layers: [n, L_total, H_kv, D].  Returns (idx, outs [n, H_q,
+    D_v], lses [n, H_q]).
+    """
+    s = index_scores(np.asarray(q_index)[None], np.asarray(w)[None], keys, [L])[0]
+    idx = topk(s, L, k)
+    outs, lses = [], []
+    for q, K, V in zip(q_layers, K_layers, V_layers):
+        o, lse = sparse_attn(q, K, V, idx, scale)
+        outs.append(o)
+        lses.append(lse)
+    return idx, np.stack(outs), np.stack(lses)
+
+
+def mixed_kv_sets(idx, L, G):
+    """Index sets of the mixed-KV drafting the same section describes for
+    GLM-5.1 (kept here as a negative control): draft step j (0-based) attends
+    to the step-1 selection plus the draft-written slots L .. L+j-1, whose KV
+    came from the MTP layer's own hidden states.  Returns [G, len(idx) + G - 1]
+    index rows padded with -1."""
+    idx = np.asarray(idx, dtype=np.int64)
+    rows = np.full((G, len(idx) + G - 1), -1, dtype=np.int64)
+    for j in range(G):
+        sel = np.concatenate([idx[idx >= 0], np.arange(L, L + j)])
+        rows[j, : len(sel)] = sel
+    return rows
+
+
+def mixed_kv_draft_block(q_index, w, keys, L, k, q_steps, K, V, scale):
+    """The mixed-KV chain: like draft_block, but step j also sees slots
+    L .. L+j-1 (mixed_kv_sets).  Returns (sets, outs [G, H_q, D_v], lses)."""
+    s = index_scores(np.asarray(q_index)[None], np.asarray(w)[None], keys, [L])[0]
+    sets = mixed_kv_sets(topk(s, L, k), L, len(q_steps))
+    outs, lses = [], []
+    for qj, sj in zip(q_steps, sets):
+        o, lse = sparse_attn(qj, K, V, sj, scale)
+        outs.append(o)
+        lses.append(lse)
+    return sets, np.stack(outs), np.stack(lses)
 
 
 # ----------------------------------------------------------------------------

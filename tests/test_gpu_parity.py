@@ -380,6 +380,61 @@ def test_greedy_verify_special_rows():
 
 
 # ----------------------------------------------------------------------------
+# cross-layer IndexShare and the mixed-KV negative control
+# ----------------------------------------------------------------------------
+def test_cross_layer_index_share():
+    """One indexer + top-k for a block of 4 layers; each layer attends with its
+    own queries and paged KV over the shared selection."""
+    lens = [3000, 1777]
+    layers = [I.draft_inputs(60 + l, lens, H_I=64, D_I=128, H_q=16, H_kv=8, D_qk=128, D_v=128, k=512, G=1,
+                             shuffle_pages=True, integer_indexer=True) for l in range(4)]
+    d0 = layers[0]
+    dd0 = DraftDev(d0)
+    scores = dsa.index_scores(dd0.q_index, dd0.w, dd0.kidx, dd0.bt, dd0.row_len, page=d0.page, ld=dd0.ld)
+    idx = dsa.topk(scores, dd0.row_len, d0.k)[:, 0]
+    for b in range(len(lens)):
+        ref_idx, ref_o, ref_lse = O.layer_block(d0.q_index[b, 0], d0.w[b, 0], d0.keys[b], lens[b], d0.k,
+                                                [l.q[0, b] for l in layers], [l.K[b] for l in layers],
+                                                [l.V[b] for l in layers], d0.sm_scale)
+        np.testing.assert_array_equal(idx.cpu().numpy()[b], ref_idx)
+        for li, l in enumerate(layers):
+            dl = DraftDev(l)
+            o, lse = dsa.sparse_attn(dl.q[0][:, None], dl.k, dl.v, dl.bt, idx, page=l.page, sm_scale=l.sm_scale)
+            assert np.abs(o.cpu().numpy()[b, 0] - ref_o[li]).max() <= ATTN_TOL
+            assert np.abs(lse.cpu().numpy()[b, 0] - ref_lse[li]).max() <= ATTN_TOL
+
+
+@pytest.mark.parametrize("poison", [False, True])
+def test_mixed_kv_negative_control(poison):
+    """GLM-5.1 mixed-KV drafting: step j also reads draft-written slots
+    L..L+j-1 (per-row index sets, one call with S_q = G).  Clean inputs match
+    the oracle; with those slots poisoned (NaN) every step after the first
+    turns NaN, while the IndexShare chain over the same cache stays finite."""
+    G = 7
+    d = I.draft_inputs(31, [2500], H_I=64, D_I=128, H_q=16, H_kv=16, D_qk=128, D_v=128, k=256, G=G,
+                       integer_indexer=True, poison=poison)
+    dd = DraftDev(d)
+    L = int(d.lens[0])
+    scores = dsa.index_scores(dd.q_index, dd.w, dd.kidx, dd.bt, dd.row_len, page=d.page, ld=dd.ld)
+    idx = dsa.topk(scores, dd.row_len, d.k)[:, 0]
+    sets = O.mixed_kv_sets(idx.cpu().numpy()[0], L, G)                   # [G, k + G - 1]
+    q = dd.q[:, 0][None].contiguous()                                      # [1, G, H, D]: one row per step
+    o, lse = dsa.sparse_attn(q, dd.k, dd.v, dd.bt, to_dev(sets.astype(np.int32))[None], page=d.page,
+                             sm_scale=d.sm_scale)
+    o = o.cpu().numpy()[0]
+    o_share, _ = dsa.sparse_attn(q, dd.k, dd.v, dd.bt, idx, page=d.page, sm_scale=d.sm_scale)
+    assert np.all(np.isfinite(o_share.cpu().numpy()))
+    if poison:
+        assert np.all(np.isfinite(o[0]))
+        assert np.all(np.isnan(o[1:]))
+    else:
+        _, ref_o, ref_lse = O.mixed_kv_draft_block(d.q_index[0, 0], d.w[0, 0], d.keys[0], L, d.k, d.q[:, 0],
+                                                   d.K[0], d.V[0], d.sm_scale)
+        assert np.abs(o - ref_o).max() <= ATTN_TOL
+        assert np.abs(lse.cpu().numpy()[0] - ref_lse).max() <= ATTN_TOL
+
+
+# ----------------------------------------------------------------------------
 # HIP graph capture of the draft block: every replay matches the eager result
 # ----------------------------------------------------------------------------
 def test_draft_block_graph_replays():

@@ -252,6 +252,72 @@ def test_index_share_steps_see_only_target_written_positions():
     np.testing.assert_array_equal(outs, outs_p)
 
 
+def test_mixed_kv_control_sees_draft_written_slots():
+    """Negative control (GLM-5.1 mixed KV): poisoning the draft-written slots
+    leaves step 0 untouched but reaches every later step, the opposite of the
+    KVShare invariant above."""
+    rng = np.random.default_rng(24)
+    L, G, H, D, I = 30, 7, 2, 8, 2
+    keys = rng.standard_normal((L + G, D))
+    K = rng.standard_normal((L + G, H, D))
+    V = rng.standard_normal((L + G, H, D))
+    q_idx, w = rng.standard_normal((I, D)), rng.random(I)
+    q = rng.standard_normal((G, H, D))
+    sets, outs, _ = O.mixed_kv_draft_block(q_idx, w, keys, L, 12, q, K, V, 0.3)
+    idx, outs_share, _ = O.draft_block(q_idx, w, keys, L, 12, q, K, V, 0.3)
+    for j in range(G):   # the sets: the selection plus exactly the j newest draft slots
+        sel = sets[j][sets[j] >= 0]
+        assert set(sel.tolist()) == set(idx[idx >= 0].tolist()) | set(range(L, L + j))
+    np.testing.assert_array_equal(outs[0], outs_share[0])
+    K_p, V_p = K.copy(), V.copy()
+    K_p[L:] = np.nan
+    V_p[L:] = np.nan
+    _, outs_p, _ = O.mixed_kv_draft_block(q_idx, w, keys, L, 12, q, K_p, V_p, 0.3)
+    np.testing.assert_array_equal(outs_p[0], outs[0])
+    assert np.all(np.isnan(outs_p[1:]))
+
+
+def test_mixed_kv_step_matches_torch_sdpa_over_union():
+    rng = np.random.default_rng(25)
+    L, G, H, D = 40, 5, 3, 16
+    K = rng.standard_normal((L + G, H, D))
+    V = rng.standard_normal((L + G, H, D))
+    q = rng.standard_normal((H, D))
+    idx = np.sort(rng.choice(L, 9, replace=False))
+    sets = O.mixed_kv_sets(np.concatenate([idx, [-1, -1]]), L, G)
+    for j in range(G):
+        o, _ = O.sparse_attn(q, K, V, sets[j], 0.25)
+        pos = np.concatenate([idx, np.arange(L, L + j)])
+        Kt = torch.from_numpy(K[pos]).permute(1, 0, 2)[None]
+        Vt = torch.from_numpy(V[pos]).permute(1, 0, 2)[None]
+        ref = torch.nn.functional.scaled_dot_product_attention(torch.from_numpy(q)[None, :, None], Kt, Vt,
+                                                               scale=0.25)[0, :, 0].numpy()
+        np.testing.assert_allclose(o, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_layer_block_reuses_one_selection():
+    """Cross-layer IndexShare: every layer of the block uses the first
+    layer's selection with its own queries and KV; a layer equals a
+    stand-alone sparse attention over that selection."""
+    rng = np.random.default_rng(26)
+    L, n, H, D, I = 50, 4, 2, 8, 2
+    keys = rng.standard_normal((L, D))
+    Ks = rng.standard_normal((n, L, H, D))
+    Vs = rng.standard_normal((n, L, H, D))
+    qs = rng.standard_normal((n, H, D))
+    q_idx, w = rng.standard_normal((I, D)), rng.random(I)
+    idx, outs, _ = O.layer_block(q_idx, w, keys, L, 10, qs, Ks, Vs, 0.3)
+    ref_idx = O.topk(O.index_scores(q_idx[None], w[None], keys, [L])[0], L, 10)
+    np.testing.assert_array_equal(idx, ref_idx)
+    for l in range(n):
+        sel = idx[idx >= 0]
+        Kt = torch.from_numpy(Ks[l][sel]).permute(1, 0, 2)[None]
+        Vt = torch.from_numpy(Vs[l][sel]).permute(1, 0, 2)[None]
+        ref = torch.nn.functional.scaled_dot_product_attention(torch.from_numpy(qs[l])[None, :, None], Kt, Vt,
+                                                               scale=0.3)[0, :, 0].numpy()
+        np.testing.assert_allclose(outs[l], ref, rtol=1e-12, atol=1e-12)
+
+
 # ----------------------------------------------------------------------------
 # a4 verification
 # ----------------------------------------------------------------------------

@@ -57,6 +57,8 @@ struct AttnArgs {
   float* lse;
   float* part_o;           // [B*S_q*H_q][nsplit][D_v]
   float* part_ml;          // [B*S_q*H_q][nsplit][2]
+  int batch, head_groups;
+  int row_grouped;         // 1: flat grid, the S_q rows of one (b, split, head group) share an XCD
   int nsplit;
   int tok_per_split;
 };
@@ -152,9 +154,29 @@ __global__ __launch_bounds__(kThreads) void mha_attn_kernel(AttnArgs a) {
   __shared__ float s_ml[kWaves][NH][2];
   __shared__ float s_o[kWaves][NH][D];
 
-  const int split = blockIdx.x;
-  const int hg = blockIdx.y;                         // KV head group
-  const int bs = blockIdx.z;                         // b * S_q + s
+  int split, hg, bs;
+  if (a.row_grouped) {
+    // Several query rows (the verify pass): workgroups are dealt to the 8
+    // XCDs round-robin by linear id, so XCD x's k-th workgroup takes row
+    // k % S_q of unit (k / S_q) * 8 + x.  The S_q rows of a unit (same
+    // sequence, split and head group) then run on one XCD at about the same
+    // time, and rows with (nearly) the same index set read the same KV rows
+    // through that XCD's L2.
+    const int id = blockIdx.x;
+    const int slot = id >> 3;
+    const int unit = (slot / a.S_q) * 8 + (id & 7);
+    const int s_row = slot % a.S_q;
+    const int per_seq = a.nsplit * a.head_groups;
+    if (unit >= a.batch * per_seq) return;          // padding of the unit count to a multiple of 8
+    const int bb = unit / per_seq;
+    split = (unit % per_seq) / a.head_groups;
+    hg = unit % a.head_groups;
+    bs = bb * a.S_q + s_row;
+  } else {
+    split = blockIdx.x;
+    hg = blockIdx.y;                                 // KV head group
+    bs = blockIdx.z;                                 // b * S_q + s
+  }
   const int b = bs / a.S_q;
   const int s = bs % a.S_q;
   const int tid = threadIdx.x;
@@ -566,9 +588,21 @@ Plan make_plan(int B, int S_q, int H_q, int H_kv, int D_qk, int D_v, int k) {
 }
 
 template <int D, int GQ>
-void launch_mha(const AttnArgs& a, const Plan& p, int B, hipStream_t s) {
-  dim3 grid(p.nsplit, p.head_groups, B * a.S_q);
-  hipLaunchKernelGGL((mha_attn_kernel<D, GQ, DSA_ATTN_UNROLL>), grid, dim3(kThreads), 0, s, a);
+void launch_mha(AttnArgs a, const Plan& p, int B, hipStream_t s) {
+  a.batch = B;
+  a.head_groups = p.head_groups;
+  if (a.S_q > 1) {
+    // flat grid: units (b, split, head group) padded to a multiple of the 8
+    // XCDs, times S_q rows (see the kernel)
+    const long long units = ((long long)B * p.nsplit * p.head_groups + 7) / 8 * 8;
+    a.row_grouped = 1;
+    hipLaunchKernelGGL((mha_attn_kernel<D, GQ, DSA_ATTN_UNROLL>), dim3((unsigned)(units * a.S_q)), dim3(kThreads), 0,
+                       s, a);
+  } else {
+    a.row_grouped = 0;
+    dim3 grid(p.nsplit, p.head_groups, B * a.S_q);
+    hipLaunchKernelGGL((mha_attn_kernel<D, GQ, DSA_ATTN_UNROLL>), grid, dim3(kThreads), 0, s, a);
+  }
 }
 
 }  // namespace

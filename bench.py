@@ -47,6 +47,8 @@ def parse():
                     help="only the side measurements (for profiling them on their own)")
     ap.add_argument("--extras-reps", type=int, default=20,
                     help="graph replays per side measurement")
+    ap.add_argument("--extras", default=",".join(EXTRA_GROUPS),
+                    help="comma-separated side measurement groups: " + ", ".join(EXTRA_GROUPS))
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device copy (HBM counter calibration)")
     return ap.parse_args()
@@ -106,7 +108,7 @@ def main():
         return
     if args.extras_only:
         import dsa_sparse_attention_lightning_amd as dsa
-        print(json.dumps({"extras": extra_measurements(dsa, args.extras_reps)}), flush=True)
+        print(json.dumps({"extras": extra_measurements(dsa, args.extras_reps, args.extras.split(","))}), flush=True)
         return
     import numpy as np
     import torch
@@ -247,7 +249,7 @@ def main():
         "accepted_len": acc_len.cpu().tolist(),
     }
     if not args.no_extras:
-        result["extras"] = extra_measurements(dsa, args.extras_reps)
+        result["extras"] = extra_measurements(dsa, args.extras_reps, args.extras.split(","))
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(d, v, scores, idx, args.cpu_seconds)
     print(json.dumps(result), flush=True)
@@ -278,12 +280,24 @@ def _time_graph(fn, reps=20, inner=8):
     return 1e3 * a.elapsed_time(b) / (reps * inner)
 
 
-def extra_measurements(dsa, reps=20):
-    """Side measurements on the other workload shapes (not the headline):
-    spec_verify (and greedy verification) on the 256 x 8 x 151,552 verification batch, sparse
-    attention on the 16-sequence batched configuration, and the
-    indexer at 1M context for one row (draft step 1, HBM-bound) and eight
-    rows (verify-pass shape, MFMA-bound)."""
+EXTRA_GROUPS = ("verify", "attn_batched", "cross_layer", "verify_pass", "indexer_1m")
+
+
+def extra_measurements(dsa, reps=20, groups=EXTRA_GROUPS):
+    """Side measurements on the other workload shapes (not the headline), by
+    group: verify = spec_verify and greedy verification on the 256 x 8 x
+    151,552 verification batch; attn_batched = sparse attention on the
+    16-sequence batched configuration; cross_layer = a 4-layer IndexShare
+    block at 32K; verify_pass = the 8-row verify-pass DSA step at 32K;
+    indexer_1m = the indexer at 1M context for one row (draft step 1,
+    HBM-bound) and eight rows (verify-pass shape, MFMA-bound)."""
+    out = {}
+    for g in groups:
+        out.update(_EXTRAS[g](dsa, reps))
+    return out
+
+
+def _extra_verify(dsa, reps):
     import torch
     from dsa_inputs import device as DI
     out = {}
@@ -311,6 +325,13 @@ def extra_measurements(dsa, reps=20):
         "GBps": gbytes / us / 1e3, "frac_hbm": gbytes / us / 1e3 / HBM_PEAK_GBS,
         "mean_accepted": float(n.float().mean())}
     del v, ws, gws, gdr
+    return out
+
+
+def _extra_attn_batched(dsa, reps):
+    import torch
+    from dsa_inputs import device as DI
+    out = {}
     # sparse attention on the batched configuration: 16 sequences with context
     # uniform in [16K, 64K], paged KV from one shuffled pool (about 1 GiB of
     # gathered K/V per call, more than the last-level cache holds)
@@ -334,6 +355,13 @@ def extra_measurements(dsa, reps=20):
         "us_per_call": us, "algorithmic_bytes": abytes, "GBps": abytes / us / 1e3,
         "frac_hbm": abytes / us / 1e3 / HBM_PEAK_GBS, "context_tokens_per_s": sum(d.lens) / (us * 1e-6)}
     del d, idx, o, lse, aws
+    return out
+
+
+def _extra_cross_layer(dsa, reps):
+    import torch
+    from dsa_inputs import device as DI
+    out = {}
     # cross-layer IndexShare at context 32K: one indexer + top-k serves a block
     # of 4 layers (each with its own queries and KV), against an indexer per layer
     layers = [DI.draft_inputs(40 + l, [32768], H_I=64, D_I=128, H_q=64, H_kv=64, D_qk=128, D_v=128, k=2048, G=1)
@@ -370,6 +398,13 @@ def extra_measurements(dsa, reps=20):
         "us_per_block_shared": us_shared, "us_per_block_indexer_each_layer": us_per,
         "speedup": us_per / us_shared}
     del layers, d0, sc, ix, o, lse, aws
+    return out
+
+
+def _extra_verify_pass(dsa, reps):
+    import torch
+    from dsa_inputs import device as DI
+    out = {}
     # verify-pass DSA at context 32K: 8 chained rows (7 drafts + bonus), row r
     # sees [0, L + r + 1); indexer at R = 8, per-row top-k, 8-row attention
     # with per-row index sets
@@ -395,6 +430,13 @@ def extra_measurements(dsa, reps=20):
     out["verify_pass_dsa_32k_8rows"] = {"us_per_call": us, "rows_per_s": R / (us * 1e-6),
                                         "context_tokens_per_s": R * L / (us * 1e-6)}
     del d, rl, sc, ix, qv, o, lse, aws, tws
+    return out
+
+
+def _extra_indexer_1m(dsa, reps):
+    import torch
+    from dsa_inputs import device as DI
+    out = {}
     L = 1 << 20
     for R in (1, 8):
         d = DI.draft_inputs(3, [L], H_I=64, D_I=128, H_q=64, D_qk=576, D_v=512, k=2048, G=0, R=R,
@@ -409,6 +451,10 @@ def extra_measurements(dsa, reps=20):
             "GBps": kbytes / us / 1e3, "frac_hbm": kbytes / us / 1e3 / HBM_PEAK_GBS}
         del d, sc
     return out
+
+
+_EXTRAS = {"verify": _extra_verify, "attn_batched": _extra_attn_batched, "cross_layer": _extra_cross_layer,
+           "verify_pass": _extra_verify_pass, "indexer_1m": _extra_indexer_1m}
 
 
 def cpu_baseline(d, v, scores, idx, budget_s):

@@ -253,8 +253,6 @@ __device__ void decide(const VerifyArgs& a, const VerifyWs& ws, int b, float* s_
   const int nrows = 2 * G + 1;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int nw = blockDim.x >> 6;
   // the draft tokens' logits are fetched first so that their latency overlaps the fold
   float tv = 0.f, dv = 0.f;
   if (tid < G) {
@@ -262,27 +260,34 @@ __device__ void decide(const VerifyArgs& a, const VerifyWs& ws, int b, float* s_
     tv = a.tl[((size_t)b * (G + 1) + lane) * V + d];
     dv = a.dl[((size_t)b * G + lane) * V + d];
   }
-  // row r folded by wave r % nw: lane l merges chunks l, l + 64, ... in that
-  // order, then a butterfly (merging is symmetric, so every lane, and every
-  // workgroup of the sequence, ends with the same bits)
-  for (int r = wave; r < nrows; r += nw) {
-    const float2* p = ws.part + ((size_t)b * nrows + r) * a.nchunks;
+  // 16 lanes per row, all rows at once (one round of loads): lane j of row
+  // r's group merges chunks j, j + 16, ... in that order, then a 16-lane
+  // butterfly (merging is symmetric, so every lane, and every workgroup of
+  // the sequence, ends with the same bits)
+  const int groups = blockDim.x / 16;
+  const int g16 = tid >> 4, j16 = tid & 15;
+  for (int r0 = 0; r0 < nrows; r0 += groups) {
+    const int r = r0 + g16;
     float M = -INFINITY, S = 0.f;
-    for (int c = lane; c < a.nchunks; c += 64) {
-      const float2 v = p[c];
-      ms_merge(M, S, v.x, v.y);
+    if (r < nrows) {
+      const float2* p = ws.part + ((size_t)b * nrows + r) * a.nchunks;
+      for (int c = j16; c < a.nchunks; c += 16) {
+        const float2 v = p[c];
+        ms_merge(M, S, v.x, v.y);
+      }
     }
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
+    for (int o = 8; o >= 1; o >>= 1) {
       const float m2 = __shfl_xor(M, o, 64);
       const float s2 = __shfl_xor(S, o, 64);
       ms_merge(M, S, m2, s2);
     }
-    if (lane == 0) {
+    if (r < nrows && j16 == 0) {
       s_m[r] = M;
       s_z[r] = S;
     }
   }
+
   __syncthreads();
   if (tid < 64) {
     bool reject = false;

@@ -365,7 +365,7 @@ dsa_status launch_rows(const void* q, const float* w, const void* kidx, const in
   const uint16_t* qq = static_cast<const uint16_t*>(q);
   const uint16_t* kk = static_cast<const uint16_t*>(kidx);
   // up to 4 rows: one row per wave (Q fragments 64 VGPRs); 5..8 rows: two
-  // rows per wave in 4 waves (128 VGPRs of Q; rows past R hold zero Q)
+  // rows per wave in four waves (128 VGPRs of Q; rows past R hold zero Q)
 #define DSA_ROWS_LAUNCH(RPW, NW) \
   hipLaunchKernelGGL((index_scores_rows_kernel<KS16, RPW, NW>), grid, dim3(NW * 64), 0, s, qq, w, kk, bt, row_len, \
                      scores, R, H, page, max_pages, ld, chunk)
@@ -373,12 +373,7 @@ dsa_status launch_rows(const void* q, const float* w, const void* kidx, const in
     case 2: DSA_ROWS_LAUNCH(1, 2); break;
     case 3: DSA_ROWS_LAUNCH(1, 3); break;
     case 4: DSA_ROWS_LAUNCH(1, 4); break;
-#ifdef DSA_INDEX_R8_RPW1
-    case 5: case 6: DSA_ROWS_LAUNCH(2, 4); break;
-    default: DSA_ROWS_LAUNCH(1, 8); break;
-#else
     default: DSA_ROWS_LAUNCH(2, 4); break;
-#endif
   }
 #undef DSA_ROWS_LAUNCH
   return launch_status("dsa_index_scores");

@@ -593,8 +593,8 @@ int chunk_for_rows(int64_t rows, int V) {
 
 int stats_chunk(int B, int G, int V) { return chunk_for_rows((int64_t)B * (2 * G + 1), V); }
 
-// Tiles per residual-mass chunk: 16K-logit chunks when there are enough
-// sequences to fill the GPU with them, else 4K.
+// Tiles per residual-mass chunk: 8K-logit chunks (kBigChunkTiles tiles)
+// when there are enough sequences to fill the GPU with them, else 4K.
 int mass_chunk_tiles(int B, int V) {
   const int64_t big = (V + kBigChunkTiles * kTile - 1) / (kBigChunkTiles * kTile);
   return (int64_t)B * big >= 1024 ? kBigChunkTiles : kSmallChunkTiles;

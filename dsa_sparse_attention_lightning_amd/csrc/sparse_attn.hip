@@ -283,7 +283,13 @@ __global__ __launch_bounds__(kThreads) void mha_attn_kernel(AttnArgs a) {
 // loads of all its split partials at once, so the fold is one memory round
 // trip with no barrier.
 constexpr int kCombineMaxSplits = 128;
-constexpr int kLatentMaxSplits = 32;
+#ifndef DSA_LAT_MAX_SPLITS
+#define DSA_LAT_MAX_SPLITS 32
+#endif
+#ifndef DSA_LAT_MIN_TILES
+#define DSA_LAT_MIN_TILES 2
+#endif
+constexpr int kLatentMaxSplits = DSA_LAT_MAX_SPLITS;
 
 template <int D, int MAXSPLIT>
 __global__ __launch_bounds__(D) void combine_kernel(const float* __restrict__ part_o,
@@ -430,9 +436,9 @@ __global__ __launch_bounds__(NW * 64) void latent_attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int j = 0; j < PER_T; ++j) {
       const int c = tid + j * NT;
-      const int tt = min(tile * kLatTile + c / kLatChunks, ntok - 1);
+      const int tt = min(tile * kLatTile + c % kLatTile, ntok - 1);
       const int64_t off = max(s_off[tt], (int64_t)0);
-      pre[j] = *reinterpret_cast<const uint4*>(a.kc + off + (c % kLatChunks) * 8);
+      pre[j] = *reinterpret_cast<const uint4*>(a.kc + off + (c / kLatTile) * 8);
     }
   };
   fetch(0);
@@ -441,8 +447,12 @@ __global__ __launch_bounds__(NW * 64) void latent_attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int j = 0; j < PER_T; ++j) {
       const int c = tid + j * NT;
-      const int tt = c / kLatChunks;
-      const int ch = c % kLatChunks;
+      // piece c = token c % 32, chunk c / 32: the lanes of a wave hold 32
+      // consecutive tokens of two chunks, so the transposed 2-byte V stores
+      // of one instruction go to two rows, 32 consecutive columns each
+      // (conflict-free), and the 16-byte K stores to 32 rows 1168 bytes apart
+      const int tt = c % kLatTile;
+      const int ch = c / kLatTile;
       *reinterpret_cast<uint4*>(s_k + tt * kLatKRow + ch * 16) = pre[j];
       if (ch < kLatDv / 8) {
         const uint32_t w4[4] = {pre[j].x, pre[j].y, pre[j].z, pre[j].w};
@@ -567,7 +577,7 @@ Plan make_plan(int B, int S_q, int H_q, int H_kv, int D_qk, int D_v, int k) {
   const int nslot = latent ? 1 : 64 / (D_qk / 8);
   p.head_groups = latent ? 1 : (H_kv + nslot - 1) / nslot;
   const long long base = (long long)B * S_q * p.head_groups;
-  const int min_tok = latent ? 4 * kLatTile : DSA_ATTN_MIN_TOKENS;
+  const int min_tok = latent ? DSA_LAT_MIN_TILES * kLatTile : DSA_ATTN_MIN_TOKENS;
   const int max_split = latent ? kLatentMaxSplits : kCombineMaxSplits;
   int ns = (int)((DSA_ATTN_TARGET_WGS + base - 1) / base);
   const int max_ns = (k + min_tok - 1) / min_tok;

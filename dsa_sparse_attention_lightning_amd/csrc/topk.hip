@@ -30,6 +30,7 @@ namespace {
 constexpr int kBins = 4096;
 constexpr int kHistThreads = 256;
 constexpr int kChunk = 4096;          // positions per workgroup in passes 2-4
+constexpr int kPerThread = kChunk / kHistThreads;   // 16 loads in flight per thread
 constexpr int kFinThreads = 1024;
 constexpr int kMaxK = 8192;
 constexpr int kCandCap = 8192;        // candidates held in LDS by pass 5
@@ -149,7 +150,12 @@ __global__ __launch_bounds__(kHistThreads) void topk_hist1_kernel(const float* _
   __syncthreads();
   const float* s = scores + (size_t)row * ld;
   const int t1 = min(t0 + kChunk, L);
-  for (int t = t0 + threadIdx.x; t < t1; t += kHistThreads) atomicAdd(&h[order_key(s[t]) >> 20], 1u);
+  float v[kPerThread];   // all of the chunk's loads in flight at once
+#pragma unroll
+  for (int u = 0; u < kPerThread; ++u) v[u] = s[min(t0 + (int)threadIdx.x + u * kHistThreads, t1 - 1)];
+#pragma unroll
+  for (int u = 0; u < kPerThread; ++u)
+    if (t0 + (int)threadIdx.x + u * kHistThreads < t1) atomicAdd(&h[order_key(v[u]) >> 20], 1u);
   __syncthreads();
   uint32_t* g = ws.hist1 + (size_t)row * kBins;
   for (int i = threadIdx.x; i < kBins; i += kHistThreads)
@@ -172,9 +178,13 @@ __global__ __launch_bounds__(kHistThreads) void topk_hist2_kernel(const float* _
   const uint32_t T1 = (uint32_t)s_t1;
   const float* s = scores + (size_t)row * ld;
   const int t1 = min(t0 + kChunk, L);
-  for (int t = t0 + threadIdx.x; t < t1; t += kHistThreads) {
-    const uint32_t key = order_key(s[t]);
-    if ((key >> 20) == T1) atomicAdd(&h[(key >> 8) & 0xfffu], 1u);
+  float v[kPerThread];
+#pragma unroll
+  for (int u = 0; u < kPerThread; ++u) v[u] = s[min(t0 + (int)threadIdx.x + u * kHistThreads, t1 - 1)];
+#pragma unroll
+  for (int u = 0; u < kPerThread; ++u) {
+    const uint32_t key = order_key(v[u]);
+    if (t0 + (int)threadIdx.x + u * kHistThreads < t1 && (key >> 20) == T1) atomicAdd(&h[(key >> 8) & 0xfffu], 1u);
   }
   __syncthreads();
   uint32_t* g = ws.hist2 + (size_t)row * kBins;
@@ -188,6 +198,9 @@ __global__ __launch_bounds__(kHistThreads) void topk_collect_kernel(const float*
   __shared__ uint32_t s_wave[kHistThreads / 64];
   __shared__ int s_t1, s_t2;
   __shared__ uint32_t s_a1, s_a2;
+  __shared__ int32_t l_sel[kChunk];
+  __shared__ uint2 l_cand[kChunk];
+  __shared__ uint32_t s_n[2], s_base[2];
   const int row = blockIdx.y;
   const int L = row_len[row];
   const int t0 = blockIdx.x * kChunk;
@@ -200,20 +213,34 @@ __global__ __launch_bounds__(kHistThreads) void topk_collect_kernel(const float*
   uint2* cand = ws.cand + (size_t)row * ld;
   uint32_t* cnt = ws.cnt + row * 4;
   const int t1 = min(t0 + kChunk, L);
+  // the chunk's selections and candidates are gathered in LDS first; one
+  // global atomic per list and workgroup then reserves their place
+  if (threadIdx.x < 2) s_n[threadIdx.x] = 0;
+  float v[kPerThread];
+#pragma unroll
+  for (int u = 0; u < kPerThread; ++u) v[u] = s[min(t0 + (int)threadIdx.x + u * kHistThreads, t1 - 1)];
+  __syncthreads();
   // whole waves iterate together so the ballots see every lane
-  for (int tb = t0; tb < t1; tb += kHistThreads) {
-    const int t = tb + threadIdx.x;
-    uint32_t key = 0;
-    bool valid = t < t1;
-    if (valid) key = order_key(s[t]);
+#pragma unroll
+  for (int u = 0; u < kPerThread; ++u) {
+    const int t = t0 + (int)threadIdx.x + u * kHistThreads;
+    const bool valid = t < t1;
+    const uint32_t key = order_key(v[u]);
     const uint32_t top = key >> 8;
     const bool is_sel = valid && top > prefix;
     const bool is_cand = valid && top == prefix;
-    const uint32_t ps = wave_append(is_sel, &cnt[0]);
-    if (is_sel && ps < (uint32_t)k) sel[ps] = t;
-    const uint32_t pc = wave_append(is_cand, &cnt[1]);
-    if (is_cand && pc < (uint32_t)ld) cand[pc] = make_uint2(key, (uint32_t)t);
+    const uint32_t ps = wave_append(is_sel, &s_n[0]);
+    if (is_sel) l_sel[ps] = t;
+    const uint32_t pc = wave_append(is_cand, &s_n[1]);
+    if (is_cand) l_cand[pc] = make_uint2(key, (uint32_t)t);
   }
+  __syncthreads();
+  if (threadIdx.x < 2) s_base[threadIdx.x] = s_n[threadIdx.x] ? atomicAdd(&cnt[threadIdx.x], s_n[threadIdx.x]) : 0u;
+  __syncthreads();
+  for (uint32_t i = threadIdx.x; i < s_n[0]; i += kHistThreads)
+    if (s_base[0] + i < (uint32_t)k) sel[s_base[0] + i] = l_sel[i];
+  for (uint32_t i = threadIdx.x; i < s_n[1]; i += kHistThreads)
+    if (s_base[1] + i < (uint32_t)ld) cand[s_base[1] + i] = l_cand[i];
 }
 
 // Composite rank of a candidate: key bits 7..0, then ~position (lower

@@ -280,7 +280,7 @@ def _time_graph(fn, reps=20, inner=8):
     return 1e3 * a.elapsed_time(b) / (reps * inner)
 
 
-EXTRA_GROUPS = ("verify", "attn_batched", "cross_layer", "verify_pass", "indexer_1m")
+EXTRA_GROUPS = ("verify", "attn_batched", "cross_layer", "verify_pass", "indexer_1m", "long_1m")
 
 
 def extra_measurements(dsa, reps=20, groups=EXTRA_GROUPS):
@@ -290,7 +290,8 @@ def extra_measurements(dsa, reps=20, groups=EXTRA_GROUPS):
     16-sequence batched configuration; cross_layer = a 4-layer IndexShare
     block at 32K; verify_pass = the 8-row verify-pass DSA step at 32K;
     indexer_1m = the indexer at 1M context for one row (draft step 1,
-    HBM-bound) and eight rows (verify-pass shape, MFMA-bound)."""
+    HBM-bound) and eight rows (verify-pass shape, MFMA-bound); long_1m = the
+    whole 1M-context latent-MQA draft block."""
     out = {}
     for g in groups:
         out.update(_EXTRAS[g](dsa, reps))
@@ -453,8 +454,48 @@ def _extra_indexer_1m(dsa, reps):
     return out
 
 
+def _extra_long_1m(dsa, reps):
+    """The 1M-context draft block (latent MQA): indexer (R = 1) and top-k over
+    2^20 positions once, then 7 latent sparse-attention steps reusing the
+    indices; phases timed separately and as one graph."""
+    import torch
+    from dsa_inputs import device as DI
+    out = {}
+    d = DI.draft_inputs(3, [1 << 20], H_I=64, D_I=128, H_q=64, D_qk=576, D_v=512, k=2048, G=7, latent=True)
+    sc = torch.empty((1, 1, d.ld), dtype=torch.float32, device="cuda:0")
+    ix = torch.empty((1, 1, d.k), dtype=torch.int32, device="cuda:0")
+    tws = torch.empty(max(1, dsa.topk_workspace_size(1, 1, d.ld, d.k)), dtype=torch.uint8, device="cuda:0")
+    o = torch.empty((d.G, 1, 1, d.H_q, d.D_v), dtype=torch.float32, device="cuda:0")
+    lse = torch.empty((d.G, 1, 1, d.H_q), dtype=torch.float32, device="cuda:0")
+    aws = torch.zeros(max(1, dsa.sparse_attn_workspace_size(1, 1, d.H_q, 1, d.D_qk, d.D_v, d.k)), dtype=torch.uint8,
+                      device="cuda:0")
+
+    def indexer():
+        dsa.index_scores(d.q_index, d.w, d.kidx, d.block_table, d.row_len, page=d.page, out=sc)
+
+    def select():
+        dsa.topk(sc, d.row_len, d.k, out=ix, workspace=tws)
+
+    def attend():
+        for j in range(d.G):
+            dsa.sparse_attn(d.q[j][:, None], d.k_cache, d.v_cache, d.block_table, ix[:, 0], page=d.page,
+                            D_v=d.D_v, sm_scale=d.sm_scale, out=o[j], lse=lse[j], workspace=aws)
+
+    def block():
+        indexer()
+        select()
+        attend()
+
+    us_block = _time_graph(block, reps, inner=2)
+    out["long_1m_latent_draft_block"] = {
+        "us_per_block": us_block, "context_tokens_per_s": d.G * (1 << 20) / (us_block * 1e-6),
+        "us_indexer": _time_graph(indexer, reps), "us_topk": _time_graph(select, reps),
+        "us_attention_per_step": _time_graph(attend, reps, inner=2) / d.G}
+    return out
+
+
 _EXTRAS = {"verify": _extra_verify, "attn_batched": _extra_attn_batched, "cross_layer": _extra_cross_layer,
-           "verify_pass": _extra_verify_pass, "indexer_1m": _extra_indexer_1m}
+           "verify_pass": _extra_verify_pass, "indexer_1m": _extra_indexer_1m, "long_1m": _extra_long_1m}
 
 
 def cpu_baseline(d, v, scores, idx, budget_s):

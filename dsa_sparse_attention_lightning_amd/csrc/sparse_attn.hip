@@ -86,9 +86,21 @@ __device__ __forceinline__ void issue_loads(const AttnArgs& a, const int64_t* s_
 // Online-softmax update with one stage of U tokens: the U dot products and
 // their DPP reductions are independent (they overlap), then the running max,
 // sum and accumulator are rescaled once for the whole stage.
+// q . k over a lane's 8 dims straight from the packed bf16 pairs
+// (v_dot2_f32_bf16: both products exact in fp32), two chains for ILP
+__device__ __forceinline__ float dot8_bf16(const uint4& q, const uint4& k) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  auto p = [](uint32_t x) { return __builtin_bit_cast(bf16x2_t, x); };
+  float d0 = __builtin_amdgcn_fdot2_f32_bf16(p(q.x), p(k.x), 0.f, false);
+  float d1 = __builtin_amdgcn_fdot2_f32_bf16(p(q.y), p(k.y), 0.f, false);
+  d0 = __builtin_amdgcn_fdot2_f32_bf16(p(q.z), p(k.z), d0, false);
+  d1 = __builtin_amdgcn_fdot2_f32_bf16(p(q.w), p(k.w), d1, false);
+  return d0 + d1;
+}
+
 template <int D, int GQ, int U>
 __device__ __forceinline__ void consume(const int64_t* s_off, int i, int ntok, float scale_log2,
-                                        const float (&qv)[GQ][8], float (&m)[GQ], float (&l)[GQ],
+                                        const uint4 (&qv)[GQ], float (&m)[GQ], float (&l)[GQ],
                                         float (&acc)[GQ][8], const uint4 (&kr)[U], const uint4 (&vr)[U]) {
   constexpr int SLOT = D / 8;
   bool ok[U];
@@ -102,17 +114,7 @@ __device__ __forceinline__ void consume(const int64_t* s_off, int i, int ntok, f
     float sc[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const float k0 = bf16_lo(kr[u].x), k1 = bf16_hi(kr[u].x), k2 = bf16_lo(kr[u].y), k3 = bf16_hi(kr[u].y);
-      const float k4 = bf16_lo(kr[u].z), k5 = bf16_hi(kr[u].z), k6 = bf16_lo(kr[u].w), k7 = bf16_hi(kr[u].w);
-      float d0 = qv[j][0] * k0;
-      float d1 = qv[j][1] * k1;
-      d0 = fmaf(qv[j][2], k2, d0);
-      d1 = fmaf(qv[j][3], k3, d1);
-      d0 = fmaf(qv[j][4], k4, d0);
-      d1 = fmaf(qv[j][5], k5, d1);
-      d0 = fmaf(qv[j][6], k6, d0);
-      d1 = fmaf(qv[j][7], k7, d1);
-      sc[u] = group_sum_dpp<SLOT>(d0 + d1) * scale_log2;
+      sc[u] = group_sum_dpp<SLOT>(dot8_bf16(qv[j], kr[u])) * scale_log2;
     }
     float smax = m[j];
 #pragma unroll
@@ -197,15 +199,11 @@ __global__ __launch_bounds__(kThreads) void mha_attn_kernel(AttnArgs a) {
     s_off[i] = t >= 0 ? (int64_t)bt[t / a.page] * a.page_stride + (int64_t)(t % a.page) * a.row_stride : -1;
   }
 
-  float qv[GQ][8];
+  uint4 qv[GQ];   // this lane's 8 query dims per head, packed bf16 pairs
 #pragma unroll
   for (int j = 0; j < GQ; ++j) {
-    uint4 raw = make_uint4(0, 0, 0, 0);
-    if (head_ok) raw = *reinterpret_cast<const uint4*>(a.q + ((size_t)bs * a.H_q + g * GQ + j) * D + sub * 8);
-    qv[j][0] = bf16_lo(raw.x); qv[j][1] = bf16_hi(raw.x);
-    qv[j][2] = bf16_lo(raw.y); qv[j][3] = bf16_hi(raw.y);
-    qv[j][4] = bf16_lo(raw.z); qv[j][5] = bf16_hi(raw.z);
-    qv[j][6] = bf16_lo(raw.w); qv[j][7] = bf16_hi(raw.w);
+    qv[j] = make_uint4(0, 0, 0, 0);
+    if (head_ok) qv[j] = *reinterpret_cast<const uint4*>(a.q + ((size_t)bs * a.H_q + g * GQ + j) * D + sub * 8);
   }
   float m[GQ], l[GQ], acc[GQ][8];
 #pragma unroll

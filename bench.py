@@ -341,7 +341,17 @@ def _extra_attn_batched(dsa, reps):
                         G=1, shuffle_pages=True)
     sc = dsa.index_scores(d.q_index, d.w, d.kidx, d.block_table, d.row_len, page=d.page, ld=d.ld)
     idx = dsa.topk(sc, d.row_len, d.k)
-    del sc
+    # the indexer (one row per sequence, draft step 1) and the top-k on the same batch
+    us_ix = _time_graph(lambda: dsa.index_scores(d.q_index, d.w, d.kidx, d.block_table, d.row_len, page=d.page,
+                                                 out=sc), reps)
+    tws = torch.empty(max(1, dsa.topk_workspace_size(d.B, 1, d.ld, d.k)), dtype=torch.uint8, device="cuda:0")
+    us_tk = _time_graph(lambda: dsa.topk(sc, d.row_len, d.k, out=idx, workspace=tws), reps)
+    L_total = sum(d.lens)
+    ibytes = L_total * d.D_I * 2 + L_total * 4
+    out["indexer_batched_16x16k_64k"] = {"us_per_call": us_ix, "algorithmic_bytes": ibytes,
+                                         "GBps": ibytes / us_ix / 1e3, "frac_hbm": ibytes / us_ix / 1e3 / HBM_PEAK_GBS}
+    out["topk_batched_16x16k_64k"] = {"us_per_call": us_tk, "rows": d.B}
+    del sc, tws
     o = torch.empty((d.B, 1, d.H_q, d.D_v), dtype=torch.float32, device="cuda:0")
     lse = torch.empty((d.B, 1, d.H_q), dtype=torch.float32, device="cuda:0")
     aws = torch.zeros(max(1, dsa.sparse_attn_workspace_size(d.B, 1, d.H_q, d.H_kv, d.D_qk, d.D_v, d.k)),
@@ -530,17 +540,28 @@ def cpu_baseline(d, v, scores, idx, budget_s):
 
     threads = sum(p.get("num_threads", 0) for p in threadpool_info() if p.get("user_api") == "blas") or 1
     reps, spent = 0, 0.0
+    per_op = {"index_scores": 0.0, "topk": 0.0, "sparse_attn_x7": 0.0, "spec_verify": 0.0}
     while spent < budget_s and reps < 200:
         t0 = time.perf_counter()
-        O.draft_block(q_idx, w, keys, L, d.k, q, K, V, d.sm_scale)
+        s_row = O.index_scores(q_idx[None], w[None], keys, [L])[0]
+        t1 = time.perf_counter()
+        sel = O.topk(s_row, L, d.k)
+        t2 = time.perf_counter()
+        for j in range(d.G):
+            O.sparse_attn(q[j], K, V, sel, d.sm_scale)
+        t3 = time.perf_counter()
         O.spec_verify_seq(tl, dl, dr, ua[0], us[0])
-        spent += time.perf_counter() - t0
+        t4 = time.perf_counter()
+        for key, dt in zip(per_op, (t1 - t0, t2 - t1, t3 - t2, t4 - t3)):
+            per_op[key] += dt
+        spent += t4 - t0
         reps += 1
     per_step = spent / reps
     return {"value": d.G * L / per_step, "unit": "context tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{reps} full steps of the same workload (1 sequence, context {L}: indexer, top-k, "
                       f"{d.G} attention steps, verify over vocab {v.draft_logits.shape[-1]}); "
                       f"float64 NumPy, {per_step:.3f} s/step, input conversion {prep:.1f} s not timed",
+            "seconds_per_op": {key: v / reps for key, v in per_op.items()},
             "cpu_model": _cpu_model()}
 
 

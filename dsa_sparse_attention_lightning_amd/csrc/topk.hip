@@ -361,17 +361,17 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const int32_t*
 }
 
 // ---------------------------------------------------------------------------
-// One-workgroup path for rows up to kOneMaxLd positions: a single launch.
-// The row's keys stay in LDS when they fit (else each pass re-reads the
-// scores).  Radix select on 12/12/8-bit digits finds the k-th largest key
+// One-workgroup path for rows whose keys fit in LDS (up to kOneMaxLd
+// positions): a single launch.  Longer rows go to the multi-workgroup
+// pipeline above, which is faster once the keys no longer fit.  Radix select on 12/12/8-bit digits finds the k-th largest key
 // prefix; the output is an ordered compaction over positions (each wave owns
 // a contiguous position range, ballots give in-order ranks), so equal keys
 // are taken lowest position first and no sort is needed.
 // ---------------------------------------------------------------------------
 constexpr int kOneThreads = 1024;
 constexpr int kOneWaves = kOneThreads / 64;
-constexpr int kOneMaxLd = 131072;
 constexpr int kOneLdsKeys = 35840;       // 140 KiB of keys
+constexpr int kOneMaxLd = kOneLdsKeys;
 
 constexpr int kOneCand = kBins / 2;    // threshold-bin candidates resolved in LDS (reuses hist)
 
@@ -400,7 +400,8 @@ __device__ void one_find_bin(OneShared& sh, int nbins, uint32_t need) {
   if (lane_id() == 63) sh.wave_tot[wave] = inc;
   __syncthreads();
   uint32_t run = inc - tot;
-  for (int w = 0; w < wave; ++w) run += sh.wave_tot[w];
+#pragma unroll
+  for (int w = 0; w < kOneWaves; ++w) run += w < wave ? sh.wave_tot[w] : 0u;   // all reads issued together
   if (owns)
     for (int j = 0; j < per; ++j) {
       const uint32_t c = sh.hist[hi - j];
@@ -414,7 +415,6 @@ __device__ void one_find_bin(OneShared& sh, int nbins, uint32_t need) {
   __syncthreads();
 }
 
-template <bool kLds>
 __global__ __launch_bounds__(kOneThreads) void topk_one_kernel(const float* __restrict__ scores,
                                                                const int32_t* __restrict__ row_len, int64_t ld,
                                                                int k, int32_t* __restrict__ idx) {
@@ -433,7 +433,7 @@ __global__ __launch_bounds__(kOneThreads) void topk_one_kernel(const float* __re
   }
   const float* s = scores + (size_t)row * ld;
   constexpr int kU = 8;   // loads in flight per thread
-  auto key_at = [&](int t) -> uint32_t { return kLds ? keys[t] : order_key(s[t]); };
+  auto key_at = [&](int t) -> uint32_t { return keys[t]; };
   // Stage the keys (when they fit) and find the key range in the same pass:
   // the bits every key shares are resolved for free, so the first digit
   // spreads over the range the scores actually occupy (indexer scores sit in
@@ -449,7 +449,7 @@ __global__ __launch_bounds__(kOneThreads) void topk_one_kernel(const float* __re
       const uint32_t key = order_key(v[u]);   // clamped duplicates do not change min/max
       kmin = min(kmin, key);
       kmax = max(kmax, key);
-      if (kLds && t0 + u * kOneThreads < L) keys[t0 + u * kOneThreads] = key;
+      if (t0 + u * kOneThreads < L) keys[t0 + u * kOneThreads] = key;
     }
   }
 #pragma unroll
@@ -520,14 +520,9 @@ __global__ __launch_bounds__(kOneThreads) void topk_one_kernel(const float* __re
     if (tid == 0) sh.ncand = 0;
     __syncthreads();
     auto keys4 = [&](int t, uint32_t (&kk)[4]) {
-      if (kLds) {
-        // t % 4 == 0; lanes past the range read the array's last quad (masked by the caller)
-        const uint4 v = *reinterpret_cast<const uint4*>(keys + min(t, kOneLdsKeys - 4));
-        kk[0] = v.x; kk[1] = v.y; kk[2] = v.z; kk[3] = v.w;
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) kk[i] = order_key(s[min(t + i, L - 1)]);
-      }
+      // t % 4 == 0; lanes past the range read the array's last quad (masked by the caller)
+      const uint4 v = *reinterpret_cast<const uint4*>(keys + min(t, kOneLdsKeys - 4));
+      kk[0] = v.x; kk[1] = v.y; kk[2] = v.z; kk[3] = v.w;
     };
     uint32_t gt_lane = 0;
     for (int tb = p0; tb < p1; tb += 256) {
@@ -555,7 +550,15 @@ __global__ __launch_bounds__(kOneThreads) void topk_one_kernel(const float* __re
     for (int i = tid; i < n; i += kOneThreads) {
       const uint2 c = cand[i];
       uint32_t rank = 0;
-      for (int j = 0; j < n; ++j) {
+      int j = 0;
+      for (; j + 8 <= n; j += 8) {   // eight independent reads per step
+        uint2 e[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) e[u] = cand[j + u];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) rank += (e[u].x > c.x || (e[u].x == c.x && e[u].y < c.y)) ? 1u : 0u;
+      }
+      for (; j < n; ++j) {
         const uint2 e = cand[j];
         rank += (e.x > c.x || (e.x == c.x && e.y < c.y)) ? 1u : 0u;
       }
@@ -569,7 +572,8 @@ __global__ __launch_bounds__(kOneThreads) void topk_one_kernel(const float* __re
     const uint32_t kthr = sh.kthr;
     const int pthr = sh.pthr;
     uint32_t out_pos = 0;
-    for (int w = 0; w < wave; ++w) out_pos += sh.wave_gt[w] + sh.wave_eq[w];
+#pragma unroll
+    for (int w = 0; w < kOneWaves; ++w) out_pos += w < wave ? sh.wave_gt[w] + sh.wave_eq[w] : 0u;
     for (int tb = p0; tb < p1; tb += 256) {
       const int t = tb + lane * 4;
       uint32_t kk[4];
@@ -614,9 +618,10 @@ __global__ __launch_bounds__(kOneThreads) void topk_one_kernel(const float* __re
   }
   __syncthreads();
   uint32_t base_gt = 0, base_eq = 0;
-  for (int w = 0; w < wave; ++w) {
-    base_gt += sh.wave_gt[w];
-    base_eq += sh.wave_eq[w];
+#pragma unroll
+  for (int w = 0; w < kOneWaves; ++w) {
+    base_gt += w < wave ? sh.wave_gt[w] : 0u;
+    base_eq += w < wave ? sh.wave_eq[w] : 0u;
   }
   uint32_t eq_seen = base_eq;
   uint32_t out_pos = base_gt + min(base_eq, need);
@@ -641,9 +646,7 @@ __global__ __launch_bounds__(kOneThreads) void topk_one_kernel(const float* __re
   // no padding needed: L > k means exactly k positions were written
 }
 
-size_t one_lds_bytes(bool in_lds) {
-  return align_up(sizeof(OneShared), 16) + (in_lds ? (size_t)kOneLdsKeys * 4 : 0);
-}
+size_t one_lds_bytes() { return align_up(sizeof(OneShared), 16) + (size_t)kOneLdsKeys * 4; }
 
 }  // namespace
 }  // namespace dsa
@@ -667,9 +670,8 @@ extern "C" dsa_status dsa_topk(const float* scores, const int32_t* row_len, int 
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (ld <= kOneMaxLd) {
     // one launch, no workspace
-    const bool in_lds = ld <= kOneLdsKeys;
-    const size_t lds = one_lds_bytes(in_lds);
-    auto kern = in_lds ? topk_one_kernel<true> : topk_one_kernel<false>;
+    const size_t lds = one_lds_bytes();
+    auto kern = topk_one_kernel;
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)lds) != hipSuccess) {
       set_error("dsa_topk: %zu bytes of LDS not available", lds);

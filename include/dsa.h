@@ -94,6 +94,8 @@ dsa_status dsa_index_scores(const void* q, const float* w, const void* k_index,
  *
  *   scores  fp32 [B*R, ld] (NaN not allowed)   row_len int32 [B*R]
  *   idx     int32 [B*R, k]                      1 <= k <= 8192
+ * workspace: dsa_topk_workspace_size() bytes (0 when ld <= 35840: one launch
+ *   per call, the row's keys held in LDS); no initialisation required.
  */
 size_t dsa_topk_workspace_size(int B, int R, int64_t ld, int k);
 dsa_status dsa_topk(const float* scores, const int32_t* row_len, int B, int R,

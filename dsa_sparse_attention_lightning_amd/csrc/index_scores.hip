@@ -41,7 +41,10 @@ __global__ __launch_bounds__(kThreads) void index_scores_kernel(
   const int b = blockIdx.y;
   const int tid = threadIdx.x;
   int lmax = 0;
-  for (int r = 0; r < R; ++r) lmax = max(lmax, row_len[b * R + r]);
+  // row lengths are clamped to what the score rows and the block table can
+  // address (a longer row_len is outside the contract; this keeps it in bounds)
+  const int cap = (int)min(ld, (int64_t)max_pages * page);
+  for (int r = 0; r < R; ++r) lmax = max(lmax, min(row_len[b * R + r], cap));
   const int t_begin = blockIdx.x * chunk;
   if (t_begin >= lmax) return;  // uniform across the workgroup
   const int t_end = min(t_begin + chunk, lmax);
@@ -136,7 +139,7 @@ __global__ __launch_bounds__(kThreads) void index_scores_kernel(
       for (int tile = 1; tile < TILES; ++tile)
         if (g == tile) mine = sacc[tile];
       const int t = base + g * 16 + n;
-      if (g < TILES && t < t_end && t < row_len[b * R + r]) scores[(size_t)(b * R + r) * ld + t] = mine;
+      if (g < TILES && t < t_end && t < row_len[b * R + r]) scores[(size_t)(b * R + r) * ld + t] = mine;   // t_end <= cap
     }
   }
 }
@@ -223,7 +226,10 @@ __global__ __launch_bounds__(NWAVE * 64) __attribute__((amdgpu_waves_per_eu(DSA_
   const int l32 = lane & 31;
   const int hi = lane >> 5;
   int lmax = 0;
-  for (int r = 0; r < R; ++r) lmax = max(lmax, row_len[b * R + r]);
+  // row lengths are clamped to what the score rows and the block table can
+  // address (a longer row_len is outside the contract; this keeps it in bounds)
+  const int cap = (int)min(ld, (int64_t)max_pages * page);
+  for (int r = 0; r < R; ++r) lmax = max(lmax, min(row_len[b * R + r], cap));
   const int t_begin = blockIdx.x * chunk;
   if (t_begin >= lmax) return;
   const int t_end = min(t_begin + chunk, lmax);
@@ -409,6 +415,7 @@ extern "C" dsa_status dsa_index_scores(const void* q, const float* w, const void
               "dsa_index_scores: D_I=%d not in {32, 64, 128}", D_I);
   DSA_REQUIRE(H_I <= 64, DSA_ERR_UNSUPPORTED, "dsa_index_scores: H_I=%d > 64", H_I);
   DSA_REQUIRE(R <= 8, DSA_ERR_UNSUPPORTED, "dsa_index_scores: R=%d > 8", R);
+  DSA_REQUIRE(B <= 65535, DSA_ERR_UNSUPPORTED, "dsa_index_scores: B=%d > 65535", B);
   DSA_REQUIRE(ld <= ((int64_t)1 << 31) - 1, DSA_ERR_UNSUPPORTED, "dsa_index_scores: ld too large");
   DSA_REQUIRE(aligned16(q) && aligned16(k_index), DSA_ERR_INVALID_ARG,
               "dsa_index_scores: q and k_index must be 16-byte aligned");

@@ -196,7 +196,8 @@ __global__ __launch_bounds__(kThreads) void mha_attn_kernel(AttnArgs a) {
   const int ntok = min(a.tok_per_split, a.k - t_lo);
   for (int i = tid; i < ntok; i += kThreads) {
     const int t = idx[t_lo + i];
-    s_off[i] = t >= 0 ? (int64_t)bt[t / a.page] * a.page_stride + (int64_t)(t % a.page) * a.row_stride : -1;
+    // positions outside the block table (outside the contract) count as absent
+    s_off[i] = (t >= 0 && t / a.page < a.max_pages) ? (int64_t)bt[t / a.page] * a.page_stride + (int64_t)(t % a.page) * a.row_stride : -1;
   }
 
   uint4 qv[GQ];   // this lane's 8 query dims per head, packed bf16 pairs
@@ -405,7 +406,8 @@ __global__ __launch_bounds__(NW * 64) void latent_attn_kernel(AttnArgs a) {
   const int ntok = min(a.tok_per_split, a.k - t_lo);
   for (int i = tid; i < ntok; i += NT) {
     const int t = idx[t_lo + i];
-    s_off[i] = t >= 0 ? (int64_t)bt[t / a.page] * a.page_stride + (int64_t)(t % a.page) * a.row_stride : -1;
+    // positions outside the block table (outside the contract) count as absent
+    s_off[i] = (t >= 0 && t / a.page < a.max_pages) ? (int64_t)bt[t / a.page] * a.page_stride + (int64_t)(t % a.page) * a.row_stride : -1;
   }
   // Q fragments of this wave's 16 heads: A operand, lane holds head 16w + l%16,
   // dims ks*32 + (l/16)*8 .. +8
@@ -635,6 +637,8 @@ extern "C" dsa_status dsa_sparse_attn(const void* q, const void* k_cache, const 
   DSA_REQUIRE(B >= 1 && S_q >= 1 && H_q >= 1 && H_kv >= 1 && D_qk >= 1 && D_v >= 1 && page >= 1 &&
                   max_pages >= 1 && k >= 1,
               DSA_ERR_INVALID_ARG, "dsa_sparse_attn: sizes must be positive");
+  DSA_REQUIRE((int64_t)B * S_q <= 65535, DSA_ERR_UNSUPPORTED, "dsa_sparse_attn: B*S_q=%lld > 65535",
+              (long long)B * S_q);
   DSA_REQUIRE(idx_rows == 1 || idx_rows == S_q, DSA_ERR_INVALID_ARG,
               "dsa_sparse_attn: idx_rows=%d must be 1 or S_q=%d", idx_rows, S_q);
   DSA_REQUIRE(kv_page_stride >= 0 && kv_row_stride >= 0 && kv_head_stride >= 0, DSA_ERR_INVALID_ARG,

@@ -143,7 +143,7 @@ __global__ __launch_bounds__(kHistThreads) void topk_hist1_kernel(const float* _
                                                                   int64_t ld, int k, RowWs ws) {
   __shared__ uint32_t h[kBins];
   const int row = blockIdx.y;
-  const int L = row_len[row];
+  const int L = (int)min((int64_t)row_len[row], ld);   // row_len <= ld is a precondition
   const int t0 = blockIdx.x * kChunk;
   if (L <= k || t0 >= L) return;
   for (int i = threadIdx.x; i < kBins; i += kHistThreads) h[i] = 0;
@@ -170,7 +170,7 @@ __global__ __launch_bounds__(kHistThreads) void topk_hist2_kernel(const float* _
   __shared__ int s_t1;
   __shared__ uint32_t s_a1;
   const int row = blockIdx.y;
-  const int L = row_len[row];
+  const int L = (int)min((int64_t)row_len[row], ld);   // row_len <= ld is a precondition
   const int t0 = blockIdx.x * kChunk;
   if (L <= k || t0 >= L) return;
   for (int i = threadIdx.x; i < kBins; i += kHistThreads) h[i] = 0;
@@ -202,7 +202,7 @@ __global__ __launch_bounds__(kHistThreads) void topk_collect_kernel(const float*
   __shared__ uint2 l_cand[kChunk];
   __shared__ uint32_t s_n[2], s_base[2];
   const int row = blockIdx.y;
-  const int L = row_len[row];
+  const int L = (int)min((int64_t)row_len[row], ld);   // row_len <= ld is a precondition
   const int t0 = blockIdx.x * kChunk;
   if (L <= k || t0 >= L) return;
   find_threshold_4096(ws.hist1 + (size_t)row * kBins, (uint32_t)k, s_wave, &s_t1, &s_a1);
@@ -314,7 +314,7 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const int32_t*
   __shared__ uint32_t s_cnt;
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
-  const int L = row_len[row];
+  const int L = (int)min((int64_t)row_len[row], ld);   // row_len <= ld is a precondition
   int32_t* dst = idx + (size_t)row * k;
   if (L <= k) {
     for (int i = tid; i < k; i += kFinThreads) dst[i] = i < L ? i : -1;
@@ -666,6 +666,7 @@ extern "C" dsa_status dsa_topk(const float* scores, const int32_t* row_len, int 
               "dsa_topk: sizes must be positive (B=%d R=%d ld=%lld k=%d)", B, R, (long long)ld, k);
   DSA_REQUIRE(k <= kMaxK, DSA_ERR_UNSUPPORTED, "dsa_topk: k=%d > %d", k, kMaxK);
   DSA_REQUIRE(ld <= ((int64_t)1 << 31) - 1, DSA_ERR_UNSUPPORTED, "dsa_topk: ld too large");
+  DSA_REQUIRE((int64_t)B * R <= 65535, DSA_ERR_UNSUPPORTED, "dsa_topk: B*R=%lld rows > 65535", (long long)B * R);
   const int rows = B * R;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (ld <= kOneMaxLd) {

@@ -77,7 +77,8 @@ int dsa_abi_version(void);
  * Products are exact bf16*bf16 in fp32; dot products accumulate in fp32
  * (MFMA), the ReLU/weight/head sum runs in fp32.
  * Supported: D_I in {32, 64, 128}, 1 <= H_I <= 64, 1 <= R <= 8,
- * R*H_I padded to 16 <= 512.  q and k_index 16-byte aligned.
+ * B <= 65535.  q and k_index 16-byte aligned.  A row_len beyond the bound
+ * above is clamped to it (no access outside the score rows or the table).
  */
 dsa_status dsa_index_scores(const void* q, const float* w, const void* k_index,
                             const int32_t* block_table, const int32_t* row_len,
@@ -93,7 +94,8 @@ dsa_status dsa_index_scores(const void* q, const float* w, const void* k_index,
  * ascending position order and the rest of the row is filled with -1.
  *
  *   scores  fp32 [B*R, ld] (NaN not allowed)   row_len int32 [B*R]
- *   idx     int32 [B*R, k]                      1 <= k <= 8192
+ *   idx     int32 [B*R, k]                      1 <= k <= 8192, B*R <= 65535
+ * A row_len above ld is treated as ld.
  * workspace: dsa_topk_workspace_size() bytes (0 when ld <= 35840: one launch
  *   per call, the row's keys held in LDS); no initialisation required.
  */
@@ -122,15 +124,16 @@ dsa_status dsa_topk(const float* scores, const int32_t* row_len, int B, int R,
  *   k_cache, v_cache  bf16 paged; v_cache may equal k_cache (latent KV,
  *            V = the first D_v dims of the key row)
  *   idx      int32 [B, idx_rows, k], idx_rows = 1 (shared by every query
- *            row) or S_q (one set per row); -1 entries are ignored
+ *            row) or S_q (one set per row); -1 entries, and positions at or
+ *            past page*max_pages, are ignored
  *   lse      fp32 [B, S_q, H_q] or NULL
  * workspace: dsa_sparse_attn_workspace_size() bytes (0: none needed) for
  *   split-k partial results; no initialisation required.
  * Supported: (H_q == H_kv or H_q/H_kv in {2, 4}) with D_qk == D_v in
  * {64, 128}; or H_kv == 1, H_q == 64, D_qk == 576, D_v == 512 with
  * v_cache == k_cache (latent MQA; QK^T and PV on bf16 MFMA, P rounded to
- * bf16).  k <= 131072 (latent: k <= 32768).  Rows/heads/base pointers
- * 16-byte aligned.
+ * bf16).  k <= 131072 (latent: k <= 32768), B*S_q <= 65535.  Rows/heads/base
+ * pointers 16-byte aligned.
  */
 size_t dsa_sparse_attn_workspace_size(int B, int S_q, int H_q, int H_kv,
                                       int D_qk, int D_v, int k);

@@ -54,6 +54,7 @@ def test_index_scores_validation():
     assert _scores_call(D=96) == _lib.DSA_ERR_UNSUPPORTED
     assert _scores_call(H=65) == _lib.DSA_ERR_UNSUPPORTED
     assert _scores_call(R=9) == _lib.DSA_ERR_UNSUPPORTED
+    assert _scores_call(B=65536) == _lib.DSA_ERR_UNSUPPORTED          # grid limit
     assert _scores_call(q=MISALIGNED) == _lib.DSA_ERR_INVALID_ARG
 
 
@@ -67,6 +68,9 @@ def test_topk_validation():
     assert lib.dsa_topk(FAKE, FAKE, 1, 1, 100, 9000, FAKE, FAKE, ws, None) == _lib.DSA_ERR_UNSUPPORTED
     assert lib.dsa_topk(FAKE, FAKE, 2, 1, 200000, 64, FAKE, FAKE, ws - 1, None) == _lib.DSA_ERR_WORKSPACE
     assert lib.dsa_topk(FAKE, FAKE, 2, 1, 200000, 64, FAKE, None, ws, None) == _lib.DSA_ERR_WORKSPACE
+    assert lib.dsa_topk(FAKE, FAKE, 8192, 8, 100, 8, FAKE, FAKE, ws, None) == _lib.DSA_ERR_UNSUPPORTED   # B*R > 65535
+    assert lib.dsa_topk_workspace_size(1, 1, 35840, 64) == 0            # keys fit in LDS: one launch
+    assert lib.dsa_topk_workspace_size(1, 1, 35841, 64) > 0
 
 
 def _attn_call(**over):
@@ -88,6 +92,7 @@ def test_sparse_attn_validation():
     assert _attn_call(idx_rows=3, S_q=2) == _lib.DSA_ERR_INVALID_ARG
     assert _attn_call(rs=64 * 128 + 4) == _lib.DSA_ERR_INVALID_ARG    # row not 16-byte aligned
     assert _attn_call(scale=float("nan")) == _lib.DSA_ERR_INVALID_ARG
+    assert _attn_call(B=65536) == _lib.DSA_ERR_UNSUPPORTED            # B*S_q grid limit
     need = lib.dsa_sparse_attn_workspace_size(1, 1, 64, 64, 128, 128, 2048)
     assert need > 0
     assert _attn_call(ws_bytes=need - 1) == _lib.DSA_ERR_WORKSPACE

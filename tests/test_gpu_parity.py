@@ -435,6 +435,38 @@ def test_mixed_kv_negative_control(poison):
 
 
 # ----------------------------------------------------------------------------
+# lengths and positions outside the contract are clamped, never read or
+# written out of bounds
+# ----------------------------------------------------------------------------
+def test_out_of_contract_lengths_are_clamped():
+    d = I.draft_inputs(71, [3000], H_I=64, D_I=128, H_q=16, H_kv=16, D_qk=128, D_v=128, k=256, G=2,
+                       integer_indexer=True)
+    dd = DraftDev(d)
+    ld = 3002
+    cap = min(ld, d.page * d.max_pages)
+    ref = dsa.index_scores(dd.q_index, dd.w, dd.kidx, dd.bt, torch.full((1, 1), cap, dtype=torch.int32, device=DEV),
+                           page=d.page, ld=ld)
+    big = torch.full((1, 1), 1 << 30, dtype=torch.int32, device=DEV)
+    got = dsa.index_scores(dd.q_index, dd.w, dd.kidx, dd.bt, big, page=d.page, ld=ld)
+    assert torch.equal(got[..., :cap], ref[..., :cap])
+    # top-k: a row_len above ld acts as ld (one-workgroup and pipeline paths)
+    for L in (3002, 40000):
+        sc = torch.randn((1, 1, L), device=DEV)
+        a = dsa.topk(sc, torch.full((1, 1), L, dtype=torch.int32, device=DEV), 256)
+        b = dsa.topk(sc, torch.full((1, 1), L + 1000, dtype=torch.int32, device=DEV), 256)
+        assert torch.equal(a, b)
+    # attention: positions past the block table are ignored like -1
+    idx = dsa.topk(ref, torch.full((1, 1), 3000, dtype=torch.int32, device=DEV), d.k)[:, 0]
+    bad = idx.clone()
+    bad[0, :5] = d.page * d.max_pages + torch.arange(5, device=DEV, dtype=torch.int32) * 1000
+    neg = idx.clone()
+    neg[0, :5] = -1
+    o1, l1 = dsa.sparse_attn(dd.q[0][:, None], dd.k, dd.v, dd.bt, bad, page=d.page, sm_scale=d.sm_scale)
+    o2, l2 = dsa.sparse_attn(dd.q[0][:, None], dd.k, dd.v, dd.bt, neg, page=d.page, sm_scale=d.sm_scale)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# ----------------------------------------------------------------------------
 # HIP graph capture of the draft block: every replay matches the eager result
 # ----------------------------------------------------------------------------
 def test_draft_block_graph_replays():

@@ -16,6 +16,8 @@
 // re-used for every key tile the workgroup streams.  The epilogue (ReLU, * w,
 // sum over heads) stays in fp32: a lane holds 4 heads x 1 position per
 // 16-head block, sums them, and two cross-lane adds finish the head sum.
+#include <type_traits>
+
 #include "dsa_common.h"
 
 namespace dsa {
@@ -188,8 +190,8 @@ dsa_status launch_index(const void* q, const float* w, const void* kidx, const i
 // ---------------------------------------------------------------------------
 // Several query rows (R >= 2, e.g. the verify-pass shape with one row per
 // chained position): the contraction has M = R * 64 (row, head) pairs, so it
-// is a real GEMM.  Wave w owns RPW query rows = RPW*2 M blocks of 32 (row,
-// head) pairs, whose Q fragments stay in registers for the whole kernel.  The
+// is a real GEMM.  Wave w owns query row w = 2 M blocks of 32 (row, head)
+// pairs, whose Q fragments stay in registers for the whole kernel.  The
 // workgroup stages 32-position key tiles in LDS once for all its waves (the
 // next tile is prefetched into registers while the current one is consumed)
 // and every wave runs v_mfma_f32_32x32x16_bf16 over them.  Epilogue as in the
@@ -204,19 +206,19 @@ constexpr int kMaxChunkPositions = 4096;   // per-workgroup chunk cap (LDS row t
 #ifndef DSA_INDEX_WPE
 #define DSA_INDEX_WPE 2
 #endif
-template <int KS16, int RPW, int NWAVE>
+template <int KS16, int NWAVE>
 __global__ __launch_bounds__(NWAVE * 64) __attribute__((amdgpu_waves_per_eu(DSA_INDEX_WPE))) void index_scores_rows_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ w, const uint16_t* __restrict__ kidx,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ row_len, float* __restrict__ scores,
     int R, int H, int page, int max_pages, int64_t ld, int chunk) {
   constexpr int D = KS16 * 16;
   constexpr int NT = NWAVE * 64;
-  constexpr int MBW = RPW * 2;                       // 32-row M blocks per wave
+  constexpr int MBW = 2;                             // 32-row M blocks per wave (one row)
   constexpr int KROW = D * 2 + 16;                   // padded LDS row (bytes)
   constexpr int CHUNKS = kRowsTile * D / 8;          // 16-byte pieces per tile
   constexpr int PER = (CHUNKS + NT - 1) / NT;
   __shared__ __align__(16) unsigned char s_k[2 * kRowsTile * KROW];
-  __shared__ __align__(16) float s_w[NWAVE * RPW][64];
+  __shared__ __align__(16) float s_w[NWAVE][64];
   __shared__ int s_row[kMaxChunkPositions];   // physical key row of each chunk position
 
   const int b = blockIdx.y;
@@ -240,24 +242,23 @@ __global__ __launch_bounds__(NWAVE * 64) __attribute__((amdgpu_waves_per_eu(DSA_
     const int t = t_begin + i;
     s_row[i] = bt[t / page] * page + t % page;
   }
-  // the row this lane stores and how far it is valid (read before the tile
-  // loop, so that the loop's only global loads are the key prefetches)
-  const int r_st = RPW == 2 ? wave * 2 + hi : wave;
-  const int t_lim = (r_st < R && (RPW == 2 || hi == 0)) ? min(t_end, row_len[b * R + r_st]) : 0;
+  // how far this lane's row is valid (read before the tile loop, so that the
+  // loop's only global loads are the key prefetches); the low lane half stores
+  const int t_lim = (wave < R && hi == 0) ? min(t_end, row_len[b * R + wave]) : 0;
 
-  // Q fragments: block mb = (row 2w + mb/2... generally RPW*w + mb/2, heads (mb%2)*32 + l%32)
+  // Q fragments: block mb = row w, heads mb*32 + l%32
   bf16x8_t qa[MBW][KS16];
 #pragma unroll
   for (int mb = 0; mb < MBW; ++mb) {
-    const int r = wave * RPW + mb / 2;
-    const int h = (mb % 2) * 32 + l32;
+    const int r = wave;
+    const int h = mb * 32 + l32;
     const bool ok = r < R && h < H;
     const uint16_t* src = q + ((size_t)(b * R + (ok ? r : 0)) * H + (ok ? h : 0)) * D + hi * 8;
 #pragma unroll
     for (int ks = 0; ks < KS16; ++ks)
       qa[mb][ks] = ok ? *reinterpret_cast<const bf16x8_t*>(src + ks * 16) : bf16x8_t{};
   }
-  for (int i = tid; i < NWAVE * RPW * 64; i += NT) {
+  for (int i = tid; i < NWAVE * 64; i += NT) {
     const int r = i / 64, h = i % 64;
     s_w[r][h] = (r < R && h < H) ? 0.5f * w[(size_t)(b * R + r) * H + h] : 0.f;
   }
@@ -310,31 +311,25 @@ __global__ __launch_bounds__(NWAVE * 64) __attribute__((amdgpu_waves_per_eu(DSA_
       kb = kn;
     }
     // epilogue: rows of block mb are heads (mb%2)*32 + (v/4)*8 + hi*4 + v%4
-    float part[RPW];
-#pragma unroll
-    for (int rr = 0; rr < RPW; ++rr) part[rr] = 0.f;
+    float part = 0.f;
 #pragma unroll
     for (int mb = 0; mb < MBW; ++mb) {
-      const int rloc = wave * RPW + mb / 2;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         // s_w holds w/2, and (x + |x|) * (w/2) equals w * ReLU(x) exactly
         // (power-of-two scaling), without a compare per element
-        const float4 wv = *reinterpret_cast<const float4*>(&s_w[rloc][(mb % 2) * 32 + g * 8 + hi * 4]);
-        float sum = part[mb / 2];
-        sum = fmaf(wv.x, acc[mb][g * 4 + 0] + fabsf(acc[mb][g * 4 + 0]), sum);
-        sum = fmaf(wv.y, acc[mb][g * 4 + 1] + fabsf(acc[mb][g * 4 + 1]), sum);
-        sum = fmaf(wv.z, acc[mb][g * 4 + 2] + fabsf(acc[mb][g * 4 + 2]), sum);
-        sum = fmaf(wv.w, acc[mb][g * 4 + 3] + fabsf(acc[mb][g * 4 + 3]), sum);
-        part[mb / 2] = sum;
+        const float4 wv = *reinterpret_cast<const float4*>(&s_w[wave][mb * 32 + g * 8 + hi * 4]);
+        part = fmaf(wv.x, acc[mb][g * 4 + 0] + fabsf(acc[mb][g * 4 + 0]), part);
+        part = fmaf(wv.y, acc[mb][g * 4 + 1] + fabsf(acc[mb][g * 4 + 1]), part);
+        part = fmaf(wv.z, acc[mb][g * 4 + 2] + fabsf(acc[mb][g * 4 + 2]), part);
+        part = fmaf(wv.w, acc[mb][g * 4 + 3] + fabsf(acc[mb][g * 4 + 3]), part);
       }
     }
-#pragma unroll
-    for (int rr = 0; rr < RPW; ++rr) part[rr] += __shfl_xor(part[rr], 32, 64);
-    // lane half hi stores row wave*RPW + hi (RPW = 2) or row wave (RPW = 1, low half only)
+    part += __shfl_xor(part, 32, 64);
+    // the low lane half stores row `wave`
     const int t = t0 + l32;
-    const float v = (RPW == 2 && hi) ? part[RPW - 1] : part[0];
-    if (t < t_lim) scores[(size_t)(b * R + r_st) * ld + t] = v;
+    const float v = part;
+    if (t < t_lim) scores[(size_t)(b * R + wave) * ld + t] = v;
     return next;
   };
   __syncthreads();   // s_row, s_w ready
@@ -356,6 +351,195 @@ __global__ __launch_bounds__(NWAVE * 64) __attribute__((amdgpu_waves_per_eu(DSA_
   if (tg + 2 < n_tiles) tile_step(pre2, tg + 2);
 }
 
+// Five to eight rows: eight waves, one query row each (Q fragments 64 VGPRs,
+// head weights 32, two accumulator sets 64), two waves per SIMD.  Key tiles
+// are staged in LDS four at a time (128 positions per barrier, two stages in
+// flight in registers), and each wave software-pipelines its tiles: the
+// MFMAs of tile i issue while its VALU runs the epilogue of tile i-1 out of
+// the other accumulator set, with the weights in registers (no LDS access in
+// the epilogue).  Same arithmetic, in the same order, as
+// index_scores_rows_kernel.
+#ifndef DSA_INDEX_SUPER_WGS
+#define DSA_INDEX_SUPER_WGS 256
+#endif
+constexpr int kSuperTiles = 4;                        // 32-position tiles per LDS stage
+constexpr int kSuperPos = kSuperTiles * kRowsTile;    // 128 positions
+constexpr int kSuperThreads = 512;
+
+template <int KS16>
+constexpr size_t super_lds_bytes() {
+  return (size_t)2 * kSuperPos * (KS16 * 32 + 16);
+}
+
+template <int KS16>
+__global__ __launch_bounds__(kSuperThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void index_scores_rows8_kernel(
+    const uint16_t* __restrict__ q, const float* __restrict__ w, const uint16_t* __restrict__ kidx,
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ row_len, float* __restrict__ scores,
+    int R, int H, int page, int max_pages, int64_t ld, int chunk) {
+  constexpr int NT = kSuperThreads;
+  constexpr int MBW = 2;                               // 32-head M blocks of the wave's row
+  constexpr int D = KS16 * 16;
+  constexpr int KROW = D * 2 + 16;                     // padded LDS row (bytes)
+  constexpr int CHUNKS = kSuperPos * D / 8;            // 16-byte pieces per stage
+  static_assert(CHUNKS % NT == 0, "stage pieces must divide evenly");
+  constexpr int PER = CHUNKS / NT;
+  constexpr int EPS = 16 / KS16;                       // epilogue elements per MFMA slot
+  constexpr int PF = 2;                                // stages in flight
+  extern __shared__ __align__(16) unsigned char s_k[];   // [2][kSuperPos][KROW]
+  __shared__ int s_row[kMaxChunkPositions];
+
+  const int b = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  int lmax = 0;
+  const int cap = (int)min(ld, (int64_t)max_pages * page);
+  for (int r = 0; r < R; ++r) lmax = max(lmax, min(row_len[b * R + r], cap));
+  const int t_begin = blockIdx.x * chunk;
+  if (t_begin >= lmax) return;
+  const int t_end = min(t_begin + chunk, lmax);
+  const int32_t* bt = block_table + (size_t)b * max_pages;
+  for (int i = tid; i < t_end - t_begin; i += NT) {
+    const int t = t_begin + i;
+    s_row[i] = bt[t / page] * page + t % page;
+  }
+  // wave w owns row w; after the cross-half sum the low lane half stores it
+  const int t_lim = (wave < R && hi == 0) ? min(t_end, row_len[b * R + wave]) : 0;
+
+  bf16x8_t qa[MBW][KS16];
+  float wr[MBW][16];   // w/2 of the heads this lane's accumulator registers hold
+#pragma unroll
+  for (int mb = 0; mb < MBW; ++mb) {
+    const int h = mb * 32 + l32;
+    const bool ok = wave < R && h < H;
+    const uint16_t* src = q + ((size_t)(b * R + (ok ? wave : 0)) * H + (ok ? h : 0)) * D + hi * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS16; ++ks)
+      qa[mb][ks] = ok ? *reinterpret_cast<const bf16x8_t*>(src + ks * 16) : bf16x8_t{};
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int hv = mb * 32 + (v / 4) * 8 + hi * 4 + v % 4;
+      wr[mb][v] = (wave < R && hv < H) ? 0.5f * w[(size_t)(b * R + wave) * H + hv] : 0.f;
+    }
+  }
+  __syncthreads();   // s_row ready
+
+  struct Slot {
+    uint4 v[PER];
+  };
+  // physical key rows of the stage fetched next, read one stage ahead of use
+  int krow[PER];
+  auto read_rows = [&](int st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int c = tid + j * NT;
+      const int t = min(t_begin + st * kSuperPos + c / (D / 8), t_end - 1);
+      krow[j] = s_row[t - t_begin];
+    }
+  };
+  auto fetch = [&]() __attribute__((always_inline)) {
+    Slot out;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int c = tid + j * NT;
+      out.v[j] = *reinterpret_cast<const uint4*>(kidx + (size_t)krow[j] * D + (c % (D / 8)) * 8);
+    }
+    return out;
+  };
+  const f32x16_t zero{};
+  auto epilogue_store = [&](float p, int g) __attribute__((always_inline)) {
+    // head sum across the lane halves: lane l gets p(l) + p(l ^ 32)
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p), __float_as_uint(p), false, false);
+    const float v = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    const int t = t_begin + g * kRowsTile + l32;
+    if (t < t_lim) scores[(size_t)(b * R + wave) * ld + t] = v;
+  };
+  auto epi_elem = [&](const f32x16_t (&accP)[MBW], int e, float& p) __attribute__((always_inline)) {
+    const int mb = e / 16, v = e % 16;
+    const float x = accP[mb][v];
+    // (x + |x|) * (w/2) equals w * ReLU(x) exactly
+    p = fmaf(wr[mb][v], x + fabsf(x), p);
+  };
+  // B fragments of a stage are read in order f = u * KS16 + ks (tile u,
+  // k step ks) through a ring, BPF fragments ahead of their MFMAs
+  constexpr int BPF = 2;
+  constexpr int NF = kSuperTiles * KS16;
+  bf16x8_t kf[BPF + 1];
+  auto frag = [&](const unsigned char* bbase, int f) __attribute__((always_inline)) {
+    return *reinterpret_cast<const bf16x8_t*>(bbase + (f / KS16) * kRowsTile * KROW + (f % KS16) * 32);
+  };
+  // tile U of the stage (global tile g): MFMAs into accC and, interleaved
+  // with them, the epilogue of tile g-1 out of accP
+  auto tile = [&](auto has_prev, auto u_c, const unsigned char* bbase, int g, f32x16_t (&accC)[MBW],
+                  f32x16_t (&accP)[MBW]) __attribute__((always_inline)) {
+    constexpr bool EPI = decltype(has_prev)::value;
+    constexpr int U = decltype(u_c)::value;
+    float p = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS16; ++ks) {
+      const int f = U * KS16 + ks;
+      if (f + BPF < NF) kf[(f + BPF) % (BPF + 1)] = frag(bbase, f + BPF);
+#pragma unroll
+      for (int mb = 0; mb < MBW; ++mb) {
+        accC[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mb][ks], kf[f % (BPF + 1)], ks == 0 ? zero : accC[mb], 0, 0, 0);
+        if constexpr (EPI) {
+#pragma unroll
+          for (int e = 0; e < EPS; ++e) epi_elem(accP, (ks * MBW + mb) * EPS + e, p);
+        }
+      }
+    }
+    if constexpr (EPI) epilogue_store(p, g - 1);
+  };
+  using no_prev = std::integral_constant<bool, false>;
+  using with_prev = std::integral_constant<bool, true>;
+  f32x16_t accA[MBW], accB[MBW];
+  // one stage: store it to LDS, prefetch PF stages ahead, run its four tiles
+  // (even tiles in set A, odd in set B)
+  auto step = [&](auto first, Slot slot, int st) __attribute__((always_inline)) {
+    unsigned char* buf = s_k + (st & 1) * (kSuperPos * KROW);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int c = tid + j * NT;
+      *reinterpret_cast<uint4*>(buf + (c / (D / 8)) * KROW + (c % (D / 8)) * 16) = slot.v[j];
+    }
+    __syncthreads();
+    const Slot next = fetch();   // stage st + PF (rows read last step)
+    read_rows(st + PF + 1);
+    const unsigned char* bbase = buf + l32 * KROW + hi * 16;
+#pragma unroll
+    for (int f = 0; f < BPF; ++f) kf[f] = frag(bbase, f);
+    const int g = st * kSuperTiles;
+    if constexpr (decltype(first)::value) tile(no_prev{}, std::integral_constant<int, 0>{}, bbase, g, accA, accB);
+    else tile(with_prev{}, std::integral_constant<int, 0>{}, bbase, g, accA, accB);
+    tile(with_prev{}, std::integral_constant<int, 1>{}, bbase, g + 1, accB, accA);
+    tile(with_prev{}, std::integral_constant<int, 2>{}, bbase, g + 2, accA, accB);
+    tile(with_prev{}, std::integral_constant<int, 3>{}, bbase, g + 3, accB, accA);
+    return next;
+  };
+  using first_stage = std::integral_constant<bool, true>;
+  using later_stage = std::integral_constant<bool, false>;
+  const int n_st = (t_end - t_begin + kSuperPos - 1) / kSuperPos;
+  read_rows(0);
+  Slot pre0 = fetch();
+  read_rows(1);
+  Slot pre1 = fetch();
+  read_rows(2);
+  pre0 = step(first_stage{}, pre0, 0);
+  int st = 1;
+  for (; st + 2 <= n_st; st += 2) {   // whole rounds (stage st in slot st % 2)
+    pre1 = step(later_stage{}, pre1, st);
+    pre0 = step(later_stage{}, pre0, st + 1);
+  }
+  if (st < n_st) step(later_stage{}, pre1, st);
+  // the last tile (odd index) is still in set B
+  float p = 0.f;
+#pragma unroll
+  for (int e = 0; e < MBW * 16; ++e) epi_elem(accB, e, p);
+  epilogue_store(p, n_st * kSuperTiles - 1);
+}
+
 template <int KS16>
 dsa_status launch_rows(const void* q, const float* w, const void* kidx, const int32_t* bt, const int32_t* row_len,
                        float* scores, int B, int R, int H, int page, int max_pages, int64_t ld, hipStream_t s) {
@@ -370,16 +554,32 @@ dsa_status launch_rows(const void* q, const float* w, const void* kidx, const in
   dim3 grid((unsigned)((ld + chunk - 1) / chunk), (unsigned)B);
   const uint16_t* qq = static_cast<const uint16_t*>(q);
   const uint16_t* kk = static_cast<const uint16_t*>(kidx);
-  // up to 4 rows: one row per wave (Q fragments 64 VGPRs); 5..8 rows: two
-  // rows per wave in four waves (128 VGPRs of Q; rows past R hold zero Q)
-#define DSA_ROWS_LAUNCH(RPW, NW) \
-  hipLaunchKernelGGL((index_scores_rows_kernel<KS16, RPW, NW>), grid, dim3(NW * 64), 0, s, qq, w, kk, bt, row_len, \
+  // up to 4 rows: one wave per row; 5..8 rows: eight waves (rows past R hold
+  // zero Q), staged four tiles per barrier and software-pipelined
+#define DSA_ROWS_LAUNCH(NW) \
+  hipLaunchKernelGGL((index_scores_rows_kernel<KS16, NW>), grid, dim3(NW * 64), 0, s, qq, w, kk, bt, row_len, \
                      scores, R, H, page, max_pages, ld, chunk)
   switch (R) {
-    case 2: DSA_ROWS_LAUNCH(1, 2); break;
-    case 3: DSA_ROWS_LAUNCH(1, 3); break;
-    case 4: DSA_ROWS_LAUNCH(1, 4); break;
-    default: DSA_ROWS_LAUNCH(2, 4); break;
+    case 2: DSA_ROWS_LAUNCH(2); break;
+    case 3: DSA_ROWS_LAUNCH(3); break;
+    case 4: DSA_ROWS_LAUNCH(4); break;
+    default: {
+      // five to eight rows: one workgroup per CU, chunks of whole 128-position stages
+      int sp = (int)((tiles * B + DSA_INDEX_SUPER_WGS - 1) / DSA_INDEX_SUPER_WGS);
+      sp = (sp + kSuperTiles - 1) / kSuperTiles * kSuperTiles;
+      sp = sp > kMaxChunkPositions / kRowsTile ? kMaxChunkPositions / kRowsTile : sp;
+      const int schunk = sp * kRowsTile;
+      const size_t lds = super_lds_bytes<KS16>();
+      auto kern = index_scores_rows8_kernel<KS16>;
+      if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)lds) != hipSuccess) {
+        set_error("dsa_index_scores: %zu bytes of LDS not available", lds);
+        return DSA_ERR_HIP;
+      }
+      hipLaunchKernelGGL(kern, dim3((unsigned)((ld + schunk - 1) / schunk), (unsigned)B), dim3(kSuperThreads), lds, s,
+                         qq, w, kk, bt, row_len, scores, R, H, page, max_pages, ld, schunk);
+      break;
+    }
   }
 #undef DSA_ROWS_LAUNCH
   return launch_status("dsa_index_scores");

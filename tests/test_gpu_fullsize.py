@@ -142,6 +142,17 @@ def test_long_1m_latent():
     log(f"  latent attention max err {err:.2e}")
 
 
+@pytest.mark.parametrize("integer", [True, False])
+def test_indexer_1m_8rows(integer):
+    """The 8-row indexer at 2^20 positions (verify-pass shape), as the benchmark launches it."""
+    log("indexer_1m_8rows", integer)
+    d = DI.draft_inputs(5, [1 << 20], H_I=64, D_I=128, H_q=64, D_qk=576, D_v=512, k=2048, G=0, R=8, latent=True,
+                        integer_indexer=integer)
+    scores = dsa.index_scores(d.q_index, d.w, d.kidx, d.block_table, d.row_len, page=d.page, ld=d.ld)
+    torch.cuda.synchronize()
+    check_scores(d, scores, 0, exact=integer, n_sample=2048, seed=1)
+
+
 @pytest.mark.parametrize("std", [0.5, 2.0, 6.0])
 def test_verify_256x8x151552(std):
     B, G, V = 256, 7, 151552

@@ -37,6 +37,9 @@ def log(*a):
     dict(lens=[3001, 1500], H_I=64, D_I=128, page=64, shuffle=True, R=1),  # ragged, paged
     dict(lens=[777], H_I=20, D_I=64, page=16, shuffle=True, R=3),          # odd heads, 3 rows
     dict(lens=[2048], H_I=64, D_I=128, page=64, shuffle=False, R=8),       # verify-pass rows
+    dict(lens=[4133, 900], H_I=64, D_I=64, page=16, shuffle=True, R=5),    # 5 rows, ragged, 2 sequences
+    dict(lens=[1300], H_I=48, D_I=32, page=64, shuffle=True, R=7),         # 7 rows, partial head block
+    dict(lens=[9000], H_I=64, D_I=128, page=64, shuffle=True, R=6),        # 6 rows, several tiles per workgroup
 ])
 def test_index_scores_exact(case):
     log("index_scores", case)

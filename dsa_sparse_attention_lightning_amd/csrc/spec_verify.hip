@@ -440,13 +440,36 @@ __device__ __forceinline__ RowWeights decided_row(const VerifyArgs& a, const Dec
 }
 
 // Kernel 3: the mass of one chunk (CT tiles) of the sampled row (sum of its
-// tile masses in tile order).
-template <int CT, bool NT>
+// tile masses in tile order).  With DECIDE (a few sequences, where one launch
+// costs more than the repeated work) every workgroup runs the decision itself
+// from the chunk partials, chunk 0 records it for the pick kernel, and the
+// separate decide launch is skipped; the decision is the same bits either way.
+template <int CT, bool NT, bool DECIDE>
 __global__ __launch_bounds__(kMassThreads) void verify_mass_kernel(VerifyArgs a, VerifyWs ws) {
   __shared__ float s_tile[CT];
   const int c = blockIdx.x;
   const int b = blockIdx.y;
-  const RowWeights rw = decided_row(a, ws.dec[b], b);
+  RowWeights rw;
+  if constexpr (DECIDE) {
+    __shared__ float s_m[2 * kMaxG + 1], s_z[2 * kMaxG + 1];
+    __shared__ int s_jstar;
+    __shared__ float s_us;
+    decide(a, ws, b, s_m, s_z, &s_jstar, &s_us, c == 0);
+    rw = sampled_row(a, b, s_jstar, s_m, s_z);
+    if (c == 0 && threadIdx.x == 0) {
+      Decision dd;
+      dd.jstar = s_jstar;
+      dd.us = s_us;
+      dd.mt = rw.mt;
+      dd.inv_zt = rw.inv_zt;
+      dd.md = rw.md;
+      dd.inv_zd = rw.inv_zd;
+      dd.pad0 = dd.pad1 = 0;
+      ws.dec[b] = dd;
+    }
+  } else {
+    rw = decided_row(a, ws.dec[b], b);
+  }
   const int ntiles = (a.V + kTile - 1) / kTile;
   const int t0 = c * CT;
   const int t1 = min(t0 + CT, ntiles);
@@ -788,15 +811,23 @@ extern "C" dsa_status spec_verify(const float* target_logits, const float* draft
   else hipLaunchKernelGGL(verify_stats_kernel<false>, gs, dim3(kStatThreads), 0, s, a);
   dsa_status st = launch_status("spec_verify(stats)");
   if (st != DSA_OK) return st;
-  hipLaunchKernelGGL(verify_decide_kernel, dim3(B), dim3(kDecideThreads), 0, s, a, ws);
-  st = launch_status("spec_verify(decide)");
-  if (st != DSA_OK) return st;
-  if (ws.chunk_tiles == kBigChunkTiles) {
-    if (nt) hipLaunchKernelGGL((verify_mass_kernel<kBigChunkTiles, true>), gm, dim3(kMassThreads), 0, s, a, ws);
-    else hipLaunchKernelGGL((verify_mass_kernel<kBigChunkTiles, false>), gm, dim3(kMassThreads), 0, s, a, ws);
+#ifndef DSA_VERIFY_FUSE_MAX_B
+#define DSA_VERIFY_FUSE_MAX_B 8
+#endif
+  if (B <= DSA_VERIFY_FUSE_MAX_B && !nt && ws.chunk_tiles == kSmallChunkTiles) {
+    // decision inside the mass kernel: three launches
+    hipLaunchKernelGGL((verify_mass_kernel<kSmallChunkTiles, false, true>), gm, dim3(kMassThreads), 0, s, a, ws);
   } else {
-    if (nt) hipLaunchKernelGGL((verify_mass_kernel<kSmallChunkTiles, true>), gm, dim3(kMassThreads), 0, s, a, ws);
-    else hipLaunchKernelGGL((verify_mass_kernel<kSmallChunkTiles, false>), gm, dim3(kMassThreads), 0, s, a, ws);
+    hipLaunchKernelGGL(verify_decide_kernel, dim3(B), dim3(kDecideThreads), 0, s, a, ws);
+    st = launch_status("spec_verify(decide)");
+    if (st != DSA_OK) return st;
+    if (ws.chunk_tiles == kBigChunkTiles) {
+      if (nt) hipLaunchKernelGGL((verify_mass_kernel<kBigChunkTiles, true, false>), gm, dim3(kMassThreads), 0, s, a, ws);
+      else hipLaunchKernelGGL((verify_mass_kernel<kBigChunkTiles, false, false>), gm, dim3(kMassThreads), 0, s, a, ws);
+    } else {
+      if (nt) hipLaunchKernelGGL((verify_mass_kernel<kSmallChunkTiles, true, false>), gm, dim3(kMassThreads), 0, s, a, ws);
+      else hipLaunchKernelGGL((verify_mass_kernel<kSmallChunkTiles, false, false>), gm, dim3(kMassThreads), 0, s, a, ws);
+    }
   }
   st = launch_status("spec_verify(mass)");
   if (st != DSA_OK) return st;

@@ -304,6 +304,76 @@ __device__ void select_candidates(const uint2* cand_g, const uint64_t* cand_l, i
   __syncthreads();
 }
 
+// Ascending bitonic sort of list[0, 256*E), E elements per thread in
+// registers (threads 0..255 hold data; every thread of the block must call
+// it, for the barriers).  Strides below E are swaps inside a thread, strides
+// below 64*E lane exchanges inside a wave, and only strides of a wave's whole
+// span or more go through LDS (two barriers each: 3 of the 66 stages at 2048
+// elements, instead of a barrier per stage).
+template <int E>
+__device__ void sort_regs(int32_t* list) {
+  constexpr int P = 256 * E;
+  constexpr int WE = 64 * E;
+  const int tid = threadIdx.x;
+  const bool act = tid < 256;
+  const int lane = tid & 63;
+  const int base = (tid >> 6) * WE + lane * E;
+  int32_t a[E];
+  if (act) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) a[e] = list[base + e];
+  }
+#pragma unroll
+  for (int size = 2; size <= P; size <<= 1) {
+#pragma unroll
+    for (int stride = size / 2; stride > 0; stride >>= 1) {
+      if (stride >= WE) {
+        // element i keeps min(a_i, a_{i^stride}) if it is the lower index of
+        // an ascending block or the upper index of a descending one, else max
+        if (act) {
+#pragma unroll
+          for (int e = 0; e < E; ++e) list[base + e] = a[e];
+        }
+        __syncthreads();
+        if (act) {
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            const int i = base + e;
+            const int32_t p = list[i ^ stride];
+            a[e] = (((i & stride) == 0) == ((i & size) == 0)) ? min(a[e], p) : max(a[e], p);
+          }
+        }
+        __syncthreads();
+      } else if (stride >= E) {
+        if (act) {
+          const int lx = stride / E;
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            const int i = base + e;
+            const int32_t p = __shfl_xor(a[e], lx, 64);
+            a[e] = (((i & stride) == 0) == ((i & size) == 0)) ? min(a[e], p) : max(a[e], p);
+          }
+        }
+      } else if (act) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          if ((e & stride) == 0) {
+            const int32_t x = a[e], y = a[e | stride];
+            const bool asc = ((base + e) & size) == 0;
+            a[e] = asc ? min(x, y) : max(x, y);
+            a[e | stride] = asc ? max(x, y) : min(x, y);
+          }
+        }
+      }
+    }
+  }
+  if (act) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) list[base + e] = a[e];
+  }
+  __syncthreads();
+}
+
 __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const int32_t* __restrict__ row_len, int k,
                                                                   int32_t* __restrict__ idx, RowWs ws,
                                                                   int64_t ld) {
@@ -337,24 +407,32 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const int32_t*
     __syncthreads();
     select_candidates<false>(cand, cand_l, n_cand, m, hist, list, &s_cnt, s_misc);
   }
-  // bitonic sort of the k kept positions, ascending
+  // bitonic sort of the k kept positions, ascending (in registers when k > 1024)
   int P = 1;
   while (P < k) P <<= 1;
   for (int i = k + tid; i < P; i += kFinThreads) list[i] = 0x7fffffff;
   __syncthreads();
-  for (int size = 2; size <= P; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < P / 2; i += kFinThreads) {
-        const int lo = 2 * i - (i & (stride - 1));
-        const int hi = lo + stride;
-        const bool up = (lo & size) == 0;
-        const int32_t a = list[lo], b = list[hi];
-        if ((a > b) == up) {
-          list[lo] = b;
-          list[hi] = a;
+  if (P == 2048) {
+    sort_regs<8>(list);
+  } else if (P == 4096) {
+    sort_regs<16>(list);
+  } else if (P == 8192) {
+    sort_regs<32>(list);
+  } else {
+    for (int size = 2; size <= P; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int i = tid; i < P / 2; i += kFinThreads) {
+          const int lo = 2 * i - (i & (stride - 1));
+          const int hi = lo + stride;
+          const bool up = (lo & size) == 0;
+          const int32_t a = list[lo], b = list[hi];
+          if ((a > b) == up) {
+            list[lo] = b;
+            list[hi] = a;
+          }
         }
+        __syncthreads();
       }
-      __syncthreads();
     }
   }
   for (int i = tid; i < k; i += kFinThreads) dst[i] = list[i];

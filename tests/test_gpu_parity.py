@@ -131,7 +131,7 @@ def test_topk_small_k_and_k_ge_L(ld):
     _topk_case(s, [ld, ld - 1, ld // 2], 1)                          # k = 1
 
 
-@pytest.mark.parametrize("k", [1, 7, 64, 2048, 8192])
+@pytest.mark.parametrize("k", [1, 7, 64, 1500, 2048, 3000, 8192])
 @pytest.mark.parametrize("ld", [30000, 50000, 180000])
 def test_topk_various_k(k, ld):
     rng = np.random.default_rng(k)

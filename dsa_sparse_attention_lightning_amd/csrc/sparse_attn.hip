@@ -64,6 +64,10 @@ struct AttnArgs {
 };
 
 constexpr int kMaxTokPerSplit = 1024;
+#ifndef DSA_ATTN_STREAM_BYTES
+#define DSA_ATTN_STREAM_BYTES (256ll << 20)
+#endif
+constexpr long long kAttnStreamBytes = DSA_ATTN_STREAM_BYTES;   // last-level cache (MALL) size
 
 // ---------------------------------------------------------------------------
 // Per-head KV gather kernel
@@ -71,15 +75,25 @@ constexpr int kMaxTokPerSplit = 1024;
 // Loads of U tokens' K and V pieces.  Loads are unconditional (invalid
 // tokens and padding heads read row 0 / the last head, and are ignored by
 // consume) so that the compiler keeps all of them in flight at once.
-template <int D, int GQ, int U>
+// 16 bytes of a KV row; NT: non-temporal (a gather far larger than the
+// last-level cache, whose rows are not read again by this call)
+template <bool NT>
+__device__ __forceinline__ uint4 ld_row16(const uint16_t* p) {
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  const u32x4_t v = NT ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p))
+                       : *reinterpret_cast<const u32x4_t*>(p);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+template <int D, int GQ, int U, bool NT>
 __device__ __forceinline__ void issue_loads(const AttnArgs& a, const int64_t* s_off, int i, int ntok,
                                             size_t lane_off, uint4 (&kr)[U], uint4 (&vr)[U]) {
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int li = min(i + u * kWaves, ntok - 1);
     const int64_t off = max(s_off[li], (int64_t)0);
-    kr[u] = *reinterpret_cast<const uint4*>(a.kc + off + lane_off);
-    vr[u] = *reinterpret_cast<const uint4*>(a.vc + off + lane_off);
+    kr[u] = ld_row16<NT>(a.kc + off + lane_off);
+    vr[u] = ld_row16<NT>(a.vc + off + lane_off);
   }
 }
 
@@ -147,7 +161,7 @@ __device__ __forceinline__ void consume(const int64_t* s_off, int i, int ntok, f
   }
 }
 
-template <int D, int GQ, int U>
+template <int D, int GQ, int U, bool NT>
 __global__ __launch_bounds__(kThreads) void mha_attn_kernel(AttnArgs a) {
   constexpr int SLOT = D / 8;            // lanes per KV row
   constexpr int NSLOT = 64 / SLOT;       // KV heads per wave
@@ -222,13 +236,13 @@ __global__ __launch_bounds__(kThreads) void mha_attn_kernel(AttnArgs a) {
   constexpr int STEP = kWaves * U;
   uint4 kA[U], vA[U], kB[U], vB[U];
   int i = wave;
-  issue_loads<D, GQ, U>(a, s_off, i, ntok, lane_off, kA, vA);
+  issue_loads<D, GQ, U, NT>(a, s_off, i, ntok, lane_off, kA, vA);
   while (i < ntok) {
-    issue_loads<D, GQ, U>(a, s_off, i + STEP, ntok, lane_off, kB, vB);
+    issue_loads<D, GQ, U, NT>(a, s_off, i + STEP, ntok, lane_off, kB, vB);
     consume<D, GQ, U>(s_off, i, ntok, a.scale_log2, qv, m, l, acc, kA, vA);
     i += STEP;
     if (i >= ntok) break;
-    issue_loads<D, GQ, U>(a, s_off, i + STEP, ntok, lane_off, kA, vA);
+    issue_loads<D, GQ, U, NT>(a, s_off, i + STEP, ntok, lane_off, kA, vA);
     consume<D, GQ, U>(s_off, i, ntok, a.scale_log2, qv, m, l, acc, kB, vB);
     i += STEP;
   }
@@ -606,12 +620,19 @@ void launch_mha(AttnArgs a, const Plan& p, int B, hipStream_t s) {
     // XCDs, times S_q rows (see the kernel)
     const long long units = ((long long)B * p.nsplit * p.head_groups + 7) / 8 * 8;
     a.row_grouped = 1;
-    hipLaunchKernelGGL((mha_attn_kernel<D, GQ, DSA_ATTN_UNROLL>), dim3((unsigned)(units * a.S_q)), dim3(kThreads), 0,
-                       s, a);
+    hipLaunchKernelGGL((mha_attn_kernel<D, GQ, DSA_ATTN_UNROLL, false>), dim3((unsigned)(units * a.S_q)),
+                       dim3(kThreads), 0, s, a);
   } else {
     a.row_grouped = 0;
     dim3 grid(p.nsplit, p.head_groups, B * a.S_q);
-    hipLaunchKernelGGL((mha_attn_kernel<D, GQ, DSA_ATTN_UNROLL>), grid, dim3(kThreads), 0, s, a);
+    // one query row per sequence: a gather larger than the last-level cache
+    // streams (non-temporal loads); smaller ones stay cacheable, since the
+    // draft steps that share the index set re-read the same rows
+    const double bytes = (double)B * a.k * a.H_kv * D * 2 * 2;
+    if (bytes > (double)kAttnStreamBytes)
+      hipLaunchKernelGGL((mha_attn_kernel<D, GQ, DSA_ATTN_UNROLL, true>), grid, dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((mha_attn_kernel<D, GQ, DSA_ATTN_UNROLL, false>), grid, dim3(kThreads), 0, s, a);
   }
 }
 

@@ -299,8 +299,8 @@ constexpr int kCombineMaxSplits = 128;
 #ifndef DSA_LAT_MAX_SPLITS
 #define DSA_LAT_MAX_SPLITS 32
 #endif
-#ifndef DSA_LAT_MIN_TILES
-#define DSA_LAT_MIN_TILES 2
+#ifndef DSA_LAT_MIN_TOKENS
+#define DSA_LAT_MIN_TOKENS 64
 #endif
 constexpr int kLatentMaxSplits = DSA_LAT_MAX_SPLITS;
 
@@ -353,24 +353,27 @@ void launch_combine(const float* part_o, const float* part_ml, int rows, int nsp
 }
 
 // ---------------------------------------------------------------------------
-// Latent MQA kernel: one KV head of D_qk = 576 (K = whole row, V = its first
-// 512 dims) shared by NW*16 query heads.  Per 32-token tile:
-//   * the tile's rows go to LDS twice: row-major (K, B operand of QK^T) and
-//     transposed in the first 512 dims (V, B operand of PV), so every MFMA
-//     operand is one 16-byte LDS read;
-//   * wave w computes S = Q[16w..16w+15] K^T (18 K-steps x 2 N-blocks of
-//     v_mfma_f32_16x16x32_bf16), runs the online softmax for its 16 heads
-//     (16-lane DPP max/sum) and publishes P (bf16) and the rescale factors;
-//   * wave w then accumulates O[all heads][its 512/NW value dims] += P V.
+// Latent MQA kernel: one KV head of D_qk = 576 (K = the whole row, V = its
+// first 512 dims) shared by 64 query heads.  A workgroup owns one split of the
+// selected tokens and one group of 16 heads (the grid also runs over the four
+// head groups, so a split's partial is 16 x 512 floats, and 128 workgroups run
+// at k = 2048).  Per 64-token chunk, four waves:
+//   * wave w loads the K rows of tokens 16w..16w+15 straight into B fragments
+//     and computes S = Q K^T for them (18 K-steps of v_mfma_f32_16x16x32_bf16);
+//   * every thread loads V pieces (lane = token) and writes them transposed
+//     into LDS, so the PV operand is one 16-byte LDS read;
+//   * the chunk's softmax statistics are combined across the waves in LDS
+//     (online over chunks, exp2 domain), P goes to LDS as bf16;
+//   * wave w accumulates O[16 heads][dims 128w..128w+127] += P V.
 // Split-k partials (unnormalised O, m, l) go to the combine kernel as in the
 // per-head kernel.
 // ---------------------------------------------------------------------------
 constexpr int kLatD = 576;
 constexpr int kLatDv = 512;
-constexpr int kLatTile = 32;
-constexpr int kLatKRow = kLatD * 2 + 16;          // bytes per K row in LDS (padded)
-constexpr int kLatVRow = kLatTile * 2 + 16;       // bytes per transposed V row in LDS (padded)
-constexpr int kLatChunks = kLatD / 8;             // 16-byte chunks per row (72)
+constexpr int kLatChunk = 64;                     // tokens per chunk (4 waves x 16)
+constexpr int kLatHeads = 16;                     // heads per workgroup
+constexpr int kLatVRow = kLatChunk * 2 + 16;      // bytes per transposed V row in LDS (padded)
+constexpr int kLatPRow = kLatChunk + 8;           // bf16 per P row in LDS (padded)
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_max_step(float v) {
@@ -390,21 +393,19 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rn(float f) {
   return (uint16_t)(u >> 16);
 }
 
-template <int NW>
-__global__ __launch_bounds__(NW * 64) void latent_attn_kernel(AttnArgs a) {
-  constexpr int NT = NW * 64;
-  constexpr int H = NW * 16;
-  constexpr int DV_W = kLatDv / NW;               // value dims per wave
-  constexpr int NBV = DV_W / 16;                   // N-blocks of PV per wave
+__global__ __launch_bounds__(256) void latent_attn_kernel(AttnArgs a) {
+  constexpr int NT = 256;
   constexpr int KS = kLatD / 32;                   // 18 K-steps of QK
-  constexpr int PER_T = kLatTile * kLatChunks / NT;  // 16-byte chunks per thread per tile
+  constexpr int DV_W = kLatDv / 4;                 // value dims per wave
+  constexpr int NBV = DV_W / 16;                   // N-blocks of PV per wave
+  constexpr int VPT = kLatChunk * (kLatDv / 8) / NT;   // 16-byte V pieces per thread per chunk (16)
   __shared__ int64_t s_off[kMaxTokPerSplit];
-  __shared__ __align__(16) unsigned char s_k[kLatTile * kLatKRow];
   __shared__ __align__(16) unsigned char s_vt[kLatDv * kLatVRow];
-  __shared__ __align__(16) uint16_t s_p[H][kLatTile + 8];
-  __shared__ float s_corr[H], s_lfin[H];
+  __shared__ __align__(16) uint16_t s_p[kLatHeads][kLatPRow];
+  __shared__ float s_wmax[4][kLatHeads], s_wsum[4][kLatHeads];
 
   const int split = blockIdx.x;
+  const int hg = blockIdx.y;
   const int bs = blockIdx.z;
   const int b = bs / a.S_q;
   const int s = bs % a.S_q;
@@ -423,19 +424,17 @@ __global__ __launch_bounds__(NW * 64) void latent_attn_kernel(AttnArgs a) {
     // positions outside the block table (outside the contract) count as absent
     s_off[i] = (t >= 0 && t / a.page < a.max_pages) ? (int64_t)bt[t / a.page] * a.page_stride + (int64_t)(t % a.page) * a.row_stride : -1;
   }
-  // Q fragments of this wave's 16 heads: A operand, lane holds head 16w + l%16,
-  // dims ks*32 + (l/16)*8 .. +8
+  // Q fragments (A operand): lane holds head 16hg + l%16, dims ks*32 + (l/16)*8 .. +8
   bf16x8_t qa[KS];
   {
-    const uint16_t* qrow = a.q + ((size_t)bs * a.H_q + wave * 16 + r16) * kLatD + grp * 8;
+    const uint16_t* qrow = a.q + ((size_t)bs * a.H_q + hg * kLatHeads + r16) * kLatD + grp * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qa[ks] = *reinterpret_cast<const bf16x8_t*>(qrow + ks * 32);
   }
-  f32x4_t o[NW][NBV];
+  // accumulators: lane holds heads 4*grp + i, dims 128w + nb*16 + l%16
+  f32x4_t o[NBV];
 #pragma unroll
-  for (int mb = 0; mb < NW; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < NBV; ++nb) o[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int nb = 0; nb < NBV; ++nb) o[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run[4], l_run[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -444,105 +443,93 @@ __global__ __launch_bounds__(NW * 64) void latent_attn_kernel(AttnArgs a) {
   }
   __syncthreads();
 
-  const int ntiles = (ntok + kLatTile - 1) / kLatTile;
-  uint4 pre[PER_T];
-  auto fetch = [&](int tile) {
+  const int nchunks = (ntok + kLatChunk - 1) / kLatChunk;
+  for (int ch = 0; ch < nchunks; ++ch) {
+    const int c0 = ch * kLatChunk;
+    // V pieces: lane = token c0 + lane, dim chunk wave + 4j (tokens past ntok read row 0)
+    uint4 vp[VPT];
+    {
+      const int li = min(c0 + lane, ntok - 1);
+      const int64_t off = max(s_off[li], (int64_t)0);
 #pragma unroll
-    for (int j = 0; j < PER_T; ++j) {
-      const int c = tid + j * NT;
-      const int tt = min(tile * kLatTile + c % kLatTile, ntok - 1);
-      const int64_t off = max(s_off[tt], (int64_t)0);
-      pre[j] = *reinterpret_cast<const uint4*>(a.kc + off + (c / kLatTile) * 8);
+      for (int j = 0; j < VPT; ++j) vp[j] = *reinterpret_cast<const uint4*>(a.kc + off + (wave + 4 * j) * 8);
     }
-  };
-  fetch(0);
-  for (int tile = 0; tile < ntiles; ++tile) {
-    // stage the tile: K row-major, V transposed
+    // K fragments of this wave's 16 tokens (B operand): lane holds token
+    // c0 + 16w + l%16, dims ks*32 + (l/16)*8 .. +8
+    const int my_tok = c0 + wave * 16 + r16;
+    const bool valid = my_tok < ntok && s_off[min(my_tok, ntok - 1)] >= 0;
+    bf16x8_t kf[KS];
+    {
+      const int64_t off = max(s_off[min(my_tok, ntok - 1)], (int64_t)0);
 #pragma unroll
-    for (int j = 0; j < PER_T; ++j) {
-      const int c = tid + j * NT;
-      // piece c = token c % 32, chunk c / 32: the lanes of a wave hold 32
-      // consecutive tokens of two chunks, so the transposed 2-byte V stores
-      // of one instruction go to two rows, 32 consecutive columns each
-      // (conflict-free), and the 16-byte K stores to 32 rows 1168 bytes apart
-      const int tt = c % kLatTile;
-      const int ch = c / kLatTile;
-      *reinterpret_cast<uint4*>(s_k + tt * kLatKRow + ch * 16) = pre[j];
-      if (ch < kLatDv / 8) {
-        const uint32_t w4[4] = {pre[j].x, pre[j].y, pre[j].z, pre[j].w};
+      for (int ks = 0; ks < KS; ++ks) kf[ks] = *reinterpret_cast<const bf16x8_t*>(a.kc + off + ks * 32 + grp * 8);
+    }
+    // V transposed into LDS: one instruction writes 64 consecutive tokens of one dim
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint16_t v = (uint16_t)(e & 1 ? (w4[e >> 1] >> 16) : (w4[e >> 1] & 0xffffu));
-          *reinterpret_cast<uint16_t*>(s_vt + (ch * 8 + e) * kLatVRow + tt * 2) = v;
-        }
+    for (int j = 0; j < VPT; ++j) {
+      const int d0 = (wave + 4 * j) * 8;
+      const uint32_t w4[4] = {vp[j].x, vp[j].y, vp[j].z, vp[j].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint16_t v = (uint16_t)(e & 1 ? (w4[e >> 1] >> 16) : (w4[e >> 1] & 0xffffu));
+        *reinterpret_cast<uint16_t*>(s_vt + (d0 + e) * kLatVRow + lane * 2) = v;
       }
     }
-    __syncthreads();
-    if (tile + 1 < ntiles) fetch(tile + 1);   // next tile's loads overlap this tile's math
-
-    // S = Q K^T for this wave's heads: C layout, lane holds heads
-    // 16w + (l/16)*4 + i, token nb*16 + l%16
-    f32x4_t sacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+    // S for heads 4*grp + i, token 16w + l%16
+    f32x4_t sacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const bf16x8_t kb = *reinterpret_cast<const bf16x8_t*>(s_k + (nb * 16 + r16) * kLatKRow + ks * 64 + grp * 16);
-        sacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], kb, sacc[nb], 0, 0, 0);
-      }
-    }
-    // online softmax over the tile's tokens (exp2 domain)
-    bool valid[2];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const int li = tile * kLatTile + nb * 16 + r16;
-      valid[nb] = li < ntok && s_off[li] >= 0;
-    }
+    for (int ks = 0; ks < KS; ++ks) sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], kf[ks], sacc, 0, 0, 0);
+    float sv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float s0 = valid[0] ? sacc[0][i] * a.scale_log2 : -INFINITY;
-      const float s1 = valid[1] ? sacc[1][i] * a.scale_log2 : -INFINITY;
-      const float tmax = group_max16(fmaxf(s0, s1));
-      const float mn = fmaxf(m_run[i], tmax);
-      const float corr = mn == -INFINITY ? 1.f : fast_exp2(m_run[i] - mn);
-      const uint16_t p0 = f32_to_bf16_rn(mn == -INFINITY ? 0.f : fast_exp2(s0 - mn));
-      const uint16_t p1 = f32_to_bf16_rn(mn == -INFINITY ? 0.f : fast_exp2(s1 - mn));
-      // the row sum uses the bf16-rounded weights that PV multiplies
-      const float psum = group_sum_dpp<16>(__uint_as_float((uint32_t)p0 << 16) + __uint_as_float((uint32_t)p1 << 16));
-      l_run[i] = l_run[i] * corr + psum;
-      m_run[i] = mn;
-      const int h = wave * 16 + grp * 4 + i;
-      s_p[h][r16] = p0;
-      s_p[h][16 + r16] = p1;
-      if (r16 == 0) s_corr[h] = corr;
+      sv[i] = valid ? sacc[i] * a.scale_log2 : -INFINITY;
+      const float wm = group_max16(sv[i]);
+      if (r16 == 0) s_wmax[wave][grp * 4 + i] = wm;
     }
     __syncthreads();
-    // O[all heads][this wave's value dims] = O * corr + P V
+    // chunk statistics, the same in every wave (fixed wave order)
+    float corr[4];
 #pragma unroll
-    for (int mb = 0; mb < NW; ++mb) {
-      const bf16x8_t pa = *reinterpret_cast<const bf16x8_t*>(&s_p[mb * 16 + r16][grp * 8]);
-      float c4[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) c4[i] = s_corr[mb * 16 + grp * 4 + i];
-#pragma unroll
-      for (int nb = 0; nb < NBV; ++nb) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[mb][nb][i] *= c4[i];
-        const int dv = wave * DV_W + nb * 16 + r16;
-        const bf16x8_t vb = *reinterpret_cast<const bf16x8_t*>(s_vt + dv * kLatVRow + grp * 16);
-        o[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o[mb][nb], 0, 0, 0);
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int h = grp * 4 + i;
+      const float cm = fmaxf(fmaxf(s_wmax[0][h], s_wmax[1][h]), fmaxf(s_wmax[2][h], s_wmax[3][h]));
+      const float mn = fmaxf(m_run[i], cm);
+      corr[i] = mn == -INFINITY ? 1.f : fast_exp2(m_run[i] - mn);
+      const uint16_t pb = f32_to_bf16_rn(mn == -INFINITY ? 0.f : fast_exp2(sv[i] - mn));
+      // the row sum uses the bf16-rounded weights that PV multiplies
+      const float ws = group_sum_dpp<16>(__uint_as_float((uint32_t)pb << 16));
+      if (r16 == 0) s_wsum[wave][h] = ws;
+      s_p[h][wave * 16 + r16] = pb;
+      m_run[i] = mn;
     }
-    __syncthreads();   // the next tile overwrites s_k, s_vt, s_p
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = grp * 4 + i;
+      l_run[i] = l_run[i] * corr[i] + ((s_wsum[0][h] + s_wsum[1][h]) + (s_wsum[2][h] + s_wsum[3][h]));
+    }
+    // O[16 heads][this wave's dims] = O * corr + P V  (two 32-token K-steps)
+    bf16x8_t pa[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) pa[kk] = *reinterpret_cast<const bf16x8_t*>(&s_p[r16][kk * 32 + grp * 8]);
+#pragma unroll
+    for (int nb = 0; nb < NBV; ++nb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[nb][i] *= corr[i];
+      const unsigned char* vrow = s_vt + (wave * DV_W + nb * 16 + r16) * kLatVRow + grp * 16;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+        o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[kk], *reinterpret_cast<const bf16x8_t*>(vrow + kk * 64),
+                                                       o[nb], 0, 0, 0);
+    }
+    __syncthreads();   // the next chunk overwrites s_vt, s_p and the statistics
   }
 
-  // per-head statistics: owned by the wave that ran the head's softmax
+  // every wave holds the same statistics; wave 0 writes them
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int h = wave * 16 + grp * 4 + i;
-    const size_t row = (size_t)bs * a.H_q + h;
-    if (r16 == 0) {
-      s_lfin[h] = l_run[i];
+    const size_t row = (size_t)bs * a.H_q + hg * kLatHeads + grp * 4 + i;
+    if (wave == 0 && r16 == 0) {
       if (a.nsplit == 1) {
         if (a.lse) a.lse[row] = m_run[i] == -INFINITY ? -INFINITY : (m_run[i] + __log2f(l_run[i])) * kLn2;
       } else {
@@ -550,22 +537,14 @@ __global__ __launch_bounds__(NW * 64) void latent_attn_kernel(AttnArgs a) {
         a.part_ml[(row * a.nsplit + split) * 2 + 1] = l_run[i];
       }
     }
-  }
-  __syncthreads();
+    const float inv = l_run[i] > 0.f ? 1.f / l_run[i] : 0.f;
 #pragma unroll
-  for (int mb = 0; mb < NW; ++mb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = mb * 16 + grp * 4 + i;
-      const size_t row = (size_t)bs * a.H_q + h;
-      const float inv = s_lfin[h] > 0.f ? 1.f / s_lfin[h] : 0.f;
-#pragma unroll
-      for (int nb = 0; nb < NBV; ++nb) {
-        const int dv = wave * DV_W + nb * 16 + r16;
-        if (a.nsplit == 1) a.out[row * kLatDv + dv] = o[mb][nb][i] * inv;
-        else a.part_o[(row * a.nsplit + split) * kLatDv + dv] = o[mb][nb][i];
-      }
+    for (int nb = 0; nb < NBV; ++nb) {
+      const int dv = wave * DV_W + nb * 16 + r16;
+      if (a.nsplit == 1) a.out[row * kLatDv + dv] = o[nb][i] * inv;
+      else a.part_o[(row * a.nsplit + split) * kLatDv + dv] = o[nb][i];
     }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -589,9 +568,9 @@ Plan make_plan(int B, int S_q, int H_q, int H_kv, int D_qk, int D_v, int k) {
   Plan p{};
   const bool latent = is_latent(H_q, H_kv, D_qk, D_v);
   const int nslot = latent ? 1 : 64 / (D_qk / 8);
-  p.head_groups = latent ? 1 : (H_kv + nslot - 1) / nslot;
+  p.head_groups = latent ? H_q / kLatHeads : (H_kv + nslot - 1) / nslot;
   const long long base = (long long)B * S_q * p.head_groups;
-  const int min_tok = latent ? DSA_LAT_MIN_TILES * kLatTile : DSA_ATTN_MIN_TOKENS;
+  const int min_tok = latent ? DSA_LAT_MIN_TOKENS : DSA_ATTN_MIN_TOKENS;
   const int max_split = latent ? kLatentMaxSplits : kCombineMaxSplits;
   int ns = (int)((DSA_ATTN_TARGET_WGS + base - 1) / base);
   const int max_ns = (k + min_tok - 1) / min_tok;
@@ -708,8 +687,8 @@ extern "C" dsa_status dsa_sparse_attn(const void* q, const void* k_cache, const 
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (latent) {
-    dim3 grid(p.nsplit, 1, B * S_q);
-    hipLaunchKernelGGL(latent_attn_kernel<4>, grid, dim3(256), 0, s, a);
+    dim3 grid(p.nsplit, p.head_groups, B * S_q);
+    hipLaunchKernelGGL(latent_attn_kernel, grid, dim3(256), 0, s, a);
     dsa_status st = launch_status("dsa_sparse_attn(latent)");
     if (st != DSA_OK || p.nsplit == 1) return st;
     launch_combine<kLatDv>(a.part_o, a.part_ml, B * S_q * H_q, p.nsplit, out, lse, s);

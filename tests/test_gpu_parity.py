@@ -521,6 +521,8 @@ def test_draft_block_graph_replays():
     dict(lens=[3000, 1500], k=2048, shuffle=True),      # split-k, ragged, one row with -1 padding
     dict(lens=[200], k=64, shuffle=False),              # single split, k < L
     dict(lens=[100], k=128, shuffle=False),             # k > L: padding inside the split
+    dict(lens=[1500], k=1000, shuffle=True),            # splits of 63 tokens (a partial chunk)
+    dict(lens=[9000], k=8192, shuffle=True),            # several 64-token chunks per split
 ])
 def test_latent_attn_matches_oracle(case):
     log("latent", case)

@@ -304,12 +304,12 @@ constexpr int kCombineMaxSplits = 128;
 #endif
 constexpr int kLatentMaxSplits = DSA_LAT_MAX_SPLITS;
 
-template <int D, int MAXSPLIT>
-__global__ __launch_bounds__(D) void combine_kernel(const float* __restrict__ part_o,
-                                                    const float* __restrict__ part_ml, int nsplit,
-                                                    float* __restrict__ out, float* __restrict__ lse) {
+template <int D, int DW, int MAXSPLIT>
+__global__ __launch_bounds__(DW) void combine_kernel(const float* __restrict__ part_o,
+                                                     const float* __restrict__ part_ml, int nsplit,
+                                                     float* __restrict__ out, float* __restrict__ lse) {
   const int row = blockIdx.x;
-  const int d = threadIdx.x;
+  const int d = blockIdx.y * DW + threadIdx.x;
   const float* ml = part_ml + (size_t)row * nsplit * 2;
   const float* po = part_o + (size_t)row * nsplit * D + d;
   float ov[MAXSPLIT], mv[MAXSPLIT], lv[MAXSPLIT];
@@ -339,17 +339,20 @@ __global__ __launch_bounds__(D) void combine_kernel(const float* __restrict__ pa
   if (d == 0 && lse) lse[row] = M == -INFINITY ? -INFINITY : (M + __log2f(Lsum)) * kLn2;
 }
 
-template <int D>
+// D output dims per row, DW of them per workgroup (rows x D/DW workgroups:
+// the 512-dim latent rows spread over four times as many CUs)
+template <int D, int DW = (D < 128 ? D : 128)>
 void launch_combine(const float* part_o, const float* part_ml, int rows, int nsplit, float* out, float* lse,
                     hipStream_t s) {
+  const dim3 grid(rows, D / DW);
   if (nsplit <= 16)
-    hipLaunchKernelGGL((combine_kernel<D, 16>), dim3(rows), dim3(D), 0, s, part_o, part_ml, nsplit, out, lse);
+    hipLaunchKernelGGL((combine_kernel<D, DW, 16>), grid, dim3(DW), 0, s, part_o, part_ml, nsplit, out, lse);
   else if (nsplit <= 32)
-    hipLaunchKernelGGL((combine_kernel<D, 32>), dim3(rows), dim3(D), 0, s, part_o, part_ml, nsplit, out, lse);
+    hipLaunchKernelGGL((combine_kernel<D, DW, 32>), grid, dim3(DW), 0, s, part_o, part_ml, nsplit, out, lse);
   else if (nsplit <= 64)
-    hipLaunchKernelGGL((combine_kernel<D, 64>), dim3(rows), dim3(D), 0, s, part_o, part_ml, nsplit, out, lse);
+    hipLaunchKernelGGL((combine_kernel<D, DW, 64>), grid, dim3(DW), 0, s, part_o, part_ml, nsplit, out, lse);
   else
-    hipLaunchKernelGGL((combine_kernel<D, 128>), dim3(rows), dim3(D), 0, s, part_o, part_ml, nsplit, out, lse);
+    hipLaunchKernelGGL((combine_kernel<D, DW, 128>), grid, dim3(DW), 0, s, part_o, part_ml, nsplit, out, lse);
 }
 
 // ---------------------------------------------------------------------------

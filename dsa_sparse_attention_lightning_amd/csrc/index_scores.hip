@@ -27,7 +27,7 @@ constexpr int kThreads = 256;      // 4 waves
 
 // TILES 16-position MFMA N tiles per wave step; a workgroup step covers
 // 4 * 16 * TILES positions.
-template <int KS, int MB, int TILES>
+template <int KS, int MB, int TILES, bool ROWT>
 __global__ __launch_bounds__(kThreads) void index_scores_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ w,
     const uint16_t* __restrict__ kidx, const int32_t* __restrict__ block_table,
@@ -57,6 +57,17 @@ __global__ __launch_bounds__(kThreads) void index_scores_kernel(
   const int n = lane & 15;
   const int g = lane >> 4;
   const int32_t* bt = block_table + (size_t)b * max_pages;
+  // ROWT (several steps per workgroup): the physical key row of every chunk
+  // position is resolved once, so later steps' key loads wait on an LDS read
+  // instead of a dependent global load
+  int* s_row = reinterpret_cast<int*>(wl + R * MB * 16);
+  if constexpr (ROWT) {
+    for (int i = tid; i < t_end - t_begin; i += kThreads) {
+      const int t = t_begin + i;
+      s_row[i] = bt[t / page] * page + t % page;
+    }
+    __syncthreads();
+  }
 
   for (int it = 0; it < n_iter; ++it) {
     const int base = t_begin + it * kBlockPos + wave * kWavePos;
@@ -68,8 +79,8 @@ __global__ __launch_bounds__(kThreads) void index_scores_kernel(
 #pragma unroll
     for (int tile = 0; tile < TILES; ++tile) {
       const int t = min(base + tile * 16 + n, t_end - 1);
-      const int phys = bt[t / page];
-      const uint16_t* src = kidx + ((size_t)phys * page + (t % page)) * D + g * 8;
+      const size_t prow = ROWT ? (size_t)s_row[t - t_begin] : (size_t)bt[t / page] * page + (t % page);
+      const uint16_t* src = kidx + prow * D + g * 8;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) bf[tile][ks] = *reinterpret_cast<const bf16x8_t*>(src + ks * 32);
     }
@@ -151,8 +162,15 @@ dsa_status launch_index_t(const void* q, const float* w, const void* kidx, const
                           const int32_t* row_len, float* scores, int B, int R, int H, int page,
                           int max_pages, int64_t ld, hipStream_t stream) {
   constexpr int kBlockPos = kThreads / 64 * 16 * TILES;
-  const size_t lds = (size_t)R * MB * KS * 64 * 16 + (size_t)R * MB * 16 * sizeof(float);
-  auto kern = index_scores_kernel<KS, MB, TILES>;
+  // Positions per workgroup: whole steps, sized so that a long row still
+  // spreads over about 2048 workgroups.
+  const int64_t steps = (ld + kBlockPos - 1) / kBlockPos;
+  int per = (int)((steps * B + 2047) / 2048);
+  per = per < 1 ? 1 : per > 8 ? 8 : per;
+  const bool rowt = per > 1;
+  const size_t lds = (size_t)R * MB * KS * 64 * 16 + (size_t)R * MB * 16 * sizeof(float) +
+                     (rowt ? (size_t)per * kBlockPos * sizeof(int) : 0);
+  auto kern = rowt ? index_scores_kernel<KS, MB, TILES, true> : index_scores_kernel<KS, MB, TILES, false>;
   if (lds > 65536) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) {
@@ -160,11 +178,6 @@ dsa_status launch_index_t(const void* q, const float* w, const void* kidx, const
       return DSA_ERR_UNSUPPORTED;
     }
   }
-  // Positions per workgroup: whole steps, sized so that a long row still
-  // spreads over about 2048 workgroups.
-  const int64_t steps = (ld + kBlockPos - 1) / kBlockPos;
-  int per = (int)((steps * B + 2047) / 2048);
-  per = per < 1 ? 1 : per > 8 ? 8 : per;
   const int chunk = per * kBlockPos;
   const int64_t gx = (ld + chunk - 1) / chunk;
   dim3 grid((unsigned)gx, (unsigned)B);

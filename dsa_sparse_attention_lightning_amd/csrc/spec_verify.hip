@@ -19,9 +19,10 @@
 //           drafts in parallel lanes (first rejection by ballot).
 //   mass    grid (chunk, sequence): the residual (or bonus) weights of one
 //           chunk of the sampled row: per-256-logit tile masses from a wave
-//           inclusive scan, added in tile order.
+//           inclusive scan (kept in the workspace), added in tile order.
 //   pick    one workgroup per sequence draws by inverse CDF: the chunk that
-//           holds u * W, the tile inside it, then the token inside the tile.
+//           holds u * W, the tile inside it (from the stored tile masses),
+//           then the token inside the tile.
 // Uniforms come from the caller or from Philox4x64-10 (Salmon, Moraes, Dror,
 // Shaw, SC'11) evaluated in-kernel at counter (offset, b, j, stream).
 #include "dsa_common.h"
@@ -240,7 +241,9 @@ struct VerifyWs {
   float2* part;      // [B][2G+1][nchunks]
   Decision* dec;     // [B]
   float* cmass;      // [B][nmass]
+  float* tmass;      // [B][ntiles]: tile masses of the sampled row
   int nmass;
+  int ntiles;
   int chunk_tiles;   // 256-logit tiles per mass chunk
 };
 
@@ -336,11 +339,13 @@ __device__ __forceinline__ RowWeights sampled_row(const VerifyArgs& a, int b, in
 }
 
 // Tile masses (wave inclusive-scan totals) of tiles [t0, t1) of a row into
-// s_tile[0 .. t1-t0).  Tiles go round-robin to the waves; each wave issues
-// the loads of up to TPW tiles before weighting any of them.  The weights
-// and sums are the same for every TPW and NT.
+// s_tile[0 .. t1-t0), and into g_tile[0 .. t1-t0) when it is given.  Tiles go
+// round-robin to the waves; each wave issues the loads of up to TPW tiles
+// before weighting any of them.  The weights and sums are the same for every
+// TPW and NT.
 template <int TPW, bool NT>
-__device__ void tile_masses(const RowWeights& rw, int V, bool vec, int t0, int t1, float* s_tile) {
+__device__ void tile_masses(const RowWeights& rw, int V, bool vec, int t0, int t1, float* s_tile,
+                            float* g_tile = nullptr) {
   constexpr int kTilesPerWave = TPW;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -365,7 +370,10 @@ __device__ void tile_masses(const RowWeights& rw, int V, bool vec, int t0, int t
       float wv[4];
       weights4(rw, tv[i], dv[i], t * kTile + lane * 4, V, wv);
       const float incl = wave_incl_scan(((wv[0] + wv[1]) + wv[2]) + wv[3]);
-      if (lane == 63) s_tile[t - t0] = incl;
+      if (lane == 63) {
+        s_tile[t - t0] = incl;
+        if (g_tile) g_tile[t - t0] = incl;
+      }
     }
   }
 }
@@ -474,7 +482,7 @@ __global__ __launch_bounds__(kMassThreads) void verify_mass_kernel(VerifyArgs a,
   const int t0 = c * CT;
   const int t1 = min(t0 + CT, ntiles);
   constexpr int kTpw = CT / (kMassThreads / 64);
-  tile_masses<kTpw, NT>(rw, a.V, a.vec, t0, t1, s_tile);
+  tile_masses<kTpw, NT>(rw, a.V, a.vec, t0, t1, s_tile, ws.tmass + (size_t)b * ws.ntiles + t0);
   __syncthreads();
   if (threadIdx.x == 0) {
     float m = 0.f;
@@ -534,7 +542,13 @@ __global__ __launch_bounds__(kPickThreads) void verify_pick_kernel(VerifyArgs a,
   }
   float x = s_x;
   __syncthreads();
-  tile_masses<4, NT>(rw, V, a.vec, t0, t1, s_tile);
+  if (full_row) {
+    tile_masses<4, NT>(rw, V, a.vec, t0, t1, s_tile);
+  } else {
+    // the mass kernel stored these tile masses (the same bits a rescan gives)
+    const float* tm = ws.tmass + (size_t)b * ws.ntiles;
+    for (int t = t0 + tid; t < t1; t += kPickThreads) s_tile[t - t0] = tm[t];
+  }
   __syncthreads();
   if (tid < 64) {
     if (full_row) {
@@ -604,6 +618,12 @@ __global__ __launch_bounds__(kPickThreads) void verify_pick_kernel(VerifyArgs a,
   if (tid == 0) a.acc_len[b] = jstar;
 }
 
+template <int CT, bool DECIDE>
+void launch_mass(bool nt, dim3 grid, hipStream_t s, const VerifyArgs& a, const VerifyWs& ws) {
+  if (nt) hipLaunchKernelGGL((verify_mass_kernel<CT, true, DECIDE>), grid, dim3(kMassThreads), 0, s, a, ws);
+  else hipLaunchKernelGGL((verify_mass_kernel<CT, false, DECIDE>), grid, dim3(kMassThreads), 0, s, a, ws);
+}
+
 // Logits per stats workgroup: whole rows when the rows alone give about
 // kStatTargetWgs workgroups, else rows split into chunks of whole load
 // rounds so that about that many run.
@@ -632,14 +652,18 @@ size_t verify_ws(int B, int G, int V, int* nchunks, VerifyWs* out, char* base) {
   const size_t part = align_up((size_t)B * (2 * G + 1) * nc * sizeof(float2), 256);
   const size_t dec = align_up((size_t)B * sizeof(Decision), 256);
   const size_t cm = align_up((size_t)B * nm * sizeof(float), 256);
+  const int nt = (V + kTile - 1) / kTile;
+  const size_t tm = align_up((size_t)B * nt * sizeof(float), 256);
   if (out) {
     out->part = reinterpret_cast<float2*>(base);
     out->dec = reinterpret_cast<Decision*>(base + part);
     out->cmass = reinterpret_cast<float*>(base + part + dec);
+    out->tmass = reinterpret_cast<float*>(base + part + dec + cm);
     out->nmass = nm;
+    out->ntiles = nt;
     out->chunk_tiles = ct;
   }
-  return part + dec + cm;
+  return part + dec + cm + tm;
 }
 
 // ---------------------------------------------------------------------------
@@ -814,20 +838,20 @@ extern "C" dsa_status spec_verify(const float* target_logits, const float* draft
 #ifndef DSA_VERIFY_FUSE_MAX_B
 #define DSA_VERIFY_FUSE_MAX_B 8
 #endif
-  if (B <= DSA_VERIFY_FUSE_MAX_B && !nt && ws.chunk_tiles == kSmallChunkTiles) {
-    // decision inside the mass kernel: three launches
-    hipLaunchKernelGGL((verify_mass_kernel<kSmallChunkTiles, false, true>), gm, dim3(kMassThreads), 0, s, a, ws);
-  } else {
+  // up to DSA_VERIFY_FUSE_MAX_B sequences the decision runs inside the mass
+  // kernel (three launches); beyond, in a kernel of its own
+  const bool fuse = B <= DSA_VERIFY_FUSE_MAX_B;
+  if (!fuse) {
     hipLaunchKernelGGL(verify_decide_kernel, dim3(B), dim3(kDecideThreads), 0, s, a, ws);
     st = launch_status("spec_verify(decide)");
     if (st != DSA_OK) return st;
-    if (ws.chunk_tiles == kBigChunkTiles) {
-      if (nt) hipLaunchKernelGGL((verify_mass_kernel<kBigChunkTiles, true, false>), gm, dim3(kMassThreads), 0, s, a, ws);
-      else hipLaunchKernelGGL((verify_mass_kernel<kBigChunkTiles, false, false>), gm, dim3(kMassThreads), 0, s, a, ws);
-    } else {
-      if (nt) hipLaunchKernelGGL((verify_mass_kernel<kSmallChunkTiles, true, false>), gm, dim3(kMassThreads), 0, s, a, ws);
-      else hipLaunchKernelGGL((verify_mass_kernel<kSmallChunkTiles, false, false>), gm, dim3(kMassThreads), 0, s, a, ws);
-    }
+  }
+  if (ws.chunk_tiles == kBigChunkTiles) {
+    if (fuse) launch_mass<kBigChunkTiles, true>(nt, gm, s, a, ws);
+    else launch_mass<kBigChunkTiles, false>(nt, gm, s, a, ws);
+  } else {
+    if (fuse) launch_mass<kSmallChunkTiles, true>(nt, gm, s, a, ws);
+    else launch_mass<kSmallChunkTiles, false>(nt, gm, s, a, ws);
   }
   st = launch_status("spec_verify(mass)");
   if (st != DSA_OK) return st;

@@ -451,7 +451,10 @@ constexpr int kOneWaves = kOneThreads / 64;
 constexpr int kOneLdsKeys = 35840;       // 140 KiB of keys
 constexpr int kOneMaxLd = kOneLdsKeys;
 
-constexpr int kOneCand = kBins / 2;    // threshold-bin candidates resolved in LDS (reuses hist)
+constexpr int kOneCand = kBins / 4;    // threshold-bin candidates resolved in LDS (first half of hist)
+constexpr int kOneWords = (kOneLdsKeys + 63) / 64;   // kept-position bitmap (second half of hist)
+static_assert(kOneCand * 8 + kOneWords * 8 <= kBins * 4, "candidates and bitmap share the histogram");
+static_assert(kOneWords <= kOneThreads, "one bitmap word per thread");
 
 struct OneShared {
   uint32_t hist[kBins];
@@ -517,18 +520,29 @@ __global__ __launch_bounds__(kOneThreads) void topk_one_kernel(const float* __re
   // spreads over the range the scores actually occupy (indexer scores sit in
   // a few octaves; a fixed top-bits digit would put most of the row into a
   // handful of bins).
+  // 16-byte loads (4 positions per lane) over the quads inside [0, L): a
+  // wave's dword loads are address-rate bound at a quarter of this width.
+  // The last L % 4 positions (or a row not 16-byte aligned) go one by one.
   uint32_t kmin = 0xffffffffu, kmax = 0u;
-  for (int t0 = tid; t0 < L; t0 += kU * kOneThreads) {
-    float v[kU];
+  const int L4 = (reinterpret_cast<uintptr_t>(s) & 15u) == 0 ? (L & ~3) : 0;
+  for (int q0 = tid * 4; q0 < L4; q0 += kU * kOneThreads * 4) {
+    float4 v[kU];
 #pragma unroll
-    for (int u = 0; u < kU; ++u) v[u] = s[min(t0 + u * kOneThreads, L - 1)];
+    for (int u = 0; u < kU; ++u) v[u] = *reinterpret_cast<const float4*>(s + min(q0 + u * kOneThreads * 4, L4 - 4));
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const uint32_t key = order_key(v[u]);   // clamped duplicates do not change min/max
-      kmin = min(kmin, key);
-      kmax = max(kmax, key);
-      if (t0 + u * kOneThreads < L) keys[t0 + u * kOneThreads] = key;
+      const uint4 kq = make_uint4(order_key(v[u].x), order_key(v[u].y), order_key(v[u].z), order_key(v[u].w));
+      kmin = min(kmin, min(min(kq.x, kq.y), min(kq.z, kq.w)));   // clamped duplicates do not change min/max
+      kmax = max(kmax, max(max(kq.x, kq.y), max(kq.z, kq.w)));
+      const int q = q0 + u * kOneThreads * 4;
+      if (q < L4) *reinterpret_cast<uint4*>(keys + q) = kq;
     }
+  }
+  for (int t = L4 + tid; t < L; t += kOneThreads) {
+    const uint32_t key = order_key(s[t]);
+    kmin = min(kmin, key);
+    kmax = max(kmax, key);
+    keys[t] = key;
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
@@ -585,43 +599,70 @@ __global__ __launch_bounds__(kOneThreads) void topk_one_kernel(const float* __re
     }
   }
 
+  // The kept positions are staged in LDS behind the keys when both fit, then
+  // stored 16 bytes per lane (in place, scattered dword stores would be
+  // address-rate bound); otherwise they are stored directly.
+  uint32_t* obuf = keys + align_up(L, 4);
+  const bool staged = align_up(L, 4) + align_up(k, 4) <= kOneLdsKeys;
+  auto put = [&](uint32_t slot, int t) {
+    if (slot >= (uint32_t)k) return;   // exactly k are kept; never write past the row
+    if (staged) obuf[slot] = (uint32_t)t;
+    else dst[slot] = t;
+  };
+  auto flush = [&]() {
+    if (!staged) return;
+    __syncthreads();
+    if ((reinterpret_cast<uintptr_t>(dst) & 15u) == 0) {
+      const int k4 = k & ~3;
+      for (int i = tid * 4; i < k4; i += kOneThreads * 4)
+        *reinterpret_cast<uint4*>(dst + i) = *reinterpret_cast<const uint4*>(obuf + i);
+      for (int i = k4 + tid; i < k; i += kOneThreads) dst[i] = (int32_t)obuf[i];
+    } else {
+      for (int i = tid; i < k; i += kOneThreads) dst[i] = (int32_t)obuf[i];
+    }
+  };
+
   if (fast) {
-    // Wave w owns positions [p0, p1), 4 consecutive positions per lane.
-    // Pass 1 counts the wave's positions above the threshold bin and
-    // collects the bin's candidates (key, position); one thread per
-    // candidate ranks it by (key desc, position asc) to find the exact
-    // threshold pair; pass 2 writes the kept positions in order.
-    const int span4 = ((L + kOneWaves - 1) / kOneWaves + 255) / 256 * 256;
-    const int p0 = min(wave * span4, L), p1 = min(p0 + span4, L);
+    // One pass writes a bitmap of the kept positions: bit t of word t / 64
+    // is set where the key's resolved prefix lies above the threshold bin
+    // (one ballot per 64 consecutive positions), and the bin's candidates
+    // (key, position) are collected.  One thread per candidate ranks it by
+    // (key desc, position asc); the first `need` set their bits.  Then
+    // thread w emits the set bits of word w in ascending order at the
+    // exclusive prefix of the words' popcounts.
     const uint32_t P = prefix >> shift;
     uint2* cand = reinterpret_cast<uint2*>(sh.hist);
+    uint64_t* bits = reinterpret_cast<uint64_t*>(sh.hist + 2 * kOneCand);
+    const int nwords = (L + 63) / 64;
     if (tid == 0) sh.ncand = 0;
     __syncthreads();
-    auto keys4 = [&](int t, uint32_t (&kk)[4]) {
-      // t % 4 == 0; lanes past the range read the array's last quad (masked by the caller)
-      const uint4 v = *reinterpret_cast<const uint4*>(keys + min(t, kOneLdsKeys - 4));
-      kk[0] = v.x; kk[1] = v.y; kk[2] = v.z; kk[3] = v.w;
-    };
-    uint32_t gt_lane = 0;
-    for (int tb = p0; tb < p1; tb += 256) {
-      const int t = tb + lane * 4;
-      uint32_t kk[4];
-      keys4(t, kk);
+    // wave-uniform loop; the key reads of 8 words are issued together
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    constexpr int kWB = 8;
+    for (int w0 = wv; w0 < nwords; w0 += kWB * kOneWaves) {
+      uint32_t kk[kWB];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool valid = t + i < p1;
-        const uint32_t kp = kk[i] >> shift;
-        gt_lane += (valid && kp > P) ? 1u : 0u;
-        if (valid && kp == P) {
-          const uint32_t slot = atomicAdd(&sh.ncand, 1u);
-          if (slot < (uint32_t)kOneCand) cand[slot] = make_uint2(kk[i], (uint32_t)(t + i));
+      for (int u = 0; u < kWB; ++u) kk[u] = keys[min((w0 + u * kOneWaves) * 64 + lane, L - 1)];
+#pragma unroll
+      for (int u = 0; u < kWB; ++u) {
+        const int wd = w0 + u * kOneWaves;
+        if (wd >= nwords) break;
+        const int t = wd * 64 + lane;
+        const bool valid = t < L;
+        const uint32_t kp = kk[u] >> shift;
+        const uint64_t gt = __ballot(valid && kp > P);
+        const uint64_t eq = __ballot(valid && kp == P);
+        if (lane == 0) bits[wd] = gt;
+        if (eq) {   // wave-uniform: one slot reservation per wave
+          uint32_t base = 0;
+          if (lane == 0) base = atomicAdd(&sh.ncand, (uint32_t)__popcll(eq));
+          base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+          if (valid && kp == P) {
+            const uint32_t slot = base + mask_rank(eq);
+            if (slot < (uint32_t)kOneCand) cand[slot] = make_uint2(kk[u], (uint32_t)t);
+          }
         }
       }
-    }
-    const uint32_t gt_w = wave_sum_u32(gt_lane);
-    if (lane == 0) {
-      sh.wave_gt[wave] = gt_w;
-      sh.wave_eq[wave] = 0;
     }
     __syncthreads();
     const int n = (int)min(sh.ncand, (uint32_t)kOneCand);
@@ -640,36 +681,19 @@ __global__ __launch_bounds__(kOneThreads) void topk_one_kernel(const float* __re
         const uint2 e = cand[j];
         rank += (e.x > c.x || (e.x == c.x && e.y < c.y)) ? 1u : 0u;
       }
-      if (rank == need - 1) {
-        sh.kthr = c.x;
-        sh.pthr = (int)c.y;
-      }
-      if (rank < need) atomicAdd(&sh.wave_eq[c.y / span4], 1u);
+      if (rank < need) atomicOr(reinterpret_cast<unsigned long long*>(&bits[c.y >> 6]), 1ull << (c.y & 63));
     }
     __syncthreads();
-    const uint32_t kthr = sh.kthr;
-    const int pthr = sh.pthr;
-    uint32_t out_pos = 0;
+    const uint64_t wb = tid < nwords ? bits[tid] : 0ull;
+    const uint32_t c = (uint32_t)__popcll(wb);
+    const uint32_t inc = wave_incl_scan_dpp(c);
+    if (lane == 63) sh.wave_tot[wave] = inc;
+    __syncthreads();
+    uint32_t slot = inc - c;
 #pragma unroll
-    for (int w = 0; w < kOneWaves; ++w) out_pos += w < wave ? sh.wave_gt[w] + sh.wave_eq[w] : 0u;
-    for (int tb = p0; tb < p1; tb += 256) {
-      const int t = tb + lane * 4;
-      uint32_t kk[4];
-      keys4(t, kk);
-      bool take[4];
-      uint32_t c = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        take[i] = t + i < p1 && (kk[i] > kthr || (kk[i] == kthr && t + i <= pthr));
-        c += take[i] ? 1u : 0u;
-      }
-      const uint32_t incl = wave_incl_scan_dpp(c);
-      uint32_t slot = out_pos + incl - c;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (take[i]) dst[slot++] = t + i;
-      out_pos += (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
-    }
+    for (int w = 0; w < kOneWaves; ++w) slot += w < wave ? sh.wave_tot[w] : 0u;
+    for (uint64_t m = wb; m; m &= m - 1) put(slot++, tid * 64 + __ffsll((long long)m) - 1);
+    flush();
     return;
   }
 
@@ -716,12 +740,13 @@ __global__ __launch_bounds__(kOneThreads) void topk_one_kernel(const float* __re
       const uint64_t eqm = __ballot(eq);
       const bool take = gt || (eq && eq_seen + mask_rank(eqm) < need);
       const uint64_t tm = __ballot(take);
-      if (take) dst[out_pos + mask_rank(tm)] = t;
+      if (take) put(out_pos + mask_rank(tm), t);
       out_pos += __popcll(tm);
       eq_seen += __popcll(eqm);
     }
   }
   // no padding needed: L > k means exactly k positions were written
+  flush();
 }
 
 size_t one_lds_bytes() { return align_up(sizeof(OneShared), 16) + (size_t)kOneLdsKeys * 4; }

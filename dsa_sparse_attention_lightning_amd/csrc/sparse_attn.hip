@@ -290,9 +290,9 @@ __global__ __launch_bounds__(kThreads) void mha_attn_kernel(AttnArgs a) {
   }
 }
 
-// Folds split partials in split order: one workgroup of D threads per
-// (b, s, h) row, one output dim per thread.  The split statistics (m, l) are
-// the same for every thread of the row (scalar loads); each thread issues the
+// Folds split partials in split order: one workgroup per (b, s, h) row and
+// DW output dims.  The split statistics (m, l) are the
+// same for every thread of the row (scalar loads); each thread issues the
 // loads of all its split partials at once, so the fold is one memory round
 // trip with no barrier.
 constexpr int kCombineMaxSplits = 128;
@@ -304,19 +304,46 @@ constexpr int kCombineMaxSplits = 128;
 #endif
 constexpr int kLatentMaxSplits = DSA_LAT_MAX_SPLITS;
 
-template <int D, int DW, int MAXSPLIT>
-__global__ __launch_bounds__(DW) void combine_kernel(const float* __restrict__ part_o,
-                                                     const float* __restrict__ part_ml, int nsplit,
-                                                     float* __restrict__ out, float* __restrict__ lse) {
+template <int N>
+struct FVec;
+template <>
+struct FVec<1> {
+  typedef float T;
+  static __device__ __forceinline__ T zero() { return 0.f; }
+};
+template <>
+struct FVec<4> {
+  typedef float4 T;
+  static __device__ __forceinline__ T zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
+};
+__device__ __forceinline__ void fma_into(float& o, float c, float v) { o += c * v; }
+__device__ __forceinline__ void fma_into(float4& o, float c, const float4& v) {
+  o.x += c * v.x;
+  o.y += c * v.y;
+  o.z += c * v.z;
+  o.w += c * v.w;
+}
+__device__ __forceinline__ float div_by(float o, float l) { return o / l; }
+__device__ __forceinline__ float4 div_by(const float4& o, float l) {
+  return make_float4(o.x / l, o.y / l, o.z / l, o.w / l);
+}
+
+// DW output dims per workgroup, VEC of them per thread
+template <int D, int DW, int VEC, int MAXSPLIT>
+__global__ __launch_bounds__(DW / VEC) void combine_kernel(const float* __restrict__ part_o,
+                                                           const float* __restrict__ part_ml, int nsplit,
+                                                           float* __restrict__ out, float* __restrict__ lse) {
+  typedef typename FVec<VEC>::T vec_t;
   const int row = blockIdx.x;
-  const int d = blockIdx.y * DW + threadIdx.x;
+  const int d = blockIdx.y * DW + threadIdx.x * VEC;
   const float* ml = part_ml + (size_t)row * nsplit * 2;
   const float* po = part_o + (size_t)row * nsplit * D + d;
-  float ov[MAXSPLIT], mv[MAXSPLIT], lv[MAXSPLIT];
+  vec_t ov[MAXSPLIT];
+  float mv[MAXSPLIT], lv[MAXSPLIT];
 #pragma unroll
   for (int sp = 0; sp < MAXSPLIT; ++sp) {
     const int c = min(sp, nsplit - 1);
-    ov[sp] = po[(size_t)c * D];
+    ov[sp] = *reinterpret_cast<const vec_t*>(po + (size_t)c * D);
     mv[sp] = ml[2 * c];
     lv[sp] = ml[2 * c + 1];
   }
@@ -324,35 +351,39 @@ __global__ __launch_bounds__(DW) void combine_kernel(const float* __restrict__ p
 #pragma unroll
   for (int sp = 0; sp < MAXSPLIT; ++sp)
     if (sp < nsplit) M = fmaxf(M, mv[sp]);
-  float O = 0.f, Lsum = 0.f;
+  vec_t O = FVec<VEC>::zero();
+  float Lsum = 0.f;
   if (M != -INFINITY) {
 #pragma unroll
     for (int sp = 0; sp < MAXSPLIT; ++sp) {
       if (sp < nsplit) {
         const float c = fast_exp2(mv[sp] - M);
-        O += c * ov[sp];
+        fma_into(O, c, ov[sp]);
         Lsum += c * lv[sp];
       }
     }
   }
-  out[(size_t)row * D + d] = M == -INFINITY ? 0.f : O / Lsum;
+  *reinterpret_cast<vec_t*>(out + (size_t)row * D + d) = M == -INFINITY ? FVec<VEC>::zero() : div_by(O, Lsum);
   if (d == 0 && lse) lse[row] = M == -INFINITY ? -INFINITY : (M + __log2f(Lsum)) * kLn2;
 }
 
-// D output dims per row, DW of them per workgroup (rows x D/DW workgroups:
-// the 512-dim latent rows spread over four times as many CUs)
-template <int D, int DW = (D < 128 ? D : 128)>
+// D output dims per row, DW of them per workgroup (rows x D/DW workgroups),
+// VEC per thread: 16-byte accesses for the 64/128-dim rows; the 512-dim
+// latent rows keep one dim per thread, spread over four workgroups per row
+template <int D, int DW = (D < 128 ? D : 128), int VEC = (D <= 128 ? 4 : 1)>
 void launch_combine(const float* part_o, const float* part_ml, int rows, int nsplit, float* out, float* lse,
                     hipStream_t s) {
-  const dim3 grid(rows, D / DW);
-  if (nsplit <= 16)
-    hipLaunchKernelGGL((combine_kernel<D, DW, 16>), grid, dim3(DW), 0, s, part_o, part_ml, nsplit, out, lse);
+  const dim3 grid(rows, D / DW), block(DW / VEC);
+  if (nsplit <= 8)
+    hipLaunchKernelGGL((combine_kernel<D, DW, VEC, 8>), grid, block, 0, s, part_o, part_ml, nsplit, out, lse);
+  else if (nsplit <= 16)
+    hipLaunchKernelGGL((combine_kernel<D, DW, VEC, 16>), grid, block, 0, s, part_o, part_ml, nsplit, out, lse);
   else if (nsplit <= 32)
-    hipLaunchKernelGGL((combine_kernel<D, DW, 32>), grid, dim3(DW), 0, s, part_o, part_ml, nsplit, out, lse);
+    hipLaunchKernelGGL((combine_kernel<D, DW, VEC, 32>), grid, block, 0, s, part_o, part_ml, nsplit, out, lse);
   else if (nsplit <= 64)
-    hipLaunchKernelGGL((combine_kernel<D, DW, 64>), grid, dim3(DW), 0, s, part_o, part_ml, nsplit, out, lse);
+    hipLaunchKernelGGL((combine_kernel<D, DW, VEC, 64>), grid, block, 0, s, part_o, part_ml, nsplit, out, lse);
   else
-    hipLaunchKernelGGL((combine_kernel<D, DW, 128>), grid, dim3(DW), 0, s, part_o, part_ml, nsplit, out, lse);
+    hipLaunchKernelGGL((combine_kernel<D, DW, VEC, 128>), grid, block, 0, s, part_o, part_ml, nsplit, out, lse);
 }
 
 // ---------------------------------------------------------------------------
@@ -657,9 +688,9 @@ extern "C" dsa_status dsa_sparse_attn(const void* q, const void* k_cache, const 
               "dsa_sparse_attn: the latent path reads V from the key rows (pass v_cache == k_cache)");
   DSA_REQUIRE(k <= (latent ? kLatentMaxSplits : kCombineMaxSplits) * kMaxTokPerSplit, DSA_ERR_UNSUPPORTED,
               "dsa_sparse_attn: k=%d too large", k);
-  DSA_REQUIRE(aligned16(q) && aligned16(k_cache) && aligned16(v_cache) && kv_page_stride % 8 == 0 &&
-                  kv_row_stride % 8 == 0 && kv_head_stride % 8 == 0,
-              DSA_ERR_INVALID_ARG, "dsa_sparse_attn: q/K/V rows must be 16-byte aligned");
+  DSA_REQUIRE(aligned16(q) && aligned16(k_cache) && aligned16(v_cache) && aligned16(out) &&
+                  kv_page_stride % 8 == 0 && kv_row_stride % 8 == 0 && kv_head_stride % 8 == 0,
+              DSA_ERR_INVALID_ARG, "dsa_sparse_attn: q/K/V rows and out must be 16-byte aligned");
   const Plan p = make_plan(B, S_q, H_q, H_kv, D_qk, D_v, k);
   DSA_REQUIRE(p.ws_bytes == 0 || (workspace && workspace_bytes >= p.ws_bytes), DSA_ERR_WORKSPACE,
               "dsa_sparse_attn: workspace of %zu bytes needed, %zu given", p.ws_bytes, workspace_bytes);

@@ -133,7 +133,8 @@ dsa_status dsa_topk(const float* scores, const int32_t* row_len, int B, int R,
  * {64, 128}; or H_kv == 1, H_q == 64, D_qk == 576, D_v == 512 with
  * v_cache == k_cache (latent MQA; QK^T and PV on bf16 MFMA, P rounded to
  * bf16).  k <= 131072 (latent: k <= 32768), B*S_q <= 65535.  Rows/heads/base
- * pointers 16-byte aligned.
+ * pointers of q, k_cache, v_cache and out 16-byte aligned (else
+ * DSA_ERR_INVALID_ARG).
  */
 size_t dsa_sparse_attn_workspace_size(int B, int S_q, int H_q, int H_kv,
                                       int D_qk, int D_v, int k);

@@ -91,6 +91,7 @@ def test_sparse_attn_validation():
     assert _attn_call(D_qk=96, D_v=96) == _lib.DSA_ERR_UNSUPPORTED
     assert _attn_call(idx_rows=3, S_q=2) == _lib.DSA_ERR_INVALID_ARG
     assert _attn_call(rs=64 * 128 + 4) == _lib.DSA_ERR_INVALID_ARG    # row not 16-byte aligned
+    assert _attn_call(out=ctypes.c_void_p(0x10004)) == _lib.DSA_ERR_INVALID_ARG   # out not 16-byte aligned
     assert _attn_call(scale=float("nan")) == _lib.DSA_ERR_INVALID_ARG
     assert _attn_call(B=65536) == _lib.DSA_ERR_UNSUPPORTED            # B*S_q grid limit
     need = lib.dsa_sparse_attn_workspace_size(1, 1, 64, 64, 128, 128, 2048)

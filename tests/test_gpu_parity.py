@@ -123,6 +123,32 @@ def test_topk_exact(name, path):
     _topk_case(s, lens, k)
 
 
+@pytest.mark.parametrize("pattern", ["ascending", "descending", "blocks", "spikes"])
+def test_topk_clustered(pattern):
+    """Kept positions packed into whole 64-position runs (one thread of the
+    one-workgroup path emits up to 64 of them) or isolated among equal keys."""
+    rng = np.random.default_rng(abs(hash(pattern)) % 2**32)
+    k, ld = 2048, 32768
+    lens = [32768, 32000, 4096 + 37, 20000]
+    t = np.arange(ld, dtype=np.float64)
+    if pattern == "ascending":          # the top k are the last k positions
+        s = np.tile(t, (len(lens), 1))
+    elif pattern == "descending":       # the first k positions
+        s = np.tile(-t, (len(lens), 1))
+    elif pattern == "blocks":           # runs of 64 (and one of 63) high scores, rest low
+        s = rng.standard_normal((len(lens), ld)) - 100.0
+        for b in range(len(lens)):
+            starts = rng.choice(max(1, lens[b] // 64 - 1), size=40, replace=False) * 64
+            for i, st in enumerate(starts):
+                s[b, st + (i == 0):st + 64] = 50.0 + rng.standard_normal(64 - (i == 0))
+    else:                               # a few spikes above a sea of equal keys
+        s = np.full((len(lens), ld), 3.0)
+        for b in range(len(lens)):
+            s[b, rng.choice(lens[b], size=100, replace=False)] = 7.0
+    log("topk clustered", pattern, lens, k)
+    _topk_case(s.astype(np.float32), lens, k)
+
+
 @pytest.mark.parametrize("ld", [1000, 30000, 100000, 200000])
 def test_topk_small_k_and_k_ge_L(ld):
     rng = np.random.default_rng(ld)

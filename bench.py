@@ -101,7 +101,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(this build has no multi-GPU path).", file=sys.stderr)
+              "(this library has no multi-GPU path).", file=sys.stderr)
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy()

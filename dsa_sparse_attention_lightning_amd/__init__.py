@@ -79,8 +79,22 @@ def _workspace(nbytes, device, ws):
         return ws
     if ws is None:
         return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    _need(isinstance(ws, torch.Tensor) and ws.is_cuda and ws.is_contiguous(),
+          "workspace must be a contiguous device tensor")
     _need(ws.numel() * ws.element_size() >= nbytes, f"workspace needs {nbytes} bytes")
     return ws
+
+
+def _outputs(accepted_len, emitted, B, G, device):
+    if accepted_len is None:
+        accepted_len = torch.empty(B, dtype=torch.int32, device=device)
+    if emitted is None:
+        emitted = torch.empty((B, G + 1), dtype=torch.int32, device=device)
+    _dev(accepted_len, "accepted_len", (torch.int32,))
+    _dev(emitted, "emitted", (torch.int32,))
+    _need(accepted_len.shape == (B,), "accepted_len must be [B]")
+    _need(emitted.shape == (B, G + 1), "emitted must be [B, G+1]")
+    return accepted_len, emitted
 
 
 def index_scores(q, w, k_index, block_table, row_len, *, page, ld=None, out=None, stream=None):
@@ -168,6 +182,7 @@ def sparse_attn(q, k_cache, v_cache, block_table, idx, *, page, D_v=None, sm_sca
         _need(v_cache.shape[:3] == k_cache.shape[:3], "v_cache must match k_cache in [pages, page, H_kv]")
         _need(D_v == D_qk, "separate K/V caches need D_v == D_qk (shared strides)")
         strides = (page * H_kv * D_qk, H_kv * D_qk, D_qk)
+    _need(block_table.dim() == 2 and block_table.shape[0] == B, "block_table must be [B, max_pages]")
     if idx.dim() == 2:
         idx_rows, k = 1, idx.shape[1]
         _need(idx.shape[0] == B, "idx must be [B, k]")
@@ -182,6 +197,8 @@ def sparse_attn(q, k_cache, v_cache, block_table, idx, *, page, D_v=None, sm_sca
         lse = torch.empty((B, S_q, H_q), dtype=torch.float32, device=q.device)
     _dev(out, "out", (torch.float32,))
     _dev(lse, "lse", (torch.float32,))
+    _need(out.shape == (B, S_q, H_q, D_v), "out must be [B, S_q, H_q, D_v]")
+    _need(lse.shape == (B, S_q, H_q), "lse must be [B, S_q, H_q]")
     nbytes = int(lib.dsa_sparse_attn_workspace_size(B, S_q, H_q, H_kv, D_qk, D_v, k))
     ws = _workspace(nbytes, q.device, workspace)
     st = lib.dsa_sparse_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), strides[0], strides[1], strides[2],
@@ -211,10 +228,7 @@ def spec_verify(target_logits, draft_logits, draft_tokens, *, uniforms=None, see
     if uniforms is not None:
         _dev(uniforms, "uniforms", (torch.float32,))
         _need(uniforms.shape == (B, G + 1, 2), "uniforms must be [B, G+1, 2]")
-    if accepted_len is None:
-        accepted_len = torch.empty(B, dtype=torch.int32, device=target_logits.device)
-    if emitted is None:
-        emitted = torch.empty((B, G + 1), dtype=torch.int32, device=target_logits.device)
+    accepted_len, emitted = _outputs(accepted_len, emitted, B, G, target_logits.device)
     if diag is not None:
         _dev(diag, "diag", (torch.float32,))
         _need(diag.shape == (B, G + 1, 4), "diag must be [B, G+1, 4]")
@@ -241,10 +255,7 @@ def spec_verify_greedy(target_logits, draft_tokens, *, accepted_len=None, emitte
     G = G1 - 1
     _need(G >= 1, "target_logits needs G+1 >= 2 rows")
     _need(draft_tokens.shape == (B, G), "draft_tokens must be [B, G]")
-    if accepted_len is None:
-        accepted_len = torch.empty(B, dtype=torch.int32, device=target_logits.device)
-    if emitted is None:
-        emitted = torch.empty((B, G + 1), dtype=torch.int32, device=target_logits.device)
+    accepted_len, emitted = _outputs(accepted_len, emitted, B, G, target_logits.device)
     nbytes = int(lib.spec_verify_greedy_workspace_size(B, G, V))
     ws = _workspace(nbytes, target_logits.device, workspace)
     st = lib.spec_verify_greedy(_ptr(target_logits), _ptr(draft_tokens), B, G, V, _ptr(accepted_len),

@@ -608,3 +608,35 @@ def test_verify_pass_rows():
     for r in range(R):
         o_ref, _ = O.sparse_attn(d.q[r, 0], d.K[0], d.V[0], idx.cpu().numpy()[0, r], d.sm_scale)
         assert np.abs(out[r] - o_ref).max() <= ATTN_TOL
+
+
+def test_binding_rejects_bad_outputs():
+    """Caller-supplied outputs and workspaces of the wrong shape, dtype or
+    device are refused by the binding before any launch."""
+    d = I.draft_inputs(0, [300], H_I=4, D_I=32, H_q=4, H_kv=4, D_qk=64, D_v=64, k=64, G=2)
+    dd = DraftDev(d)
+    # valid inputs throughout (the generator's own cache; k = 512 needs a
+    # workspace), so only the binding's checks can fail
+    idx = torch.full((1, 512), -1, dtype=torch.int32, device=DEV)
+    q = torch.zeros((1, 1, 4, 64), dtype=torch.bfloat16, device=DEV)
+    kc = dd.k
+    assert dsa.sparse_attn_workspace_size(1, 1, 4, 4, 64, 64, 512) > 0
+    good = torch.empty((1, 1, 4, 64), dtype=torch.float32, device=DEV)
+    with pytest.raises(ValueError):
+        dsa.sparse_attn(q, kc, kc, dd.bt, idx, page=d.page, out=torch.empty((1, 1, 4, 32), device=DEV))
+    with pytest.raises(ValueError):
+        dsa.sparse_attn(q, kc, kc, dd.bt, idx, page=d.page, out=good, lse=torch.empty((1, 1, 3), device=DEV))
+    with pytest.raises(ValueError):
+        dsa.sparse_attn(q, kc, kc, dd.bt.repeat(2, 1), idx, page=d.page, out=good)
+    with pytest.raises(ValueError):
+        dsa.sparse_attn(q, kc, kc, dd.bt, idx, page=d.page, out=good,
+                        workspace=torch.empty(1 << 20, dtype=torch.uint8))          # host workspace
+    t = torch.zeros((2, 3, 50), device=DEV)
+    dl = torch.zeros((2, 2, 50), device=DEV)
+    dr = torch.zeros((2, 2), dtype=torch.int32, device=DEV)
+    with pytest.raises(ValueError):
+        dsa.spec_verify(t, dl, dr, accepted_len=torch.empty(3, dtype=torch.int32, device=DEV))
+    with pytest.raises(ValueError):
+        dsa.spec_verify(t, dl, dr, emitted=torch.empty((2, 2), dtype=torch.int32, device=DEV))
+    with pytest.raises(ValueError):
+        dsa.spec_verify_greedy(t, dr, emitted=torch.empty((2, 3), dtype=torch.int64, device=DEV))

@@ -72,28 +72,46 @@ constexpr long long kAttnStreamBytes = DSA_ATTN_STREAM_BYTES;   // last-level ca
 // ---------------------------------------------------------------------------
 // Per-head KV gather kernel
 // ---------------------------------------------------------------------------
-// Loads of U tokens' K and V pieces.  Loads are unconditional (invalid
-// tokens and padding heads read row 0 / the last head, and are ignored by
-// consume) so that the compiler keeps all of them in flight at once.
+// Row offsets (elements) of a wave's tokens: lane l holds those of the
+// wave's local tokens l and l + 64 (-1: absent).  A token's offset is the
+// same for the whole wave, so it is read into scalar registers and K/V loads
+// use a scalar row base plus the lane's 32-bit offset inside the row.
+struct WaveRows {
+  int64_t o0, o1;
+  int nw;          // tokens of this wave
+};
+static_assert(kMaxTokPerSplit <= 128 * kWaves, "a wave's tokens fit in two offsets per lane");
+
+__device__ __forceinline__ int64_t row_off(const WaveRows& r, int j) {   // j wave-uniform
+  const int jj = min(j, max(r.nw - 1, 0));
+  const int64_t v = jj < 64 ? r.o0 : r.o1;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, jj & 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)v >> 32), jj & 63);
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // 16 bytes of a KV row; NT: non-temporal (a gather far larger than the
 // last-level cache, whose rows are not read again by this call)
 template <bool NT>
-__device__ __forceinline__ uint4 ld_row16(const uint16_t* p) {
+__device__ __forceinline__ uint4 ld_row16(const uint16_t* row, uint32_t lane_bytes) {
   typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-  const u32x4_t v = NT ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p))
-                       : *reinterpret_cast<const u32x4_t*>(p);
+  const u32x4_t* p = reinterpret_cast<const u32x4_t*>(reinterpret_cast<const char*>(row) + lane_bytes);
+  const u32x4_t v = NT ? __builtin_nontemporal_load(p) : *p;
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
-template <int D, int GQ, int U, bool NT>
-__device__ __forceinline__ void issue_loads(const AttnArgs& a, const int64_t* s_off, int i, int ntok,
-                                            size_t lane_off, uint4 (&kr)[U], uint4 (&vr)[U]) {
+// Loads of the U tokens j..j+U-1 of this wave.  Loads are unconditional
+// (tokens past the wave's end repeat its last token, absent ones read the
+// cache's first row; consume ignores both) so that all are in flight at once.
+template <int U, bool NT>
+__device__ __forceinline__ void issue_loads(const AttnArgs& a, const WaveRows& wr, int j, uint32_t lane_bytes,
+                                            int64_t (&off)[U], uint4 (&kr)[U], uint4 (&vr)[U]) {
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const int li = min(i + u * kWaves, ntok - 1);
-    const int64_t off = max(s_off[li], (int64_t)0);
-    kr[u] = ld_row16<NT>(a.kc + off + lane_off);
-    vr[u] = ld_row16<NT>(a.vc + off + lane_off);
+    off[u] = row_off(wr, j + u);
+    const int64_t o = max(off[u], (int64_t)0);
+    kr[u] = ld_row16<NT>(a.kc + o, lane_bytes);
+    vr[u] = ld_row16<NT>(a.vc + o, lane_bytes);
   }
 }
 
@@ -113,16 +131,13 @@ __device__ __forceinline__ float dot8_bf16(const uint4& q, const uint4& k) {
 }
 
 template <int D, int GQ, int U>
-__device__ __forceinline__ void consume(const int64_t* s_off, int i, int ntok, float scale_log2,
+__device__ __forceinline__ void consume(const WaveRows& wr, int j, const int64_t (&off)[U], float scale_log2,
                                         const uint4 (&qv)[GQ], float (&m)[GQ], float (&l)[GQ],
                                         float (&acc)[GQ][8], const uint4 (&kr)[U], const uint4 (&vr)[U]) {
   constexpr int SLOT = D / 8;
   bool ok[U];
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int li = i + u * kWaves;
-    ok[u] = li < ntok && s_off[li] >= 0;   // wave-uniform
-  }
+  for (int u = 0; u < U; ++u) ok[u] = j + u < wr.nw && off[u] >= 0;   // wave-uniform
 #pragma unroll
   for (int j = 0; j < GQ; ++j) {
     float sc[U];
@@ -166,7 +181,6 @@ __global__ __launch_bounds__(kThreads) void mha_attn_kernel(AttnArgs a) {
   constexpr int SLOT = D / 8;            // lanes per KV row
   constexpr int NSLOT = 64 / SLOT;       // KV heads per wave
   constexpr int NH = NSLOT * GQ;         // query heads per workgroup
-  __shared__ int64_t s_off[kMaxTokPerSplit];
   __shared__ float s_ml[kWaves][NH][2];
   __shared__ float s_o[kWaves][NH][D];
 
@@ -203,16 +217,24 @@ __global__ __launch_bounds__(kThreads) void mha_attn_kernel(AttnArgs a) {
   const int g = hg * NSLOT + slot;                   // KV head of this lane
   const bool head_ok = g < a.H_kv;
 
-  // Row offsets of this split's tokens, resolved through the page table once.
+  // Row offsets of this wave's tokens (split-local w, w + kWaves, ...),
+  // resolved through the page table once, two per lane; no barrier.
   const int32_t* idx = a.idx + ((size_t)b * a.idx_rows + (a.idx_rows > 1 ? s : 0)) * a.k;
   const int32_t* bt = a.bt + (size_t)b * a.max_pages;
   const int t_lo = split * a.tok_per_split;
   const int ntok = min(a.tok_per_split, a.k - t_lo);
-  for (int i = tid; i < ntok; i += kThreads) {
-    const int t = idx[t_lo + i];
+  WaveRows wr;
+  wr.nw = wave < ntok ? (ntok - wave + kWaves - 1) / kWaves : 0;
+  auto resolve = [&](int j) -> int64_t {
+    if (j >= wr.nw) return -1;
+    const int t = idx[t_lo + wave + j * kWaves];
     // positions outside the block table (outside the contract) count as absent
-    s_off[i] = (t >= 0 && t / a.page < a.max_pages) ? (int64_t)bt[t / a.page] * a.page_stride + (int64_t)(t % a.page) * a.row_stride : -1;
-  }
+    return (t >= 0 && t / a.page < a.max_pages)
+               ? (int64_t)bt[t / a.page] * a.page_stride + (int64_t)(t % a.page) * a.row_stride
+               : (int64_t)-1;
+  };
+  wr.o0 = resolve(lane);
+  wr.o1 = resolve(lane + 64);
 
   uint4 qv[GQ];   // this lane's 8 query dims per head, packed bf16 pairs
 #pragma unroll
@@ -228,23 +250,22 @@ __global__ __launch_bounds__(kThreads) void mha_attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
   }
-  __syncthreads();
-
-  // Wave w takes local tokens w, w + kWaves, ...; loads run one U-token stage ahead.
-  // padding heads (g >= H_kv) read the last real head; their results are dropped
-  const size_t lane_off = (size_t)min(g, a.H_kv - 1) * a.head_stride + sub * 8;
-  constexpr int STEP = kWaves * U;
+  // Wave w takes split-local tokens w, w + kWaves, ... (its local tokens
+  // 0, 1, ...); loads run one U-token stage ahead.  Padding heads
+  // (g >= H_kv) read the last real head; their results are dropped.
+  const uint32_t lane_bytes = (uint32_t)(((int64_t)min(g, a.H_kv - 1) * a.head_stride + sub * 8) * 2);
   uint4 kA[U], vA[U], kB[U], vB[U];
-  int i = wave;
-  issue_loads<D, GQ, U, NT>(a, s_off, i, ntok, lane_off, kA, vA);
-  while (i < ntok) {
-    issue_loads<D, GQ, U, NT>(a, s_off, i + STEP, ntok, lane_off, kB, vB);
-    consume<D, GQ, U>(s_off, i, ntok, a.scale_log2, qv, m, l, acc, kA, vA);
-    i += STEP;
-    if (i >= ntok) break;
-    issue_loads<D, GQ, U, NT>(a, s_off, i + STEP, ntok, lane_off, kA, vA);
-    consume<D, GQ, U>(s_off, i, ntok, a.scale_log2, qv, m, l, acc, kB, vB);
-    i += STEP;
+  int64_t oA[U], oB[U];
+  int j = 0;
+  issue_loads<U, NT>(a, wr, j, lane_bytes, oA, kA, vA);
+  while (j < wr.nw) {
+    issue_loads<U, NT>(a, wr, j + U, lane_bytes, oB, kB, vB);
+    consume<D, GQ, U>(wr, j, oA, a.scale_log2, qv, m, l, acc, kA, vA);
+    j += U;
+    if (j >= wr.nw) break;
+    issue_loads<U, NT>(a, wr, j + U, lane_bytes, oA, kA, vA);
+    consume<D, GQ, U>(wr, j, oB, a.scale_log2, qv, m, l, acc, kB, vB);
+    j += U;
   }
 
   // merge the waves (fixed order)

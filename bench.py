@@ -255,11 +255,12 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def _time_graph(fn, reps=20, inner=8):
+def _time_graph(fn, reps=20, inner=8, warm_s=0.05):
     """Average duration (us) of one call of `fn`: `inner` calls captured
     back to back in one HIP graph (so the per-replay launch gap is spread
     over them), replayed `reps` times and timed with events on the launch
-    stream."""
+    stream.  At least 3 untimed replays and `warm_s` seconds of them come
+    first (a cold start measured 2-3 % slower)."""
     import torch
     fn()
     torch.cuda.synchronize()
@@ -267,9 +268,11 @@ def _time_graph(fn, reps=20, inner=8):
     with torch.cuda.graph(g, stream=torch.cuda.Stream()):
         for _ in range(inner):
             fn()
-    for _ in range(3):
+    t_end, n = time.perf_counter() + warm_s, 0
+    while n < 3 or time.perf_counter() < t_end:
         g.replay()
-    torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        n += 1
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     stream = torch.cuda.current_stream()
     a.record(stream)

@@ -40,6 +40,10 @@ def log(*a):
     dict(lens=[4133, 900], H_I=64, D_I=64, page=16, shuffle=True, R=5),    # 5 rows, ragged, 2 sequences
     dict(lens=[1300], H_I=48, D_I=32, page=64, shuffle=True, R=7),         # 7 rows, partial head block
     dict(lens=[9000], H_I=64, D_I=128, page=64, shuffle=True, R=6),        # 6 rows, several tiles per workgroup
+    # long contexts take the Q-in-LDS kernel (5-8 rows, D_I = 128, ld * B >= 2^18)
+    dict(lens=[270011], H_I=64, D_I=128, page=64, shuffle=True, R=8),      # 8 rows, ragged tail
+    dict(lens=[140000, 131075], H_I=64, D_I=128, page=16, shuffle=True, R=5),   # 2 sequences, 5 rows
+    dict(lens=[300000], H_I=48, D_I=128, page=64, shuffle=True, R=7),      # partial head block
 ])
 def test_index_scores_exact(case):
     log("index_scores", case)

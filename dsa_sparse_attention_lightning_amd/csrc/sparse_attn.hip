@@ -74,8 +74,8 @@ constexpr long long kAttnStreamBytes = DSA_ATTN_STREAM_BYTES;   // last-level ca
 // ---------------------------------------------------------------------------
 // Row offsets (elements) of a wave's tokens: lane l holds those of the
 // wave's local tokens l and l + 64 (-1: absent).  A token's offset is the
-// same for the whole wave, so it is read into scalar registers and K/V loads
-// use a scalar row base plus the lane's 32-bit offset inside the row.
+// same for the whole wave, so it is read into scalar registers (readlane)
+// and each K/V load adds the lane's 32-bit byte offset inside the row.
 struct WaveRows {
   int64_t o0, o1;
   int nw;          // tokens of this wave

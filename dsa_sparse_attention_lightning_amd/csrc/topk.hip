@@ -441,10 +441,13 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const int32_t*
 // ---------------------------------------------------------------------------
 // One-workgroup path for rows whose keys fit in LDS (up to kOneMaxLd
 // positions): a single launch.  Longer rows go to the multi-workgroup
-// pipeline above, which is faster once the keys no longer fit.  Radix select on 12/12/8-bit digits finds the k-th largest key
-// prefix; the output is an ordered compaction over positions (each wave owns
-// a contiguous position range, ballots give in-order ranks), so equal keys
-// are taken lowest position first and no sort is needed.
+// pipeline above, which is faster once the keys no longer fit.  A radix
+// select on 12-bit digits (after the bits every key shares) narrows the k-th
+// largest key to one bin.  When that bin is small, a bitmap of the kept
+// positions is built with ballots and its set bits are emitted in position
+// order; otherwise an ordered compaction (each wave owns a contiguous
+// position range, ballots give in-order ranks) writes them.  Either way equal
+// keys are taken lowest position first and no sort is needed.
 // ---------------------------------------------------------------------------
 constexpr int kOneThreads = 1024;
 constexpr int kOneWaves = kOneThreads / 64;
@@ -520,9 +523,9 @@ __global__ __launch_bounds__(kOneThreads) void topk_one_kernel(const float* __re
   // spreads over the range the scores actually occupy (indexer scores sit in
   // a few octaves; a fixed top-bits digit would put most of the row into a
   // handful of bins).
-  // 16-byte loads (4 positions per lane) over the quads inside [0, L): a
-  // wave's dword loads are address-rate bound at a quarter of this width.
-  // The last L % 4 positions (or a row not 16-byte aligned) go one by one.
+  // 16-byte loads (4 positions per lane, a quarter of the load instructions
+  // of one position per lane) over the quads inside [0, L); the last L % 4
+  // positions, or a row that is not 16-byte aligned, go one by one.
   uint32_t kmin = 0xffffffffu, kmax = 0u;
   const int L4 = (reinterpret_cast<uintptr_t>(s) & 15u) == 0 ? (L & ~3) : 0;
   for (int q0 = tid * 4; q0 < L4; q0 += kU * kOneThreads * 4) {
@@ -599,9 +602,9 @@ __global__ __launch_bounds__(kOneThreads) void topk_one_kernel(const float* __re
     }
   }
 
-  // The kept positions are staged in LDS behind the keys when both fit, then
-  // stored 16 bytes per lane (in place, scattered dword stores would be
-  // address-rate bound); otherwise they are stored directly.
+  // The kept positions are staged in LDS behind the keys when both fit and
+  // then stored 16 bytes per lane (one coalesced pass instead of scattered
+  // 4-byte stores); otherwise they are stored directly.
   uint32_t* obuf = keys + align_up(L, 4);
   const bool staged = align_up(L, 4) + align_up(k, 4) <= kOneLdsKeys;
   auto put = [&](uint32_t slot, int t) {

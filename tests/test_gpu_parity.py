@@ -339,6 +339,18 @@ def test_spec_verify_many_sequences(std):
     assert near <= 1
 
 
+@pytest.mark.parametrize("B,G,V", [
+    (1, 1, 1000),       # one draft
+    (3, 32, 4099),      # the largest chain, V not a multiple of 4
+    (9, 7, 2048),       # first batch size with the decision in a kernel of its own
+    (8, 7, 600000),     # decision inside the mass kernel, logits past the last-level cache (streamed)
+])
+def test_spec_verify_shape_edges(B, G, V):
+    vi = I.verify_inputs(B * 100 + G, B, G, V, 2.0)
+    _, _, near = _verify_case(vi, True)
+    assert near <= 1
+
+
 def test_spec_verify_special_cases():
     rng = np.random.default_rng(3)
     B, G, V = 8, 7, 2048

@@ -197,6 +197,9 @@ def _attn_vs_oracle(d, dd, idx_np, step=0, tol=ATTN_TOL, out_check=True):
     dict(lens=[900], H=8, Hkv=2, D=128, k=300, shuffle=True),
     dict(lens=[1200, 640], H=16, Hkv=4, D=64, k=1000, shuffle=True),
     dict(lens=[100], H=6, Hkv=3, D=64, k=64, shuffle=False),
+    dict(lens=[40000], H=4, Hkv=4, D=128, k=20000, shuffle=True),      # 79 splits (128-way combine)
+    dict(lens=[9000], H=32, Hkv=8, D=128, k=6000, shuffle=True),       # GQA 4, 24 splits
+    dict(lens=[140000], H=4, Hkv=4, D=64, k=131072, shuffle=True),     # largest k: 1024 tokens per split
 ])
 def test_sparse_attn_matches_oracle(case):
     log("sparse_attn", case)

@@ -568,6 +568,7 @@ def test_draft_block_graph_replays():
     dict(lens=[100], k=128, shuffle=False),             # k > L: padding inside the split
     dict(lens=[1500], k=1000, shuffle=True),            # splits of 63 tokens (a partial chunk)
     dict(lens=[9000], k=8192, shuffle=True),            # several 64-token chunks per split
+    dict(lens=[40000], k=32768, shuffle=True),          # the largest k: 32 splits of 1024 tokens
 ])
 def test_latent_attn_matches_oracle(case):
     log("latent", case)

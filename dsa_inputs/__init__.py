@@ -137,17 +137,23 @@ class DraftInputs:
         return 1.0 / np.sqrt(self.D_qk)
 
 
-def _page_table(rng, caps, page, shuffle):
+def _page_table(rng, caps, page, shuffle, spare_page0=False):
+    """Block table over one physical pool of sum_b ceil(cap_b / page) pages,
+    optionally shuffled once.  spare_page0: the pool gets one more page, at
+    physical index 0, that belongs to no sequence (every table entry shifts up
+    by one; the random draws are the same as without it)."""
     n_pages = [(c + page - 1) // page for c in caps]
     total = int(sum(n_pages))
     phys = rng.permutation(total) if shuffle else np.arange(total)
+    if spare_page0:
+        phys = phys + 1
     max_pages = max(n_pages)
     table = np.full((len(caps), max_pages), -1, np.int32)
     pos = 0
     for b, n in enumerate(n_pages):
         table[b, :n] = phys[pos:pos + n]
         pos += n
-    return table, total
+    return table, total + int(spare_page0)
 
 
 def _scatter_pages(logical, table_row, pages_arr, page):
@@ -161,13 +167,15 @@ def _scatter_pages(logical, table_row, pages_arr, page):
 
 def draft_inputs(seed, lens, *, H_I=64, D_I=128, H_q=64, H_kv=64, D_qk=128,
                  D_v=128, k=2048, G=7, R=1, page=64, shuffle_pages=False,
-                 integer_indexer=False, latent=False, poison=False):
+                 integer_indexer=False, latent=False, poison=False, spare_page0=False):
     """Synthetic draft-block inputs.
 
     Each sequence b holds L_b = lens[b] target-written positions plus G
     draft-written slots after them (capacity L_b + G).  With poison=True the
     draft-written slots and every unused page row hold bf16 NaN, so any read of
-    them shows up in the outputs.
+    them shows up in the outputs.  spare_page0=True adds a physical page 0
+    that no sequence owns (NaN when poisoned, else zeros): the cache's very
+    first row is then never a target-written row.
 
     integer_indexer: indexer q and keys are integers uniform in [-4, 4] and w
     is m/64 with m uniform in {0..63} (exact in fp32 under any summation
@@ -182,7 +190,7 @@ def draft_inputs(seed, lens, *, H_I=64, D_I=128, H_q=64, H_kv=64, D_qk=128,
     caps = [int(L) + G for L in lens]
     if latent:
         H_kv = 1
-    table, total_pages = _page_table(rng, caps, page, shuffle_pages)
+    table, total_pages = _page_table(rng, caps, page, shuffle_pages, spare_page0)
 
     # indexer queries and weights
     if integer_indexer:

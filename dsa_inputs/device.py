@@ -58,11 +58,13 @@ def _randn_bf16(shape, gen, dev, chunk=1 << 26):
 
 
 def draft_inputs(seed, lens, *, H_I=64, D_I=128, H_q=64, H_kv=64, D_qk=128, D_v=128, k=2048, G=7,
-                 R=1, page=64, shuffle_pages=False, latent=False, integer_indexer=False, dev="cuda:0"):
+                 R=1, page=64, shuffle_pages=False, latent=False, integer_indexer=False, spare_page0=False,
+                 dev="cuda:0"):
     """Device draft-block inputs.  Capacity per sequence is L_b + G (the draft
     slots exist but are never scored or selected).  Page tables follow the
     same construction as dsa_inputs: one physical pool, optionally shuffled
-    once (numpy, seeded)."""
+    once (numpy, seeded); spare_page0 adds a physical page 0 that no sequence
+    owns (see poison_)."""
     gen = torch.Generator(device=dev)
     gen.manual_seed(int(seed))
     rng = np.random.default_rng(seed)
@@ -72,6 +74,9 @@ def draft_inputs(seed, lens, *, H_I=64, D_I=128, H_q=64, H_kv=64, D_qk=128, D_v=
     n_pages = [(c + page - 1) // page for c in caps]
     total = int(sum(n_pages))
     phys = rng.permutation(total) if shuffle_pages else np.arange(total)
+    if spare_page0:
+        phys = phys + 1
+        total += 1
     table = np.full((B, max(n_pages)), -1, np.int32)
     pos = 0
     for b, n in enumerate(n_pages):
@@ -99,6 +104,32 @@ def draft_inputs(seed, lens, *, H_I=64, D_I=128, H_q=64, H_kv=64, D_qk=128, D_v=
                        page=page, latent=latent, q_index=q_index, w=w, kidx=kidx,
                        block_table=torch.from_numpy(table).to(dev), row_len=row_len, q=q,
                        k_cache=k_cache, v_cache=v_cache, ld=max(caps))
+
+
+def poison_(d):
+    """Writes bf16 NaN, in place, into every cache row that no target wrote:
+    the G draft-written slots L_b..L_b+G-1 of each sequence, the unused rows
+    of its last page, and every row of a page no sequence owns (physical page
+    0 with spare_page0).  Index keys, K and V alike.  A read of any of them
+    then shows up as NaN in the outputs."""
+    nan = torch.tensor(float("nan"), dtype=torch.bfloat16, device=d.k_cache.device)
+    caches = [d.kidx, d.k_cache] + ([] if d.latent else [d.v_cache])
+    bt = d.block_table.cpu().numpy()
+    owned = np.zeros(d.kidx.shape[0], bool)
+    pages, rows = [], []
+    for b, L in enumerate(d.lens):
+        n_pages = (L + d.G + d.page - 1) // d.page
+        owned[bt[b, :n_pages]] = True
+        t = np.arange(L, n_pages * d.page)            # draft slots, then the page's unused tail
+        pages.append(bt[b, t // d.page])
+        rows.append(t % d.page)
+    pi = torch.as_tensor(np.concatenate(pages).astype(np.int64), device=d.k_cache.device)
+    ri = torch.as_tensor(np.concatenate(rows).astype(np.int64), device=d.k_cache.device)
+    spare = torch.as_tensor(np.flatnonzero(~owned).astype(np.int64), device=d.k_cache.device)
+    for c in caches:
+        c[pi, ri] = nan
+        if spare.numel():
+            c[spare] = nan
 
 
 @dataclass

@@ -102,7 +102,8 @@ __device__ __forceinline__ uint4 ld_row16(const uint16_t* row, uint32_t lane_byt
 
 // Loads of the U tokens j..j+U-1 of this wave.  Loads are unconditional
 // (tokens past the wave's end repeat its last token, absent ones read the
-// cache's first row; consume ignores both) so that all are in flight at once.
+// cache's first row) so that all are in flight at once; consume skips both
+// entirely, so no value of those rows (NaN included) reaches the result.
 template <int U, bool NT>
 __device__ __forceinline__ void issue_loads(const AttnArgs& a, const WaveRows& wr, int j, uint32_t lane_bytes,
                                             int64_t (&off)[U], uint4 (&kr)[U], uint4 (&vr)[U]) {
@@ -501,16 +502,25 @@ __global__ __launch_bounds__(256) void latent_attn_kernel(AttnArgs a) {
   const int nchunks = (ntok + kLatChunk - 1) / kLatChunk;
   for (int ch = 0; ch < nchunks; ++ch) {
     const int c0 = ch * kLatChunk;
-    // V pieces: lane = token c0 + lane, dim chunk wave + 4j (tokens past ntok read row 0)
+    // V pieces: lane = token c0 + lane, dim chunk wave + 4j.  Loads are
+    // unconditional (absent tokens and tokens past ntok read the cache's first
+    // row), then such tokens' pieces are replaced by zeros: their softmax
+    // weight is exactly 0, but 0 * NaN (a draft-written, unused or
+    // uninitialised row) would still reach every head's output through PV.
     uint4 vp[VPT];
     {
       const int li = min(c0 + lane, ntok - 1);
       const int64_t off = max(s_off[li], (int64_t)0);
+      const bool vok = c0 + lane < ntok && s_off[li] >= 0;
 #pragma unroll
       for (int j = 0; j < VPT; ++j) vp[j] = *reinterpret_cast<const uint4*>(a.kc + off + (wave + 4 * j) * 8);
+#pragma unroll
+      for (int j = 0; j < VPT; ++j)
+        if (!vok) vp[j] = make_uint4(0u, 0u, 0u, 0u);
     }
     // K fragments of this wave's 16 tokens (B operand): lane holds token
-    // c0 + 16w + l%16, dims ks*32 + (l/16)*8 .. +8
+    // c0 + 16w + l%16, dims ks*32 + (l/16)*8 .. +8.  An absent token's K row
+    // only feeds its own column of S, which is replaced by -inf below.
     const int my_tok = c0 + wave * 16 + r16;
     const bool valid = my_tok < ntok && s_off[min(my_tok, ntok - 1)] >= 0;
     bf16x8_t kf[KS];
@@ -679,42 +689,51 @@ extern "C" size_t dsa_sparse_attn_workspace_size(int B, int S_q, int H_q, int H_
   return dsa::make_plan(B, S_q, H_q, H_kv, D_qk, D_v, k).ws_bytes;
 }
 
-extern "C" dsa_status dsa_sparse_attn(const void* q, const void* k_cache, const void* v_cache,
-                                      int64_t kv_page_stride, int64_t kv_row_stride, int64_t kv_head_stride,
-                                      const int32_t* block_table, const int32_t* idx, int idx_rows, int B,
-                                      int S_q, int H_q, int H_kv, int D_qk, int D_v, int page, int max_pages,
-                                      int k, float sm_scale, float* out, float* lse, void* workspace,
-                                      size_t workspace_bytes, void* stream) {
-  using namespace dsa;
-  clear_error();
+namespace dsa {
+namespace {
+
+// Host-side argument checks shared by both entry points (no HIP call).
+dsa_status check_args(const char* fn, const void* q, const void* k_cache, const void* v_cache,
+                      int64_t kv_page_stride, int64_t kv_row_stride, int64_t kv_head_stride,
+                      const int32_t* block_table, const int32_t* idx, int idx_rows, int B, int S_q, int H_q,
+                      int H_kv, int D_qk, int D_v, int page, int max_pages, int k, float sm_scale,
+                      const float* out) {
   DSA_REQUIRE(q && k_cache && v_cache && block_table && idx && out, DSA_ERR_INVALID_ARG,
-              "dsa_sparse_attn: null pointer argument");
+              "%s: null pointer argument", fn);
   DSA_REQUIRE(B >= 1 && S_q >= 1 && H_q >= 1 && H_kv >= 1 && D_qk >= 1 && D_v >= 1 && page >= 1 &&
                   max_pages >= 1 && k >= 1,
-              DSA_ERR_INVALID_ARG, "dsa_sparse_attn: sizes must be positive");
-  DSA_REQUIRE((int64_t)B * S_q <= 65535, DSA_ERR_UNSUPPORTED, "dsa_sparse_attn: B*S_q=%lld > 65535",
+              DSA_ERR_INVALID_ARG, "%s: sizes must be positive", fn);
+  DSA_REQUIRE((int64_t)B * S_q <= 65535, DSA_ERR_UNSUPPORTED, "%s: B*S_q=%lld > 65535", fn,
               (long long)B * S_q);
   DSA_REQUIRE(idx_rows == 1 || idx_rows == S_q, DSA_ERR_INVALID_ARG,
-              "dsa_sparse_attn: idx_rows=%d must be 1 or S_q=%d", idx_rows, S_q);
+              "%s: idx_rows=%d must be 1 or S_q=%d", fn, idx_rows, S_q);
   DSA_REQUIRE(kv_page_stride >= 0 && kv_row_stride >= 0 && kv_head_stride >= 0, DSA_ERR_INVALID_ARG,
-              "dsa_sparse_attn: strides must be non-negative");
-  DSA_REQUIRE(H_q % H_kv == 0, DSA_ERR_INVALID_ARG, "dsa_sparse_attn: H_q=%d not a multiple of H_kv=%d", H_q, H_kv);
-  DSA_REQUIRE(std::isfinite(sm_scale), DSA_ERR_INVALID_ARG, "dsa_sparse_attn: sm_scale not finite");
+              "%s: strides must be non-negative", fn);
+  DSA_REQUIRE(H_q % H_kv == 0, DSA_ERR_INVALID_ARG, "%s: H_q=%d not a multiple of H_kv=%d", fn, H_q, H_kv);
+  DSA_REQUIRE(std::isfinite(sm_scale), DSA_ERR_INVALID_ARG, "%s: sm_scale not finite", fn);
   const int gq = H_q / H_kv;
   const bool latent = is_latent(H_q, H_kv, D_qk, D_v);
   DSA_REQUIRE(latent || ((D_qk == 64 || D_qk == 128) && D_v == D_qk && (gq == 1 || gq == 2 || gq == 4)),
-              DSA_ERR_UNSUPPORTED, "dsa_sparse_attn: (H_q=%d, H_kv=%d, D_qk=%d, D_v=%d) not supported",
+              DSA_ERR_UNSUPPORTED, "%s: (H_q=%d, H_kv=%d, D_qk=%d, D_v=%d) not supported", fn,
               H_q, H_kv, D_qk, D_v);
   DSA_REQUIRE(!latent || v_cache == k_cache, DSA_ERR_UNSUPPORTED,
-              "dsa_sparse_attn: the latent path reads V from the key rows (pass v_cache == k_cache)");
+              "%s: the latent path reads V from the key rows (pass v_cache == k_cache)", fn);
   DSA_REQUIRE(k <= (latent ? kLatentMaxSplits : kCombineMaxSplits) * kMaxTokPerSplit, DSA_ERR_UNSUPPORTED,
-              "dsa_sparse_attn: k=%d too large", k);
+              "%s: k=%d too large", fn, k);
   DSA_REQUIRE(aligned16(q) && aligned16(k_cache) && aligned16(v_cache) && aligned16(out) &&
                   kv_page_stride % 8 == 0 && kv_row_stride % 8 == 0 && kv_head_stride % 8 == 0,
-              DSA_ERR_INVALID_ARG, "dsa_sparse_attn: q/K/V rows and out must be 16-byte aligned");
-  const Plan p = make_plan(B, S_q, H_q, H_kv, D_qk, D_v, k);
-  DSA_REQUIRE(p.ws_bytes == 0 || (workspace && workspace_bytes >= p.ws_bytes), DSA_ERR_WORKSPACE,
-              "dsa_sparse_attn: workspace of %zu bytes needed, %zu given", p.ws_bytes, workspace_bytes);
+              DSA_ERR_INVALID_ARG, "%s: q/K/V rows and out must be 16-byte aligned", fn);
+  return DSA_OK;
+}
+
+// Enqueues the call once the arguments are checked; `ws` holds at least
+// p.ws_bytes bytes of device memory when p.ws_bytes > 0.
+dsa_status enqueue(const Plan& p, const void* q, const void* k_cache, const void* v_cache, int64_t kv_page_stride,
+                   int64_t kv_row_stride, int64_t kv_head_stride, const int32_t* block_table, const int32_t* idx,
+                   int idx_rows, int B, int S_q, int H_q, int H_kv, int D_qk, int D_v, int page, int max_pages,
+                   int k, float sm_scale, float* out, float* lse, void* ws, hipStream_t s) {
+  const int gq = H_q / H_kv;
+  const bool latent = is_latent(H_q, H_kv, D_qk, D_v);
   AttnArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.kc = static_cast<const uint16_t*>(k_cache);
@@ -737,10 +756,9 @@ extern "C" dsa_status dsa_sparse_attn(const void* q, const void* k_cache, const 
   a.nsplit = p.nsplit;
   a.tok_per_split = p.tok_per_split;
   if (p.nsplit > 1) {
-    a.part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.part_o_off);
-    a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.part_ml_off);
+    a.part_o = reinterpret_cast<float*>(static_cast<char*>(ws) + p.part_o_off);
+    a.part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + p.part_ml_off);
   }
-  hipStream_t s = static_cast<hipStream_t>(stream);
   if (latent) {
     dim3 grid(p.nsplit, p.head_groups, B * S_q);
     hipLaunchKernelGGL(latent_attn_kernel, grid, dim3(256), 0, s, a);
@@ -764,4 +782,27 @@ extern "C" dsa_status dsa_sparse_attn(const void* q, const void* k_cache, const 
   if (D_v == 64) launch_combine<64>(a.part_o, a.part_ml, rows, p.nsplit, out, lse, s);
   else launch_combine<128>(a.part_o, a.part_ml, rows, p.nsplit, out, lse, s);
   return launch_status("dsa_sparse_attn(combine)");
+}
+
+}  // namespace
+}  // namespace dsa
+
+extern "C" dsa_status dsa_sparse_attn(const void* q, const void* k_cache, const void* v_cache,
+                                      int64_t kv_page_stride, int64_t kv_row_stride, int64_t kv_head_stride,
+                                      const int32_t* block_table, const int32_t* idx, int idx_rows, int B,
+                                      int S_q, int H_q, int H_kv, int D_qk, int D_v, int page, int max_pages,
+                                      int k, float sm_scale, float* out, float* lse, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  using namespace dsa;
+  clear_error();
+  dsa_status st = check_args("dsa_sparse_attn", q, k_cache, v_cache, kv_page_stride, kv_row_stride, kv_head_stride,
+                             block_table, idx, idx_rows, B, S_q, H_q, H_kv, D_qk, D_v, page, max_pages, k,
+                             sm_scale, out);
+  if (st != DSA_OK) return st;
+  const Plan p = make_plan(B, S_q, H_q, H_kv, D_qk, D_v, k);
+  DSA_REQUIRE(p.ws_bytes == 0 || (workspace && workspace_bytes >= p.ws_bytes), DSA_ERR_WORKSPACE,
+              "dsa_sparse_attn: workspace of %zu bytes needed, %zu given", p.ws_bytes, workspace_bytes);
+  return enqueue(p, q, k_cache, v_cache, kv_page_stride, kv_row_stride, kv_head_stride, block_table, idx, idx_rows,
+                 B, S_q, H_q, H_kv, D_qk, D_v, page, max_pages, k, sm_scale, out, lse, workspace,
+                 static_cast<hipStream_t>(stream));
 }

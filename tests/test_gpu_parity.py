@@ -245,37 +245,90 @@ def test_sparse_attn_empty_and_single():
 
 
 # ----------------------------------------------------------------------------
-# the draft block: IndexShare + KVShare on the tiny configuration
+# the draft block: IndexShare + KVShare (the tiny configuration, k > L, latent)
 # ----------------------------------------------------------------------------
+DRAFT_BLOCK_CASES = {
+    # the tiny configuration (MHA 4 x 64, k = 64 of 512)
+    "tiny": dict(lens=[512], H_I=4, D_I=32, H_q=4, H_kv=4, D_qk=64, D_v=64, k=64, latent=False, shuffle=False),
+    # k > L: -1 padding after the L kept positions, inside the one split
+    "mha_k_gt_L": dict(lens=[100, 700], H_I=64, D_I=128, H_q=16, H_kv=8, D_qk=128, D_v=128, k=512,
+                       latent=False, shuffle=True),
+    # latent MQA, k > L: two 64-token splits, the second part padding
+    "latent_k_gt_L": dict(lens=[100], H_I=64, D_I=128, H_q=64, H_kv=1, D_qk=576, D_v=512, k=128,
+                          latent=True, shuffle=True),
+    # latent MQA, two sequences: the shorter one ends with padding splits and
+    # a split that is part padding
+    "latent_two_seqs": dict(lens=[3000, 1500], H_I=64, D_I=128, H_q=64, H_kv=1, D_qk=576, D_v=512, k=2048,
+                            latent=True, shuffle=True),
+}
+
+
+def _draft_case(case, poison):
+    c = DRAFT_BLOCK_CASES[case]
+    return I.draft_inputs(0, c["lens"], H_I=c["H_I"], D_I=c["D_I"], H_q=c["H_q"], H_kv=c["H_kv"], D_qk=c["D_qk"],
+                          D_v=c["D_v"], k=c["k"], G=7, integer_indexer=True, latent=c["latent"],
+                          shuffle_pages=c["shuffle"], poison=poison, spare_page0=True)
+
+
+@pytest.mark.parametrize("case", list(DRAFT_BLOCK_CASES))
 @pytest.mark.parametrize("poison", [False, True])
-def test_draft_block_tiny(poison):
-    w = I.WORKLOADS["tiny"]
-    d = I.draft_inputs(w["seed"], w["lens"], H_I=w["H_I"], D_I=w["D_I"], H_q=w["H_q"], H_kv=w["H_kv"],
-                       D_qk=w["D_qk"], D_v=w["D_v"], k=w["k"], G=w["G"], integer_indexer=True,
-                       poison=poison)
+def test_draft_block(case, poison):
+    """Indexer -> top-k -> 7 attention steps reusing the step-1 indices.
+    Poisoned runs hold NaN in every row no target wrote: the draft slots, the
+    unused page tails and a physical page 0 that no sequence owns (the row an
+    absent token's load falls back to).  Outputs must be finite, match the
+    oracle, and equal the clean run bit for bit; idx is unchanged by the steps."""
+    log("draft block", case, "poison", poison)
+    d = _draft_case(case, poison)
     dd = DraftDev(d)
     scores = dsa.index_scores(dd.q_index, dd.w, dd.kidx, dd.bt, dd.row_len, page=d.page, ld=dd.ld)
     idx = dsa.topk(scores, dd.row_len, d.k)[:, 0]
     idx_before = idx.clone()
-    ref_idx, ref_o, ref_lse = O.draft_block(d.q_index[0, 0], d.w[0, 0], d.keys[0], d.lens[0], d.k,
-                                            d.q[:, 0], d.K[0], d.V[0], d.sm_scale)
-    np.testing.assert_array_equal(idx.cpu().numpy()[0], ref_idx)
-    assert np.all(ref_idx < d.lens[0])
     outs = []
     for j in range(d.G):
-        o, lse = dsa.sparse_attn(dd.q[j][:, None], dd.k, dd.v, dd.bt, idx, page=d.page, sm_scale=d.sm_scale)
-        o = o.cpu().numpy()[0, 0]
-        assert np.all(np.isfinite(o))
-        assert np.abs(o - ref_o[j]).max() <= ATTN_TOL
-        outs.append(o)
+        o, lse = dsa.sparse_attn(dd.q[j][:, None], dd.k, dd.v, dd.bt, idx, page=d.page, D_v=d.D_v,
+                                 sm_scale=d.sm_scale)
+        outs.append((o.cpu().numpy()[:, 0], lse.cpu().numpy()[:, 0]))
     assert torch.equal(idx, idx_before)      # steps 2..7 reuse the step-1 indices unchanged
-    if poison:
-        clean = I.draft_inputs(w["seed"], w["lens"], H_I=w["H_I"], D_I=w["D_I"], H_q=w["H_q"], H_kv=w["H_kv"],
-                               D_qk=w["D_qk"], D_v=w["D_v"], k=w["k"], G=w["G"], integer_indexer=True)
-        cd = DraftDev(clean)
+    for b in range(d.B):
+        L = int(d.lens[b])
+        ref_idx, ref_o, ref_lse = O.draft_block(d.q_index[b, 0], d.w[b, 0], d.keys[b], L, d.k,
+                                                d.q[:, b], d.K[b], d.V[b], d.sm_scale)
+        np.testing.assert_array_equal(idx.cpu().numpy()[b], ref_idx)
+        assert np.all(ref_idx < L)
         for j in range(d.G):
-            o, _ = dsa.sparse_attn(cd.q[j][:, None], cd.k, cd.v, cd.bt, idx, page=d.page, sm_scale=d.sm_scale)
-            np.testing.assert_array_equal(o.cpu().numpy()[0, 0], outs[j])
+            o, lse = outs[j]
+            assert np.all(np.isfinite(o[b])), (case, b, j)
+            assert np.abs(o[b] - ref_o[j]).max() <= ATTN_TOL
+            assert np.abs(lse[b] - ref_lse[j]).max() <= ATTN_TOL
+    if poison:
+        cd = DraftDev(_draft_case(case, False))
+        for j in range(d.G):
+            o, lse = dsa.sparse_attn(cd.q[j][:, None], cd.k, cd.v, cd.bt, idx, page=d.page, D_v=d.D_v,
+                                     sm_scale=d.sm_scale)
+            np.testing.assert_array_equal(o.cpu().numpy()[:, 0], outs[j][0])
+            np.testing.assert_array_equal(lse.cpu().numpy()[:, 0], outs[j][1])
+
+
+def test_latent_poisoned_padding_in_shuffled_splits():
+    """Latent MQA with -1 entries scattered through every split and the
+    selection in shuffled order, on a poisoned cache (NaN in the physical
+    page 0 that absent tokens fall back to): same bits as the clean cache."""
+    kw = dict(H_I=4, D_I=32, H_q=64, D_qk=576, D_v=512, k=1000, G=1, latent=True, shuffle_pages=True,
+              spare_page0=True)
+    d = I.draft_inputs(33, [1500], poison=True, **kw)
+    clean = I.draft_inputs(33, [1500], poison=False, **kw)
+    rng = np.random.default_rng(9)
+    idx = np.full((1, d.k), -1, np.int64)
+    idx[0, :700] = rng.choice(1500, 700, replace=False)
+    rng.shuffle(idx[0])
+    dd, cd = DraftDev(d), DraftDev(clean)
+    got, lse, _ = _attn_vs_oracle(d, dd, idx)
+    assert np.all(np.isfinite(got))
+    o2, l2 = dsa.sparse_attn(cd.q[0][:, None], cd.k, cd.v, cd.bt, to_dev(idx.astype(np.int32)), page=d.page,
+                             D_v=d.D_v, sm_scale=d.sm_scale)
+    np.testing.assert_array_equal(o2.cpu().numpy()[:, 0], got)
+    np.testing.assert_array_equal(l2.cpu().numpy()[:, 0], lse)
 
 
 # ----------------------------------------------------------------------------

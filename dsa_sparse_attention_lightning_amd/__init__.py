@@ -17,13 +17,14 @@ import torch
 from . import _lib
 
 __all__ = [
-    "index_scores", "topk", "sparse_attn", "spec_verify",
+    "index_scores", "topk", "sparse_attn", "sparse_attn_noalloc", "spec_verify", "NOALLOC_SCRATCH_BYTES",
     "topk_workspace_size", "sparse_attn_workspace_size", "spec_verify_workspace_size",
     "spec_verify_greedy", "spec_verify_greedy_workspace_size",
     "abi_version", "DSAError",
 ]
 
 DSAError = _lib.DSAError
+NOALLOC_SCRATCH_BYTES = _lib.NOALLOC_SCRATCH_BYTES
 
 _BF16_LIKE = (torch.bfloat16, torch.int16, torch.uint16)
 
@@ -150,17 +151,9 @@ def topk(scores, row_len, k, *, out=None, workspace=None, stream=None):
     return out
 
 
-def sparse_attn(q, k_cache, v_cache, block_table, idx, *, page, D_v=None, sm_scale=None,
-                out=None, lse=None, workspace=None, stream=None):
-    """Attention over the selected positions idx (shared by all heads).
-
-    q [B, S_q, H_q, D_qk] bf16.  k_cache [pages, page, H_kv, D_qk] bf16 and
-    v_cache [pages, page, H_kv, D_v], or a latent cache [pages, page, D_qk]
-    passed as both k_cache and v_cache (V = first D_v dims).
-    idx [B, k] or [B, S_q, k] int32 (-1 ignored).  Returns (out fp32
-    [B, S_q, H_q, D_v], lse fp32 [B, S_q, H_q]).
-    """
-    lib = _lib.load()
+def _attn_args(q, k_cache, v_cache, block_table, idx, page, D_v, sm_scale, out, lse):
+    """Checks and marshals the arguments shared by sparse_attn and
+    sparse_attn_noalloc; returns (C arguments before out, out, lse, shape)."""
     _dev(q, "q", _BF16_LIKE)
     _dev(k_cache, "k_cache", _BF16_LIKE)
     _dev(v_cache, "v_cache", _BF16_LIKE)
@@ -199,13 +192,42 @@ def sparse_attn(q, k_cache, v_cache, block_table, idx, *, page, D_v=None, sm_sca
     _dev(lse, "lse", (torch.float32,))
     _need(out.shape == (B, S_q, H_q, D_v), "out must be [B, S_q, H_q, D_v]")
     _need(lse.shape == (B, S_q, H_q), "lse must be [B, S_q, H_q]")
-    nbytes = int(lib.dsa_sparse_attn_workspace_size(B, S_q, H_q, H_kv, D_qk, D_v, k))
+    cargs = (_ptr(q), _ptr(k_cache), _ptr(v_cache), strides[0], strides[1], strides[2], _ptr(block_table),
+             _ptr(idx), idx_rows, B, S_q, H_q, H_kv, D_qk, D_v, page, block_table.shape[1], k, float(sm_scale),
+             _ptr(out), _ptr(lse))
+    return cargs, out, lse, (B, S_q, H_q, H_kv, D_qk, D_v, k)
+
+
+def sparse_attn(q, k_cache, v_cache, block_table, idx, *, page, D_v=None, sm_scale=None,
+                out=None, lse=None, workspace=None, stream=None):
+    """Attention over the selected positions idx (shared by all heads).
+
+    q [B, S_q, H_q, D_qk] bf16.  k_cache [pages, page, H_kv, D_qk] bf16 and
+    v_cache [pages, page, H_kv, D_v], or a latent cache [pages, page, D_qk]
+    passed as both k_cache and v_cache (V = first D_v dims).
+    idx [B, k] or [B, S_q, k] int32 (-1 ignored).  Returns (out fp32
+    [B, S_q, H_q, D_v], lse fp32 [B, S_q, H_q]).
+    """
+    lib = _lib.load()
+    cargs, out, lse, shape = _attn_args(q, k_cache, v_cache, block_table, idx, page, D_v, sm_scale, out, lse)
+    nbytes = int(lib.dsa_sparse_attn_workspace_size(*shape))
     ws = _workspace(nbytes, q.device, workspace)
-    st = lib.dsa_sparse_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), strides[0], strides[1], strides[2],
-                             _ptr(block_table), _ptr(idx), idx_rows, B, S_q, H_q, H_kv, D_qk, D_v,
-                             page, block_table.shape[1], k, float(sm_scale), _ptr(out), _ptr(lse),
-                             _ptr(ws), nbytes, _stream(stream))
+    st = lib.dsa_sparse_attn(*cargs, _ptr(ws), nbytes, _stream(stream))
     _lib.check("dsa_sparse_attn", st)
+    return out, lse
+
+
+def sparse_attn_noalloc(q, k_cache, v_cache, block_table, idx, *, page, D_v=None, sm_scale=None,
+                        out, lse, stream=None):
+    """sparse_attn for callers that cannot allocate: out and lse are the
+    caller's, and the split-k partials go to the library's fixed per-GPU
+    scratch of NOALLOC_SCRATCH_BYTES (shapes needing more are refused).
+    Calls that may overlap on one GPU race on that scratch."""
+    lib = _lib.load()
+    _need(out is not None and lse is not None, "sparse_attn_noalloc takes caller-allocated out and lse")
+    cargs, out, lse, _ = _attn_args(q, k_cache, v_cache, block_table, idx, page, D_v, sm_scale, out, lse)
+    st = lib.dsa_sparse_attn_noalloc(*cargs, _stream(stream))
+    _lib.check("dsa_sparse_attn_noalloc", st)
     return out, lse
 
 

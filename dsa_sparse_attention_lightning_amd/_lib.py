@@ -17,6 +17,7 @@ c_int, c_int64, c_size_t, c_uint64, c_float = (
 c_void_p, c_char_p = ctypes.c_void_p, ctypes.c_char_p
 
 DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP = range(5)
+NOALLOC_SCRATCH_BYTES = 16 << 20          # DSA_NOALLOC_SCRATCH_BYTES of include/dsa.h
 
 # name -> (restype, argtypes); the order follows include/dsa.h
 SIGNATURES = {
@@ -33,6 +34,10 @@ SIGNATURES = {
                                 c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int, c_int,
                                 c_int, c_int, c_int, c_int, c_float, c_void_p, c_void_p,
                                 c_void_p, c_size_t, c_void_p]),
+    "dsa_sparse_attn_noalloc": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_int64, c_int64,
+                                        c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int, c_int,
+                                        c_int, c_int, c_int, c_int, c_float, c_void_p, c_void_p,
+                                        c_void_p]),
     "spec_verify_workspace_size": (c_size_t, [c_int, c_int, c_int]),
     "spec_verify": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_void_p,
                             c_uint64, c_uint64, c_void_p, c_void_p, c_void_p, c_void_p,

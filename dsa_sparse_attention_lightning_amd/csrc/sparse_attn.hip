@@ -19,6 +19,7 @@
 // same gathered rows, so QK^T and PV are dense contractions over the heads and
 // run on bf16 MFMA (see latent_attn_kernel).
 #include <cmath>
+#include <mutex>
 
 #include "dsa_common.h"
 
@@ -689,6 +690,16 @@ extern "C" size_t dsa_sparse_attn_workspace_size(int B, int S_q, int H_q, int H_
   return dsa::make_plan(B, S_q, H_q, H_kv, D_qk, D_v, k).ws_bytes;
 }
 
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free entry point: the split-k partials live in a
+// file-scope device array instead of a caller workspace.  Each GPU the
+// library runs on holds its own copy until the process ends.  In host code
+// `scratch` names a host-side stand-in, not device memory: its device address
+// is looked up once per device (hipGetSymbolAddress, with that device
+// current) and only that address is ever passed to kernels.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[DSA_NOALLOC_SCRATCH_BYTES];
+
 namespace dsa {
 namespace {
 
@@ -784,6 +795,31 @@ dsa_status enqueue(const Plan& p, const void* q, const void* k_cache, const void
   return launch_status("dsa_sparse_attn(combine)");
 }
 
+constexpr size_t kScratchBytes = DSA_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+dsa_status scratch_on_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  DSA_REQUIRE(e == hipSuccess, DSA_ERR_HIP, "dsa_sparse_attn_noalloc: hipGetDevice failed: %s",
+              hipGetErrorString(e));
+  DSA_REQUIRE(dev >= 0 && dev < kMaxDevices, DSA_ERR_UNSUPPORTED,
+              "dsa_sparse_attn_noalloc: device %d beyond the %d devices supported", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    DSA_REQUIRE(e == hipSuccess && ptr, DSA_ERR_HIP,
+                "dsa_sparse_attn_noalloc: hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return DSA_OK;
+}
+
 }  // namespace
 }  // namespace dsa
 
@@ -804,5 +840,32 @@ extern "C" dsa_status dsa_sparse_attn(const void* q, const void* k_cache, const 
               "dsa_sparse_attn: workspace of %zu bytes needed, %zu given", p.ws_bytes, workspace_bytes);
   return enqueue(p, q, k_cache, v_cache, kv_page_stride, kv_row_stride, kv_head_stride, block_table, idx, idx_rows,
                  B, S_q, H_q, H_kv, D_qk, D_v, page, max_pages, k, sm_scale, out, lse, workspace,
+                 static_cast<hipStream_t>(stream));
+}
+
+extern "C" dsa_status dsa_sparse_attn_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                              int64_t kv_page_stride, int64_t kv_row_stride,
+                                              int64_t kv_head_stride, const int32_t* block_table,
+                                              const int32_t* idx, int idx_rows, int B, int S_q, int H_q,
+                                              int H_kv, int D_qk, int D_v, int page, int max_pages, int k,
+                                              float sm_scale, float* out, float* lse, void* stream) {
+  using namespace dsa;
+  clear_error();
+  dsa_status st = check_args("dsa_sparse_attn_noalloc", q, k_cache, v_cache, kv_page_stride, kv_row_stride,
+                             kv_head_stride, block_table, idx, idx_rows, B, S_q, H_q, H_kv, D_qk, D_v, page,
+                             max_pages, k, sm_scale, out);
+  if (st != DSA_OK) return st;
+  const Plan p = make_plan(B, S_q, H_q, H_kv, D_qk, D_v, k);
+  DSA_REQUIRE(p.ws_bytes <= kScratchBytes, DSA_ERR_UNSUPPORTED,
+              "dsa_sparse_attn_noalloc: this call needs %zu bytes of split-k scratch, more than the %zu bytes "
+              "the allocation-free entry point holds (call dsa_sparse_attn with a workspace instead)",
+              p.ws_bytes, kScratchBytes);
+  void* ws = nullptr;
+  if (p.ws_bytes > 0) {
+    st = scratch_on_current_device(&ws);
+    if (st != DSA_OK) return st;
+  }
+  return enqueue(p, q, k_cache, v_cache, kv_page_stride, kv_row_stride, kv_head_stride, block_table, idx, idx_rows,
+                 B, S_q, H_q, H_kv, D_qk, D_v, page, max_pages, k, sm_scale, out, lse, ws,
                  static_cast<hipStream_t>(stream));
 }

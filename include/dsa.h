@@ -148,6 +148,34 @@ dsa_status dsa_sparse_attn(const void* q, const void* k_cache, const void* v_cac
                            void* stream);
 
 /*
+ * dsa_sparse_attn_noalloc -- dsa_sparse_attn without a workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  Same
+ * arguments, semantics, kernels and output bits as dsa_sparse_attn with
+ * the same shapes; the split-k partials go to a file-scope device array of
+ * DSA_NOALLOC_SCRATCH_BYTES bytes instead, one per GPU (the calling
+ * thread's current device; `stream` must belong to it), held until the
+ * process ends.  The call allocates and frees nothing.
+ *   - A call whose split-k partials need more than DSA_NOALLOC_SCRATCH_BYTES
+ *     (dsa_sparse_attn_workspace_size() of its shape) returns
+ *     DSA_ERR_UNSUPPORTED and enqueues nothing.
+ *   - Every call on a GPU shares that GPU's array: calls that may overlap
+ *     on one GPU (different streams without ordering between them) race and
+ *     give undefined results.  Nothing in the array needs to start at zero
+ *     (every partial a call reads was written by that call).
+ *   - The first call on a device looks up the array's device address
+ *     (DSA_ERR_HIP if that fails).
+ */
+#define DSA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+dsa_status dsa_sparse_attn_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                   int64_t kv_page_stride, int64_t kv_row_stride,
+                                   int64_t kv_head_stride, const int32_t* block_table,
+                                   const int32_t* idx, int idx_rows, int B, int S_q,
+                                   int H_q, int H_kv, int D_qk, int D_v, int page,
+                                   int max_pages, int k, float sm_scale, float* out,
+                                   float* lse, void* stream);
+
+/*
  * spec_verify -- rejection-sampling verification of drafted chains
  * (section "Rejection sampling and a loss that optimizes acceptance
  * directly": drafts sampled from q are accepted or rejected against p, which

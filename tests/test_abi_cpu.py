@@ -137,3 +137,30 @@ def test_binding_fails_loudly_without_library(tmp_path):
             _lib.load(str(tmp_path / "missing.so"))
         finally:
             _lib._lib = _lib._lib_backup
+
+
+def _noalloc_call(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, ps=64 * 64 * 128, rs=64 * 128, hs=128, bt=FAKE, idx=FAKE, idx_rows=1,
+             B=1, S_q=1, H_q=64, H_kv=64, D_qk=128, D_v=128, page=64, max_pages=4, kk=2048, scale=0.1,
+             out=FAKE, lse=None)
+    a.update(over)
+    return lib.dsa_sparse_attn_noalloc(a["q"], a["k"], a["v"], a["ps"], a["rs"], a["hs"], a["bt"], a["idx"],
+                                       a["idx_rows"], a["B"], a["S_q"], a["H_q"], a["H_kv"], a["D_qk"], a["D_v"],
+                                       a["page"], a["max_pages"], a["kk"], a["scale"], a["out"], a["lse"], None)
+
+
+def test_sparse_attn_noalloc_validation():
+    """The allocation-free entry point checks its arguments like
+    dsa_sparse_attn, and refuses shapes whose split-k partials exceed its
+    fixed scratch, all before any HIP call."""
+    text = open(HEADER).read()
+    m = re.search(r"#define DSA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == _lib.NOALLOC_SCRATCH_BYTES
+    assert _noalloc_call(q=None) == _lib.DSA_ERR_INVALID_ARG
+    assert _noalloc_call(H_q=63) == _lib.DSA_ERR_INVALID_ARG
+    assert _noalloc_call(D_qk=96, D_v=96) == _lib.DSA_ERR_UNSUPPORTED
+    assert _noalloc_call(out=MISALIGNED) == _lib.DSA_ERR_INVALID_ARG
+    need = lib.dsa_sparse_attn_workspace_size(1, 8, 64, 64, 128, 128, 131072)
+    assert need > _lib.NOALLOC_SCRATCH_BYTES
+    assert _noalloc_call(S_q=8, kk=131072) == _lib.DSA_ERR_UNSUPPORTED
+    assert b"scratch" in lib.dsa_last_error()

@@ -1,7 +1,8 @@
-"""Builds libdsa.so (all HIP sources, gfx950) in-tree with hipcc.
+"""Builds libdsa.so (all HIP sources of the path, gfx950) and the
+benchmark's measurement probe libdsa_bench.so in-tree with hipcc.
 
 Every call recompiles.  Objects go to _build/ next to this file; the shared
-library lands beside this file, where the binding loads it.
+libraries land beside this file, where the binding (and bench.py) load them.
 """
 
 from __future__ import annotations
@@ -17,8 +18,10 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdsa.so")
+BENCH_LIB = os.path.join(HERE, "libdsa_bench.so")
 ARCH = "gfx950"
 SOURCES = ["abi.hip", "index_scores.hip", "topk.hip", "sparse_attn.hip", "spec_verify.hip"]
+BENCH_SOURCES = ["bench_peak.hip"]
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC",
@@ -50,18 +53,24 @@ def _run(cmd, verbose):
 def build(verbose: bool = False, jobs: int | None = None) -> str:
     hipcc = _hipcc()
     os.makedirs(BUILD, exist_ok=True)
-    objs = []
     cmds = []
-    for src in SOURCES:
-        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-        objs.append(obj)
-        cmds.append([hipcc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+
+    def objs_of(sources):
+        out = []
+        for src in sources:
+            obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+            out.append(obj)
+            cmds.append([hipcc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        return out
+
+    lib_objs, bench_objs = objs_of(SOURCES), objs_of(BENCH_SOURCES)
     jobs = jobs or min(len(cmds), max(1, (os.cpu_count() or 4)))
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
-    tmp = LIB + ".tmp"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
-    os.replace(tmp, LIB)
+    for target, objs in ((LIB, lib_objs), (BENCH_LIB, bench_objs)):
+        tmp = target + ".tmp"
+        _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
+        os.replace(tmp, target)
     return LIB
 
 

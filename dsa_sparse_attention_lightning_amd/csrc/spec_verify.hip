@@ -153,16 +153,17 @@ __global__ __launch_bounds__(kStatThreads) void verify_stats_kernel(VerifyArgs a
     for (int u = 0; u < kStatU; ++u) bm = fmaxf(bm, fmaxf(fmaxf(x[u].x, x[u].y), fmaxf(x[u].z, x[u].w)));
     const float M = fmaxf(m, bm);
     if (M == -INFINITY) continue;   // nothing but -inf logits so far
-    const float ML = M * kLog2e;
+    // exp(x - M) as 2^((x - M) log2 e): the difference is formed first, so
+    // the largest terms (x near M) carry no rounding from the scaling
     float t = 0.f;
 #pragma unroll
     for (int u = 0; u < kStatU; ++u) {
-      t += fast_exp2(x[u].x * kLog2e - ML);
-      t += fast_exp2(x[u].y * kLog2e - ML);
-      t += fast_exp2(x[u].z * kLog2e - ML);
-      t += fast_exp2(x[u].w * kLog2e - ML);
+      t += fast_exp2((x[u].x - M) * kLog2e);
+      t += fast_exp2((x[u].y - M) * kLog2e);
+      t += fast_exp2((x[u].z - M) * kLog2e);
+      t += fast_exp2((x[u].w - M) * kLog2e);
     }
-    s = s * fast_exp2(m * kLog2e - ML) + t;
+    s = s * fast_exp2((m - M) * kLog2e) + t;
     m = M;
   }
 #pragma unroll
@@ -524,7 +525,9 @@ __global__ __launch_bounds__(kPickThreads) void verify_pick_kernel(VerifyArgs a,
     if (lane == 0) {
       s_W = sum;
       s_tile_pick = c < 0 ? 0 : c;
-      s_x = dd.us * sum - before;
+      // no crossing (rounding put u * W at or past the scanned total): +inf
+      // makes the tile and token levels take their last positive entry too
+      s_x = before == INFINITY ? INFINITY : dd.us * sum - before;
     }
   }
   __syncthreads();
@@ -560,7 +563,7 @@ __global__ __launch_bounds__(kPickThreads) void verify_pick_kernel(VerifyArgs a,
     const int t = wave_first_crossing(s_tile, t1 - t0, x, &before);
     if (lane == 0) {
       s_tile_pick = t < 0 ? -1 : t0 + t;
-      s_x = x - before;
+      s_x = before == INFINITY ? INFINITY : x - before;
     }
   }
   __syncthreads();

@@ -224,7 +224,7 @@ def _verify_all(v, B, G):
     tl_all = v.target_logits.cpu().numpy()
     dl_all = v.draft_logits.cpu().numpy()
     dr_all = v.drafts.cpu().numpy()
-    near, min_margin = 0, np.inf
+    near, min_margin = [], np.inf
     for b in range(B):
         r = O.spec_verify_seq(tl_all[b], dl_all[b], dr_all[b], ua[b], us[b])
         taken = r["accept_margin"][: min(r["n"], G - 1) + 1]
@@ -232,12 +232,13 @@ def _verify_all(v, B, G):
         if r["n"] != n_gpu[b]:
             jj = min(r["n"], n_gpu[b])
             assert r["accept_margin"][jj] < 1e-5, (b, r["n"], n_gpu[b])
-            near += 1
+            near.append((b, "decision", jj, float(r["accept_margin"][jj])))
             continue
         np.testing.assert_array_equal(em_gpu[b, : n_gpu[b]], dr_all[b, : n_gpu[b]])
         if em_gpu[b, n_gpu[b]] != r["emitted"][n_gpu[b]]:
             assert r["sample_margin"] < 1e-5, (b, em_gpu[b, n_gpu[b]], r["emitted"][n_gpu[b]])
-            near += 1
+            near.append((b, "draw", int(em_gpu[b, n_gpu[b]]) - int(r["emitted"][n_gpu[b]]),
+                         float(r["sample_margin"])))
         assert np.all(em_gpu[b, n_gpu[b] + 1:] == -1)
     return n_gpu, near, min_margin
 
@@ -249,9 +250,11 @@ def test_verify_256x8x151552(std):
     seed = {0.5: 4, 2.0: 5, 6.0: 6}[std]
     v = DI.verify_inputs(seed, B, G, V, std, offset=11)
     n, near, min_margin = _verify_all(v, B, G)
-    log(f"verify std {std}: mean accepted {n.mean():.3f}, differing near-margin cases {near}, "
-        f"smallest float64 margin of any decision or draw {min_margin:.2e}")
-    assert near <= 2
+    log(f"verify std {std}: mean accepted {n.mean():.3f}, differing near-margin cases {len(near)} "
+        f"(sequence, kind, position or token offset, float64 margin): {near}; smallest float64 margin of any "
+        f"decision or draw {min_margin:.2e}")
+    # at most one differing near-margin case per 64 sequences
+    assert len(near) <= B // 64
 
 
 def test_greedy_verify_256x8x151552():

@@ -425,6 +425,32 @@ def test_spec_verify_special_cases():
     assert np.all(n == 0) and np.all(em[:, 0] < V // 2)
 
 
+@pytest.mark.parametrize("V", [2048, 5003, 151552])
+def test_spec_verify_draw_at_the_top_of_the_cdf(V):
+    """u_smp = 1 - 2^-24 puts u * W within rounding of the total residual
+    mass W, where the crossing search may find no crossing and must fall back
+    to the last positive entry at every level.  The residual is positive only
+    in the last 768 tokens (the tiles before them have zero mass) and the
+    last token holds 1/768 of W, so the oracle's draw is the last token."""
+    B, G = 4, 7
+    tl = np.zeros((B, G + 1, V), np.float32)
+    tl[..., V - 768:] = 2.0
+    dl = np.full((B, G, V), 2.0, np.float32)
+    dl[..., V - 768:] = 0.0
+    dr = np.full((B, G), 5, np.int32)                 # q(5) > p(5): rejected at j = 0 with u_acc = 0.999
+    uni = np.zeros((B, G + 1, 2), np.float32)
+    uni[..., 0] = 0.999
+    uni[..., 1] = np.float32(1.0 - 2.0**-24)
+    uni[1, :, 0] = 0.0                                # sequence 1 accepts everything: bonus draw from p
+    dr[1] = V - 1
+    n, em = dsa.spec_verify(to_dev(tl), to_dev(dl), to_dev(dr), uniforms=to_dev(uni))
+    ref_n, ref_em, _ = O.spec_verify(tl, dl, dr, uni[:, :G, 0], uni[:, :, 1])
+    n, em = n.cpu().numpy(), em.cpu().numpy()
+    np.testing.assert_array_equal(n, ref_n)
+    np.testing.assert_array_equal(em, ref_em)
+    assert ref_em[0, 0] == V - 1 and np.all(em[np.arange(B), n] >= 0)
+
+
 @pytest.mark.parametrize("std", [0.5, 2.0])
 def test_spec_verify_block16(std):
     """Block-16 layout: G = 15 drafts plus the bonus position."""

@@ -260,8 +260,8 @@ def measure_peaks(reps=10):
     flops = blocks * 4 * iters * 4 * 2 * 32 * 32 * 16
     peaks["mfma_bf16_TFLOPs"] = flops / time_warm(mfma, reps=reps, inner=1) / 1e6
     peaks["probes"] = ("libdsa_bench.so: 2 GiB stream, 16-byte non-temporal loads (copy: and stores), 2048 "
-                       "workgroups each on a contiguous chunk; register-only v_mfma_f32_32x32x16_bf16 loop, "
-                       "4 chains per wave, 8 waves per CU")
+                       "workgroups each on a contiguous chunk; register-only v_mfma_f32_32x32x16_bf16 loop on "
+                       "pseudo-random full-mantissa bf16 operands, 4 chains per wave, 8 waves per CU")
     torch.cuda.empty_cache()
     return peaks
 

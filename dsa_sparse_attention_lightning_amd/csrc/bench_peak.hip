@@ -1,8 +1,8 @@
 // Measurement probes for the benchmark (libdsa_bench.so; not part of the
 // draft-and-verify path and not linked into libdsa.so):
-//   * the dense bf16 MFMA rate this chip sustains, from a register-only loop
-//     of v_mfma_f32_32x32x16_bf16 with four independent accumulation chains
-//     per wave and no memory traffic inside the loop;
+//   * the dense bf16 MFMA rate this chip sustains on full-mantissa operands,
+//     from a register-only loop of v_mfma_f32_32x32x16_bf16 with four
+//     independent accumulation chains per wave and no memory traffic;
 //   * the HBM read and copy bandwidth it sustains: every workgroup streams
 //     its own contiguous chunk with 16-byte non-temporal loads (and stores).
 // The benchmark reports each kernel's rate against these measured peaks next
@@ -17,20 +17,32 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 
 constexpr int kThreads = 256;   // four waves, one per SIMD
 
+__device__ __forceinline__ uint32_t mix(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x7feb352du;
+  x ^= x >> 15;
+  x *= 0x846ca68bu;
+  x ^= x >> 16;
+  return x;
+}
+
+// Operands are pseudo-random bf16 values with full mantissas (the chip's
+// sustained MFMA clock depends on the data; small integers run faster than
+// the normal-distributed values the kernels see).
 __global__ __launch_bounds__(kThreads) void mfma_peak_kernel(float* __restrict__ out, int iters) {
-  // operands depend on the thread so the compiler cannot fold the loop
   bf16x8_t a, b;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    a[e] = (__bf16)(float)((threadIdx.x + e) & 7);
-    b[e] = (__bf16)(float)((threadIdx.x * 3 + e) & 7);
+    const uint32_t h = mix(threadIdx.x * 131u + blockIdx.x * 7919u + e * 17u);
+    a[e] = (__bf16)(((float)(h & 0xffffu) / 32768.f - 1.f) * 1.7f);
+    b[e] = (__bf16)(((float)(h >> 16) / 32768.f - 1.f) * 1.3f);
   }
   f32x16_t c0 = {}, c1 = {}, c2 = {}, c3 = {};
   for (int i = 0; i < iters; ++i) {
     c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
-    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, c1, 0, 0, 0);
     c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
-    c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, c3, 0, 0, 0);
   }
   float s = 0.f;
 #pragma unroll

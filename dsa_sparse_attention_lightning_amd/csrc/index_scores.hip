@@ -366,8 +366,10 @@ __global__ __launch_bounds__(NWAVE * 64) __attribute__((amdgpu_waves_per_eu(DSA_
 
 // Five to eight rows: eight waves, one query row each (Q fragments 64 VGPRs,
 // head weights 32, two accumulator sets 64), two waves per SIMD.  Key tiles
-// are staged in LDS four at a time (128 positions per barrier, two stages in
-// flight in registers), and each wave software-pipelines its tiles: the
+// are staged in LDS four at a time (128 positions per barrier; the next
+// stage's loads are in flight in registers while the current one is used:
+// one stage ahead measured 2 % faster than two, with 24 fewer VGPRs), and
+// each wave software-pipelines its tiles: the
 // MFMAs of tile i issue while its VALU runs the epilogue of tile i-1 out of
 // the other accumulator set, with the weights in registers (no LDS access in
 // the epilogue).  Same arithmetic, in the same order, as
@@ -375,8 +377,15 @@ __global__ __launch_bounds__(NWAVE * 64) __attribute__((amdgpu_waves_per_eu(DSA_
 #ifndef DSA_INDEX_SUPER_WGS
 #define DSA_INDEX_SUPER_WGS 256
 #endif
-constexpr int kSuperTiles = 4;                        // 32-position tiles per LDS stage
-constexpr int kSuperPos = kSuperTiles * kRowsTile;    // 128 positions
+#ifndef DSA_INDEX_SUPER_TILES
+#define DSA_INDEX_SUPER_TILES 4
+#endif
+constexpr int kSuperTiles = DSA_INDEX_SUPER_TILES;    // 32-position tiles per LDS stage (even)
+constexpr int kSuperPos = kSuperTiles * kRowsTile;    // positions per stage
+#ifndef DSA_INDEX_SUPER_PF
+#define DSA_INDEX_SUPER_PF 1
+#endif
+constexpr int kSuperPF = DSA_INDEX_SUPER_PF;          // stages in flight in registers (1 or 2)
 constexpr int kSuperThreads = 512;
 
 template <int KS16>
@@ -395,9 +404,10 @@ __global__ __launch_bounds__(kSuperThreads) __attribute__((amdgpu_waves_per_eu(2
   constexpr int KROW = D * 2 + 16;                     // padded LDS row (bytes)
   constexpr int CHUNKS = kSuperPos * D / 8;            // 16-byte pieces per stage
   static_assert(CHUNKS % NT == 0, "stage pieces must divide evenly");
+  static_assert(kSuperTiles == 2 || kSuperTiles == 4 || kSuperTiles == 8, "2, 4 or 8 tiles per stage");
   constexpr int PER = CHUNKS / NT;
   constexpr int EPS = 16 / KS16;                       // epilogue elements per MFMA slot
-  constexpr int PF = 2;                                // stages in flight
+  constexpr int PF = kSuperPF;                         // stages in flight
   extern __shared__ __align__(16) unsigned char s_k[];   // [2][kSuperPos][KROW]
   __shared__ int s_row[kMaxChunkPositions];
 
@@ -527,25 +537,41 @@ __global__ __launch_bounds__(kSuperThreads) __attribute__((amdgpu_waves_per_eu(2
     if constexpr (decltype(first)::value) tile(no_prev{}, std::integral_constant<int, 0>{}, bbase, g, accA, accB);
     else tile(with_prev{}, std::integral_constant<int, 0>{}, bbase, g, accA, accB);
     tile(with_prev{}, std::integral_constant<int, 1>{}, bbase, g + 1, accB, accA);
-    tile(with_prev{}, std::integral_constant<int, 2>{}, bbase, g + 2, accA, accB);
-    tile(with_prev{}, std::integral_constant<int, 3>{}, bbase, g + 3, accB, accA);
+    if constexpr (kSuperTiles >= 4) {
+      tile(with_prev{}, std::integral_constant<int, 2>{}, bbase, g + 2, accA, accB);
+      tile(with_prev{}, std::integral_constant<int, 3>{}, bbase, g + 3, accB, accA);
+    }
+    if constexpr (kSuperTiles >= 8) {
+      tile(with_prev{}, std::integral_constant<int, 4>{}, bbase, g + 4, accA, accB);
+      tile(with_prev{}, std::integral_constant<int, 5>{}, bbase, g + 5, accB, accA);
+      tile(with_prev{}, std::integral_constant<int, 6>{}, bbase, g + 6, accA, accB);
+      tile(with_prev{}, std::integral_constant<int, 7>{}, bbase, g + 7, accB, accA);
+    }
     return next;
   };
   using first_stage = std::integral_constant<bool, true>;
   using later_stage = std::integral_constant<bool, false>;
   const int n_st = (t_end - t_begin + kSuperPos - 1) / kSuperPos;
-  read_rows(0);
-  Slot pre0 = fetch();
-  read_rows(1);
-  Slot pre1 = fetch();
-  read_rows(2);
-  pre0 = step(first_stage{}, pre0, 0);
-  int st = 1;
-  for (; st + 2 <= n_st; st += 2) {   // whole rounds (stage st in slot st % 2)
-    pre1 = step(later_stage{}, pre1, st);
-    pre0 = step(later_stage{}, pre0, st + 1);
+  if constexpr (PF == 1) {
+    read_rows(0);
+    Slot pre = fetch();
+    read_rows(1);
+    pre = step(first_stage{}, pre, 0);
+    for (int st = 1; st < n_st; ++st) pre = step(later_stage{}, pre, st);
+  } else {
+    read_rows(0);
+    Slot pre0 = fetch();
+    read_rows(1);
+    Slot pre1 = fetch();
+    read_rows(2);
+    pre0 = step(first_stage{}, pre0, 0);
+    int st = 1;
+    for (; st + 2 <= n_st; st += 2) {   // whole rounds (stage st in slot st % 2)
+      pre1 = step(later_stage{}, pre1, st);
+      pre0 = step(later_stage{}, pre0, st + 1);
+    }
+    if (st < n_st) step(later_stage{}, pre1, st);
   }
-  if (st < n_st) step(later_stage{}, pre1, st);
   // the last tile (odd index) is still in set B
   float p = 0.f;
 #pragma unroll

@@ -164,3 +164,36 @@ def test_sparse_attn_noalloc_validation():
     assert need > _lib.NOALLOC_SCRATCH_BYTES
     assert _noalloc_call(S_q=8, kk=131072) == _lib.DSA_ERR_UNSUPPORTED
     assert b"scratch" in lib.dsa_last_error()
+
+
+def _params(fn):
+    """Parameter list of `fn` as declared in include/dsa.h (comments removed)."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    m = re.search(r"\b" + fn + r"\s*\(([^)]*)\)", text)
+    assert m, fn
+    return [p.strip() for p in m.group(1).replace("\n", " ").split(",") if p.strip() and p.strip() != "void"]
+
+
+def test_boundary_departures_are_the_recorded_ones():
+    """Where the exported signatures differ from the boundary sketched for
+    the four calls (status/version helpers, index_scores, topk, sparse_attn
+    and spec_verify), each difference is deliberate and listed in the
+    design notes; this pins every one of them."""
+    assert _params("dsa_status_str") == ["int status"]                       # int, not the enum type
+    idx = _params("dsa_index_scores")
+    assert idx[-2:] == ["int64_t ld", "void* stream"]                         # 64-bit ld, stream as void*
+    assert _params("dsa_topk_workspace_size") == ["int B", "int R", "int64_t ld", "int k"]
+    ws = _params("dsa_sparse_attn_workspace_size")
+    assert ws == ["int B", "int S_q", "int H_q", "int H_kv", "int D_qk", "int D_v", "int k"]   # + H_kv, D_qk
+    attn = _params("dsa_sparse_attn")
+    assert attn[7:9] == ["const int32_t* idx", "int idx_rows"]               # per-row index sets
+    sv = _params("spec_verify")
+    assert "const float* uniforms" in sv and sv.index("const float* uniforms") == 6   # caller-supplied uniforms
+    assert "float* diag" in sv
+    text = open(HEADER).read()
+    assert "diag          fp32 [B, G+1, 4]" in text                          # p, q, u_acc, u_smp per position
+    assert "D_I in {32, 64, 128}" in text
+    # entry points beyond the four calls and their helpers
+    for extra in ("dsa_last_error", "spec_verify_greedy", "spec_verify_greedy_workspace_size",
+                  "dsa_sparse_attn_noalloc"):
+        assert extra in declared_functions()

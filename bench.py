@@ -424,8 +424,10 @@ def main():
     Bv, Gv, V = v.draft_logits.shape
     ver_bytes = Bv * (2 * Gv + 1) * V * 4
     value = G * L_total / (ms_per_step * 1e-3)
+    split = dsa.sparse_attn_workspace_size(d.B, 1, d.H_q, d.H_kv, d.D_qk, d.D_v, d.k) > 0
     roofline = {
-        "bound": "hbm", "kernel": "dsa_sparse_attn call (mha_attn_kernel + split-k combine_kernel)",
+        "bound": "hbm",
+        "kernel": "dsa_sparse_attn call (mha_attn_kernel" + (" + split-k combine_kernel)" if split else ")"),
         "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
         "traffic": measured_traffic(),
         "traffic_source": os.path.relpath(TRAFFIC_PROFILE, ROOT) + " (FETCH_SIZE x2.0 + WRITE_SIZE x1.0 per call, "

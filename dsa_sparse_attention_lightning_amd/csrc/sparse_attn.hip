@@ -37,11 +37,17 @@ constexpr int kThreads = kWaves * 64;
 #ifndef DSA_ATTN_TARGET_WGS
 #define DSA_ATTN_TARGET_WGS 1024
 #endif
+#ifndef DSA_ATTN_TARGET_WGS_STREAM
+#define DSA_ATTN_TARGET_WGS_STREAM 256
+#endif
 #ifndef DSA_ATTN_MIN_TOKENS
 #define DSA_ATTN_MIN_TOKENS 256
 #endif
 #ifndef DSA_ATTN_UNROLL
 #define DSA_ATTN_UNROLL 2
+#endif
+#ifndef DSA_ATTN_UNROLL_NT
+#define DSA_ATTN_UNROLL_NT 4
 #endif
 
 struct AttnArgs {
@@ -630,6 +636,13 @@ bool is_latent(int H_q, int H_kv, int D_qk, int D_v) {
   return H_kv == 1 && D_qk == kLatD && D_v == kLatDv && H_q == 64;
 }
 
+// One query row per sequence and a per-head-KV gather larger than the
+// last-level cache: the KV rows are streamed with non-temporal loads (no
+// draft step re-reads them from that cache).
+bool streams_kv(int B, int S_q, int H_kv, int D, int k) {
+  return S_q == 1 && (double)B * k * H_kv * D * 2 * 2 > (double)kAttnStreamBytes;
+}
+
 Plan make_plan(int B, int S_q, int H_q, int H_kv, int D_qk, int D_v, int k) {
   Plan p{};
   const bool latent = is_latent(H_q, H_kv, D_qk, D_v);
@@ -638,7 +651,11 @@ Plan make_plan(int B, int S_q, int H_q, int H_kv, int D_qk, int D_v, int k) {
   const long long base = (long long)B * S_q * p.head_groups;
   const int min_tok = latent ? DSA_LAT_MIN_TOKENS : DSA_ATTN_MIN_TOKENS;
   const int max_split = latent ? kLatentMaxSplits : kCombineMaxSplits;
-  int ns = (int)((DSA_ATTN_TARGET_WGS + base - 1) / base);
+  // a streamed gather keeps every CU busy with one workgroup per (sequence,
+  // head group) once there are about 256 of them: no split, no combine
+  const long long target = (!latent && streams_kv(B, S_q, H_kv, D_qk, k)) ? DSA_ATTN_TARGET_WGS_STREAM
+                                                                         : DSA_ATTN_TARGET_WGS;
+  int ns = (int)((target + base - 1) / base);
   const int max_ns = (k + min_tok - 1) / min_tok;
   if (ns > max_ns) ns = max_ns;
   const int min_ns = (k + kMaxTokPerSplit - 1) / kMaxTokPerSplit;
@@ -671,11 +688,11 @@ void launch_mha(AttnArgs a, const Plan& p, int B, hipStream_t s) {
     a.row_grouped = 0;
     dim3 grid(p.nsplit, p.head_groups, B * a.S_q);
     // one query row per sequence: a gather larger than the last-level cache
-    // streams (non-temporal loads); smaller ones stay cacheable, since the
-    // draft steps that share the index set re-read the same rows
-    const double bytes = (double)B * a.k * a.H_kv * D * 2 * 2;
-    if (bytes > (double)kAttnStreamBytes)
-      hipLaunchKernelGGL((mha_attn_kernel<D, GQ, DSA_ATTN_UNROLL, true>), grid, dim3(kThreads), 0, s, a);
+    // streams (non-temporal loads, four tokens per stage, about 256
+    // workgroups); smaller ones stay cacheable, since the draft steps that
+    // share the index set re-read the same rows
+    if (streams_kv(B, a.S_q, a.H_kv, D, a.k))
+      hipLaunchKernelGGL((mha_attn_kernel<D, GQ, DSA_ATTN_UNROLL_NT, true>), grid, dim3(kThreads), 0, s, a);
     else
       hipLaunchKernelGGL((mha_attn_kernel<D, GQ, DSA_ATTN_UNROLL, false>), grid, dim3(kThreads), 0, s, a);
   }

@@ -9,7 +9,8 @@
 // norm(max(0, p - q)); if every draft is accepted a bonus token is drawn from
 // the last target row.
 //
-// Four launches:
+// Four launches (three for at most 16 sequences, where the decision runs in
+// every mass workgroup instead of a launch of its own):
 //   stats   grid (chunk, row): the running max and sum of exp(x - max) of
 //           each chunk of each of the 2G+1 rows of a sequence (fp32,
 //           wavefront reductions), streamed once with 16-byte loads (whole
@@ -31,14 +32,17 @@ namespace dsa {
 namespace {
 
 #ifndef DSA_VERIFY_STAT_THREADS
-#define DSA_VERIFY_STAT_THREADS 256
+#define DSA_VERIFY_STAT_THREADS 512
 #endif
 #ifndef DSA_VERIFY_STAT_U
-#define DSA_VERIFY_STAT_U 4
+#define DSA_VERIFY_STAT_U 2
 #endif
 constexpr int kStatThreads = DSA_VERIFY_STAT_THREADS;
 constexpr int kStatU = DSA_VERIFY_STAT_U;       // float4 loads in flight per thread
 constexpr int kStatStep = kStatThreads * 4;     // logits per load round of a workgroup
+constexpr int kArgThreads = 256;                // greedy argmax pass: workgroup shape
+constexpr int kArgU = 4;
+constexpr int kArgStep = kArgThreads * 4;
 constexpr int kStatTargetWgs = 512;
 constexpr size_t kStreamBytes = (size_t)256 << 20;   // above this, logits are streamed non-temporally
 constexpr int kTile = 256;           // logits per wave step (64 lanes x 4)
@@ -630,14 +634,14 @@ void launch_mass(bool nt, dim3 grid, hipStream_t s, const VerifyArgs& a, const V
 // Logits per stats workgroup: whole rows when the rows alone give about
 // kStatTargetWgs workgroups, else rows split into chunks of whole load
 // rounds so that about that many run.
-int chunk_for_rows(int64_t rows, int V) {
-  const int64_t steps = (V + kStatStep - 1) / kStatStep;
+int chunk_for_rows(int64_t rows, int V, int step) {
+  const int64_t steps = (V + step - 1) / step;
   int64_t want = (kStatTargetWgs + rows - 1) / rows;   // chunks per row
   want = want < 1 ? 1 : want > steps ? steps : want;
-  return (int)((steps + want - 1) / want) * kStatStep;
+  return (int)((steps + want - 1) / want) * step;
 }
 
-int stats_chunk(int B, int G, int V) { return chunk_for_rows((int64_t)B * (2 * G + 1), V); }
+int stats_chunk(int B, int G, int V) { return chunk_for_rows((int64_t)B * (2 * G + 1), V, kStatStep); }
 
 // Tiles per residual-mass chunk: 8K-logit chunks (kBigChunkTiles tiles)
 // when there are enough sequences to fill the GPU with them, else 4K.
@@ -709,25 +713,25 @@ struct GreedyArgs {
 
 // Kernel 1: (max, argmax) of each chunk of each target row.
 template <bool NT>
-__global__ __launch_bounds__(kStatThreads) void greedy_argmax_kernel(GreedyArgs a) {
-  __shared__ ArgMax s_w[kStatThreads / 64];
+__global__ __launch_bounds__(kArgThreads) void greedy_argmax_kernel(GreedyArgs a) {
+  __shared__ ArgMax s_w[kArgThreads / 64];
   const int c = blockIdx.x;
   const int rr = blockIdx.y;   // b * (G+1) + j
   const float* row = a.tl + (size_t)rr * a.V;
   const int e0 = c * a.chunk;
   const int e1 = min(e0 + a.chunk, a.V);
   ArgMax best{-INFINITY, INT_MAX};
-  for (int e = e0 + threadIdx.x * 4; e < e1; e += kStatU * kStatStep) {
-    float4 x[kStatU];
+  for (int e = e0 + threadIdx.x * 4; e < e1; e += kArgU * kArgStep) {
+    float4 x[kArgU];
 #pragma unroll
-    for (int u = 0; u < kStatU; ++u) {
-      const int ee = e + u * kStatStep;
+    for (int u = 0; u < kArgU; ++u) {
+      const int ee = e + u * kArgStep;
       if (a.vec) x[u] = ld16<NT>(row + (min(ee, e1 - 1) & ~3));
       else x[u] = load4(row, min(ee, e1 - 1), e1, false);
     }
 #pragma unroll
-    for (int u = 0; u < kStatU; ++u) {
-      const int ee = e + u * kStatStep;   // ascending within the thread: strict > keeps the first
+    for (int u = 0; u < kArgU; ++u) {
+      const int ee = e + u * kArgStep;   // ascending within the thread: strict > keeps the first
       if (ee + 0 < e1 && x[u].x > best.v) best = ArgMax{x[u].x, ee + 0};
       if (ee + 1 < e1 && x[u].y > best.v) best = ArgMax{x[u].y, ee + 1};
       if (ee + 2 < e1 && x[u].z > best.v) best = ArgMax{x[u].z, ee + 2};
@@ -740,7 +744,7 @@ __global__ __launch_bounds__(kStatThreads) void greedy_argmax_kernel(GreedyArgs 
   __syncthreads();
   if (threadIdx.x == 0) {
     ArgMax r = s_w[0];
-    for (int w = 1; w < kStatThreads / 64; ++w) r = am_pick(r, s_w[w]);
+    for (int w = 1; w < kArgThreads / 64; ++w) r = am_pick(r, s_w[w]);
     a.part[(size_t)rr * a.nchunks + c] = r;
   }
 }
@@ -779,7 +783,7 @@ __global__ __launch_bounds__(kGreedyThreads) void greedy_decide_kernel(GreedyArg
 }
 
 size_t greedy_ws(int B, int G, int V, int* nchunks, int* chunk) {
-  const int ch = chunk_for_rows((int64_t)B * (G + 1), V);
+  const int ch = chunk_for_rows((int64_t)B * (G + 1), V, kArgStep);
   const int nc = (V + ch - 1) / ch;
   if (nchunks) *nchunks = nc;
   if (chunk) *chunk = ch;
@@ -839,7 +843,7 @@ extern "C" dsa_status spec_verify(const float* target_logits, const float* draft
   dsa_status st = launch_status("spec_verify(stats)");
   if (st != DSA_OK) return st;
 #ifndef DSA_VERIFY_FUSE_MAX_B
-#define DSA_VERIFY_FUSE_MAX_B 8
+#define DSA_VERIFY_FUSE_MAX_B 16
 #endif
   // up to DSA_VERIFY_FUSE_MAX_B sequences the decision runs inside the mass
   // kernel (three launches); beyond, in a kernel of its own
@@ -900,9 +904,9 @@ extern "C" dsa_status spec_verify_greedy(const float* target_logits, const int32
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 g1(nchunks, B * (G + 1));
   if ((size_t)B * (G + 1) * V * sizeof(float) > kStreamBytes)
-    hipLaunchKernelGGL(greedy_argmax_kernel<true>, g1, dim3(kStatThreads), 0, s, a);
+    hipLaunchKernelGGL(greedy_argmax_kernel<true>, g1, dim3(kArgThreads), 0, s, a);
   else
-    hipLaunchKernelGGL(greedy_argmax_kernel<false>, g1, dim3(kStatThreads), 0, s, a);
+    hipLaunchKernelGGL(greedy_argmax_kernel<false>, g1, dim3(kArgThreads), 0, s, a);
   const dsa_status st = launch_status("spec_verify_greedy(argmax)");
   if (st != DSA_OK) return st;
   hipLaunchKernelGGL(greedy_decide_kernel, dim3(B), dim3(kGreedyThreads), 0, s, a);

@@ -398,7 +398,8 @@ def test_spec_verify_many_sequences(std):
 @pytest.mark.parametrize("B,G,V", [
     (1, 1, 1000),       # one draft
     (3, 32, 4099),      # the largest chain, V not a multiple of 4
-    (9, 7, 2048),       # first batch size with the decision in a kernel of its own
+    (16, 7, 2048),      # largest batch with the decision inside the mass kernel
+    (17, 7, 2048),      # first batch size with the decision in a kernel of its own
     (8, 7, 600000),     # decision inside the mass kernel, logits past the last-level cache (streamed)
 ])
 def test_spec_verify_shape_edges(B, G, V):

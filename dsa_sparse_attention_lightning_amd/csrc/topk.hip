@@ -6,64 +6,31 @@
 //
 // Scores are mapped to order-preserving 32-bit keys (-0.0 canonicalised to
 // +0.0).  The kept set is {key > K*} plus the lowest positions with key == K*,
-// where K* is the k-th largest key.  Five launches per call, all multi-
-// workgroup except the last:
-//   1 zero     clear the per-row histograms and counters
-//   2 hist1    histogram of key bits 31..20 (4096 bins; LDS, then integer
-//              atomics into the row's global histogram)
-//   3 hist2    every workgroup scans hist1 for the threshold bin T1, then
-//              histograms key bits 19..8 of the elements in bin T1
-//   4 collect  with T1 and T2 known, elements above the 24-bit threshold are
-//              appended to the row's `sel` list and those on it to `cand`
-//              (wave-aggregated integer atomics; list order is irrelevant)
-//   5 finish   one workgroup per row radix-selects the missing elements among
-//              the candidates on the composite (key low 8 bits, ~position),
-//              merges them with `sel` and bitonic-sorts the kept positions.
-// Rows with row_len <= k skip 2-4 and are written directly by 5.
-// Integer atomics only: the result is a function of the input set, and the
-// final sort makes the output order canonical, so runs are bitwise identical.
+// where K* is the k-th largest key.  No sort is needed anywhere: the kept
+// positions are produced in position order.
+//
+// Rows whose keys fit in one CU's LDS take one workgroup and one launch (see
+// the one-workgroup path below).  Longer rows take four launches; the row is
+// split into chunks of 4096 positions (more when a row has over 4096 chunks):
+//   1 zero     clear the row's global 14-bit key histogram
+//   2 hist     each chunk's histogram of key bits 31..18 in LDS, added into
+//              the row's histogram (16,384 bins) and a 128-bin coarse one
+//              with integer atomics
+//   3 collect  every workgroup finds the threshold bin T of the row (coarse,
+//              then fine) and writes its chunk's positions above T and its
+//              candidates (key, position) in T as position-ordered lists,
+//              with per-chunk counts (ranks from wave prefix scans; no
+//              atomics, so list order is position order)
+//   4 finish   one workgroup per row: prefix sums of the chunk counts, a
+//              radix select on the candidates' 18 low key bits (two 9-bit
+//              rounds), ties to the lower position by list order, and the two
+//              ascending lists merged by binary search.
+// Integer atomics only (histogram counts, order-free): runs are bitwise
+// identical.
 #include "dsa_common.h"
 
 namespace dsa {
 namespace {
-
-constexpr int kBins = 4096;
-constexpr int kHistThreads = 256;
-constexpr int kChunk = 4096;          // positions per workgroup in passes 2-4
-constexpr int kPerThread = kChunk / kHistThreads;   // 16 loads in flight per thread
-constexpr int kFinThreads = 1024;
-constexpr int kMaxK = 8192;
-constexpr int kCandCap = 8192;        // candidates held in LDS by pass 5
-
-struct RowWs {
-  uint32_t* hist1;   // [rows][kBins]
-  uint32_t* hist2;   // [rows][kBins]
-  uint32_t* cnt;     // [rows][4]: n_sel, n_cand
-  int32_t* sel;      // [rows][k]
-  uint2* cand;       // [rows][ld]: (key, position)
-};
-
-__host__ __device__ inline size_t ws_bytes(int rows, int64_t ld, int k, RowWs* out, char* base) {
-  size_t off = 0;
-  auto take = [&](size_t bytes) {
-    size_t o = off;
-    off = align_up(off + bytes, 256);
-    return o;
-  };
-  size_t h1 = take((size_t)rows * kBins * 4);
-  size_t h2 = take((size_t)rows * kBins * 4);
-  size_t cn = take((size_t)rows * 4 * 4);
-  size_t sl = take((size_t)rows * k * 4);
-  size_t cd = take((size_t)rows * ld * 8);
-  if (out) {
-    out->hist1 = reinterpret_cast<uint32_t*>(base + h1);
-    out->hist2 = reinterpret_cast<uint32_t*>(base + h2);
-    out->cnt = reinterpret_cast<uint32_t*>(base + cn);
-    out->sel = reinterpret_cast<int32_t*>(base + sl);
-    out->cand = reinterpret_cast<uint2*>(base + cd);
-  }
-  return off;
-}
 
 __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);
@@ -78,364 +45,501 @@ __device__ __forceinline__ uint32_t mask_rank(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-// Appends `pred` lanes to a list with one atomic per wave; returns the slot
-// of this lane (valid where pred).
-__device__ __forceinline__ uint32_t wave_append(bool pred, uint32_t* counter) {
-  const uint64_t m = __ballot(pred);
-  if (m == 0) return 0;
-  const int leader = __ffsll((long long)m) - 1;
-  uint32_t base = 0;
-  if (lane_id() == leader) base = atomicAdd(counter, (uint32_t)__popcll(m));
-  base = __shfl(base, leader, 64);
-  return base + mask_rank(m);
+constexpr int kMaxK = 8192;
+
+// ---------------------------------------------------------------------------
+// Multi-workgroup pipeline
+// ---------------------------------------------------------------------------
+constexpr int kDigitBits = 14;                    // first digit: key bits 31..18
+constexpr int kLowBits = 32 - kDigitBits;         // resolved among the candidates
+constexpr uint32_t kLowMask = (1u << kLowBits) - 1u;
+constexpr int kFine = 1 << kDigitBits;            // 16,384 bins
+constexpr int kCoarse = 128;
+constexpr int kPerCoarse = kFine / kCoarse;       // 128 fine bins per coarse bin
+constexpr int kPassThreads = 256;
+constexpr int kPassWaves = kPassThreads / 64;
+constexpr int kBlock = 4096;                      // positions per load round of a pass workgroup
+constexpr int kQuads = kBlock / (4 * kPassThreads);   // four 16-byte loads per thread
+#ifndef DSA_TOPK_FIN_THREADS
+#define DSA_TOPK_FIN_THREADS 1024
+#endif
+constexpr int kFinThreads = DSA_TOPK_FIN_THREADS;
+constexpr int kMaxChunks = 4 * kFinThreads;       // the finish's prefix sums take 4 chunks per thread
+constexpr int kFinWaves = kFinThreads / 64;
+constexpr int kCandLds = 4096;                    // candidates resolved in LDS (more: from the workspace)
+constexpr int kRadix = 9;                         // two rounds over the 18 low bits
+static_assert(2 * kRadix == kLowBits, "two radix rounds cover the low bits");
+static_assert(kQuads * 4 * kPassThreads == kBlock, "a load round covers a block");
+static_assert(kPerCoarse == kCoarse, "one 128-bin search finds the coarse bin, a second the fine bin in it");
+
+struct PipeWs {
+  uint32_t* fine;     // [rows][kFine]
+  uint32_t* coarse;   // [rows][kCoarse]
+  uint2* counts;      // [rows][chunks]: (above T, in T)
+  int32_t* sel;       // [rows][chunks][chunk]: positions above T, ascending
+  uint2* cand;        // [rows][chunks][chunk]: (key, position) in T, ascending
+  int chunk;          // positions per chunk: kBlock << s
+  int chunks;
+};
+
+inline int chunk_for(int64_t ld) {
+  int64_t c = kBlock;
+  while ((ld + c - 1) / c > kMaxChunks) c *= 2;
+  return (int)c;
 }
 
-// Threshold bin of a 4096-bin histogram, scanning from the top: the bin T
-// with above(T) < need <= above(T) + hist[T].  Run by all kHistThreads
-// threads; result in *t_out / *above_out (shared).
-__device__ void find_threshold_4096(const uint32_t* hist, uint32_t need, uint32_t* s_wave,
-                                    int* t_out, uint32_t* above_out) {
-  constexpr int per = kBins / kHistThreads;   // 16 bins per thread
-  const int tid = threadIdx.x;
-  if (tid == 0) {
-    *t_out = 0;
-    *above_out = 0;
+inline size_t ws_bytes(int rows, int64_t ld, PipeWs* out, char* base) {
+  const int chunk = chunk_for(ld);
+  const int chunks = (int)((ld + chunk - 1) / chunk);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  };
+  const size_t per = (size_t)chunks * chunk;
+  size_t f = take((size_t)rows * kFine * 4);
+  size_t c = take((size_t)rows * kCoarse * 4);
+  size_t n = take((size_t)rows * chunks * 8);
+  size_t sl = take((size_t)rows * per * 4);
+  size_t cd = take((size_t)rows * per * 8);
+  if (out) {
+    out->fine = reinterpret_cast<uint32_t*>(base + f);
+    out->coarse = reinterpret_cast<uint32_t*>(base + c);
+    out->counts = reinterpret_cast<uint2*>(base + n);
+    out->sel = reinterpret_cast<int32_t*>(base + sl);
+    out->cand = reinterpret_cast<uint2*>(base + cd);
+    out->chunk = chunk;
+    out->chunks = chunks;
   }
-  // thread tid owns bins [top - per*tid - per + 1, top - per*tid], top = 4095
-  const int hi_bin = kBins - 1 - tid * per;
-  uint32_t c[per];
-  uint32_t tot = 0;
+  return off;
+}
+
+__global__ __launch_bounds__(kPassThreads) void topk_zero_kernel(PipeWs ws) {
+  const int row = blockIdx.x;
+  uint4* f = reinterpret_cast<uint4*>(ws.fine + (size_t)row * kFine);
+  for (int i = threadIdx.x; i < kFine / 4; i += kPassThreads) f[i] = make_uint4(0u, 0u, 0u, 0u);
+  if (threadIdx.x < kCoarse / 4)
+    reinterpret_cast<uint4*>(ws.coarse + (size_t)row * kCoarse)[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// Keys of positions p..p+3 (p a multiple of 4).  vec: the row is 16-byte
+// aligned and ld a multiple of 4, so one 16-byte load (clamped inside the
+// row) serves them; positions at or past L read a clamped copy and are masked
+// by the caller.
+__device__ __forceinline__ uint4 load_keys4(const float* __restrict__ s, bool vec, int p, int L) {
+  float4 v;
+  if (vec) {
+    v = *reinterpret_cast<const float4*>(s + min(p, (L - 1) & ~3));
+  } else {
+    v.x = s[min(p, L - 1)];
+    v.y = s[min(p + 1, L - 1)];
+    v.z = s[min(p + 2, L - 1)];
+    v.w = s[min(p + 3, L - 1)];
+  }
+  return make_uint4(order_key(v.x), order_key(v.y), order_key(v.z), order_key(v.w));
+}
+
+__device__ __forceinline__ uint32_t q_at(const uint4& q, int e) {
+  return e == 0 ? q.x : e == 1 ? q.y : e == 2 ? q.z : q.w;
+}
+
+__global__ __launch_bounds__(kPassThreads) void topk_hist_kernel(const float* __restrict__ scores,
+                                                                 const int32_t* __restrict__ row_len, int64_t ld,
+                                                                 int k, int vec, PipeWs ws) {
+  __shared__ __align__(16) uint32_t h[kFine];
+  const int row = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int L = (int)min((int64_t)row_len[row], ld);   // row_len <= ld is a precondition
+  const int64_t c0 = (int64_t)blockIdx.x * ws.chunk;
+  if (L <= k || c0 >= L) return;
+  const int t_end = (int)min(c0 + ws.chunk, (int64_t)L);
+  for (int i = tid; i < kFine / 4; i += kPassThreads) reinterpret_cast<uint4*>(h)[i] = make_uint4(0u, 0u, 0u, 0u);
+  __syncthreads();
+  const float* s = scores + (size_t)row * ld;
+  for (int b = (int)c0; b < t_end; b += kBlock) {
+    uint4 kq[kQuads];
+#pragma unroll
+    for (int u = 0; u < kQuads; ++u) kq[u] = load_keys4(s, vec != 0, b + (u * kPassThreads + tid) * 4, L);
+#pragma unroll
+    for (int u = 0; u < kQuads; ++u) {
+      const int p = b + (u * kPassThreads + tid) * 4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (p + e < t_end) atomicAdd(&h[q_at(kq[u], e) >> kLowBits], 1u);
+    }
+  }
+  __syncthreads();
+  // bins go out lane-consecutively (bin j*256 + t), so a wave's atomics fall
+  // on two cache lines per step and merge into few memory-side requests;
+  // empty bins are skipped.  All LDS reads are issued before the atomics.
+  uint32_t* gf = ws.fine + (size_t)row * kFine;
+  constexpr int kPer = kFine / kPassThreads;   // 64
+  uint32_t c[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) c[j] = h[j * kPassThreads + tid];
+  // coarse bin t/2 gets bins [64t, 64t + 64) of thread t and its neighbour;
+  // reads rotated by t so the lanes of a wave hit distinct banks
+  uint32_t sum = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) sum += h[tid * kPer + ((j + tid) & (kPer - 1))];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j)
+    if (c[j]) atomicAdd(gf + j * kPassThreads + tid, c[j]);
+  sum += (uint32_t)__shfl_xor((int)sum, 1, 64);
+  if ((tid & 1) == 0 && sum) atomicAdd(ws.coarse + (size_t)row * kCoarse + tid / 2, sum);
+}
+
+// Bin T of the 128-bin histogram g (scanning from the top) with
+// above(T) < need <= above(T) + g[T]; kPassThreads threads call it.
+__device__ void pass_find_bin(const uint32_t* __restrict__ g, uint32_t need, uint32_t* s_tot, int* s_bin,
+                              uint32_t* s_above) {
+  const int tid = threadIdx.x;
+  const uint32_t c = tid < kCoarse ? g[kCoarse - 1 - tid] : 0u;
+  const uint32_t inc = wave_incl_scan_dpp(c);
+  if (lane_id() == 63) s_tot[tid >> 6] = inc;
+  if (tid == 0) {   // always overwritten when the counts are consistent
+    *s_bin = 0;
+    *s_above = 0;
+  }
+  __syncthreads();
+  const uint32_t run = inc - c + (tid >= 64 ? s_tot[0] : 0u);
+  if (tid < kCoarse && run < need && run + c >= need) {
+    *s_bin = kCoarse - 1 - tid;
+    *s_above = run;
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kPassThreads) void topk_collect_kernel(const float* __restrict__ scores,
+                                                                    const int32_t* __restrict__ row_len,
+                                                                    int64_t ld, int k, int vec, PipeWs ws) {
+  __shared__ uint32_t s_tot[2][kQuads][kPassWaves];   // per (list, load round, wave) counts
+  __shared__ uint32_t s_off[2][kQuads][kPassWaves];
+  __shared__ uint32_t s_sum[2];
+  __shared__ uint32_t s_w[kPassWaves];
+  __shared__ int s_bin;
+  __shared__ uint32_t s_above;
+  const int row = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int L = (int)min((int64_t)row_len[row], ld);   // row_len <= ld is a precondition
+  const int64_t c0 = (int64_t)blockIdx.x * ws.chunk;
+  if (L <= k || c0 >= L) return;
+  const int t_end = (int)min(c0 + ws.chunk, (int64_t)L);
+  const float* s = scores + (size_t)row * ld;
+  uint4 kq[kQuads];   // the first round's loads go out before the threshold search
+#pragma unroll
+  for (int u = 0; u < kQuads; ++u) kq[u] = load_keys4(s, vec != 0, (int)c0 + (u * kPassThreads + tid) * 4, L);
+  // threshold bin T of the row: coarse bin, then the fine bin inside it
+  pass_find_bin(ws.coarse + (size_t)row * kCoarse, (uint32_t)k, s_w, &s_bin, &s_above);
+  const int T0 = s_bin;
+  const uint32_t above0 = s_above;
+  __syncthreads();
+  pass_find_bin(ws.fine + (size_t)row * kFine + T0 * kPerCoarse, (uint32_t)k - above0, s_w, &s_bin, &s_above);
+  const uint32_t T = (uint32_t)(T0 * kPerCoarse + s_bin);
+  const size_t region = ((size_t)row * ws.chunks + blockIdx.x) * ws.chunk;
+  int32_t* sel = ws.sel + region;
+  uint2* cand = ws.cand + region;
+  uint32_t n_sel = 0, n_cand = 0;   // this chunk's running counts (block-uniform)
+  for (int b = (int)c0; b < t_end; b += kBlock) {
+    if (b != (int)c0) {
+#pragma unroll
+      for (int u = 0; u < kQuads; ++u) kq[u] = load_keys4(s, vec != 0, b + (u * kPassThreads + tid) * 4, L);
+    }
+    // positions ascend with (load round u, wave, lane, element): per-lane
+    // flag counts, wave prefix scans, then a prefix over (u, wave)
+    uint32_t gt_bits[kQuads], eq_bits[kQuads], ex_gt[kQuads], ex_eq[kQuads];
+#pragma unroll
+    for (int u = 0; u < kQuads; ++u) {
+      const int p = b + (u * kPassThreads + tid) * 4;
+      uint32_t g = 0, q = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t d = q_at(kq[u], e) >> kLowBits;
+        const bool valid = p + e < t_end;
+        g |= (valid && d > T) ? (1u << e) : 0u;
+        q |= (valid && d == T) ? (1u << e) : 0u;
+      }
+      gt_bits[u] = g;
+      eq_bits[u] = q;
+      const uint32_t cg = (uint32_t)__popc(g), cq = (uint32_t)__popc(q);
+      const uint32_t ig = wave_incl_scan_dpp(cg), iq = wave_incl_scan_dpp(cq);
+      ex_gt[u] = ig - cg;
+      ex_eq[u] = iq - cq;
+      if (lane == 63) {
+        s_tot[0][u][wave] = ig;
+        s_tot[1][u][wave] = iq;
+      }
+    }
+    __syncthreads();
+    if (tid < 2) {
+      uint32_t v[kQuads * kPassWaves];
+#pragma unroll
+      for (int i = 0; i < kQuads * kPassWaves; ++i) v[i] = s_tot[tid][i / kPassWaves][i % kPassWaves];
+      uint32_t run = 0;
+#pragma unroll
+      for (int i = 0; i < kQuads * kPassWaves; ++i) {
+        s_off[tid][i / kPassWaves][i % kPassWaves] = run;
+        run += v[i];
+      }
+      s_sum[tid] = run;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kQuads; ++u) {
+      const int p = b + (u * kPassThreads + tid) * 4;
+      uint32_t og = n_sel + s_off[0][u][wave] + ex_gt[u];
+      uint32_t oq = n_cand + s_off[1][u][wave] + ex_eq[u];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (gt_bits[u] & (1u << e)) sel[og++] = p + e;
+        if (eq_bits[u] & (1u << e)) cand[oq++] = make_uint2(q_at(kq[u], e), (uint32_t)(p + e));
+      }
+    }
+    n_sel += s_sum[0];
+    n_cand += s_sum[1];
+    __syncthreads();   // s_tot / s_off are rewritten by the next round
+  }
+  if (tid == 0) ws.counts[(size_t)row * ws.chunks + blockIdx.x] = make_uint2(n_sel, n_cand);
+}
+
+struct FinShared {
+  uint32_t sel_off[kMaxChunks + 1];
+  uint32_t cand_off[kMaxChunks + 1];
+  uint32_t hist[1 << kRadix];
+  uint32_t wa[kFinWaves], wb[kFinWaves];
+  uint32_t misc[4];
+};
+constexpr size_t kFinListsOff = align_up(sizeof(FinShared), 16);
+constexpr size_t kFinLds = kFinListsOff + 2 * (size_t)kMaxK * 4 + (size_t)kCandLds * 8;
+static_assert((size_t)kCandLds * 8 >= (size_t)kMaxK * 4, "the candidate area stages the output row");
+
+// Largest c in [0, n) with off[c] <= i, for two lookups at once (off
+// ascending, off[0] = 0); fixed steps, both reads issued each step.
+__device__ __forceinline__ void chunk_of2(const uint32_t* off_a, uint32_t ia, const uint32_t* off_b, uint32_t ib,
+                                          int n, int top, int& ca, int& cb) {
+  ca = 0;
+  cb = 0;
+  for (int step = top; step > 0; step >>= 1) {
+    const int ja = ca + step, jb = cb + step;
+    const uint32_t va = off_a[min(ja, n - 1)], vb = off_b[min(jb, n - 1)];
+    ca = (ja < n && va <= ia) ? ja : ca;
+    cb = (jb < n && vb <= ib) ? jb : cb;
+  }
+}
+
+// Block-wide exclusive prefix of one flag per thread in thread order; returns
+// this thread's rank, and the block's total in *total (all threads).
+__device__ __forceinline__ uint32_t fin_rank(bool f, uint32_t* wsum, uint32_t* total) {
+  const uint64_t m = __ballot(f);
+  const int wave = threadIdx.x >> 6;
+  if (lane_id() == 0) wsum[wave] = (uint32_t)__popcll(m);
+  __syncthreads();
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kFinWaves; ++w) {
+    const uint32_t c = wsum[w];
+    before += w < wave ? c : 0u;
+    all += c;
+  }
+  __syncthreads();
+  *total = all;
+  return before + mask_rank(m);
+}
+
+// Digit T of the 512-bin histogram (scanning from the top) with
+// above(T) < need <= above(T) + hist[T]; result in misc[0] (digit) and
+// misc[1] (above).
+__device__ void fin_find_digit(FinShared& sh, uint32_t need) {
+  constexpr int nb = 1 << kRadix;
+  constexpr int per = nb > kFinThreads ? nb / kFinThreads : 1;   // bins per thread, descending
+  const int tid = threadIdx.x;
+  const int hi = nb - 1 - tid * per;
+  const bool owns = tid * per < nb;
+  uint32_t cnt[per], tot = 0;
 #pragma unroll
   for (int j = 0; j < per; ++j) {
-    c[j] = hist[hi_bin - j];
-    tot += c[j];
+    cnt[j] = owns ? sh.hist[hi - j] : 0u;
+    tot += cnt[j];
   }
-  // inclusive scan over threads (descending bin order)
   const uint32_t inc = wave_incl_scan_dpp(tot);
   const int wave = tid >> 6;
-  if (lane_id() == 63) s_wave[wave] = inc;
+  if (lane_id() == 63) sh.wa[wave] = inc;
+  if (tid == 0) {   // always overwritten when the counts are consistent
+    sh.misc[0] = 0;
+    sh.misc[1] = 0;
+  }
   __syncthreads();
-  uint32_t before = 0;
-  for (int wv = 0; wv < wave; ++wv) before += s_wave[wv];
-  uint32_t run = before + inc - tot;  // elements in bins above this thread's range
+  uint32_t run = inc - tot;
+#pragma unroll
+  for (int w = 0; w < kFinWaves; ++w) run += w < wave ? sh.wa[w] : 0u;
 #pragma unroll
   for (int j = 0; j < per; ++j) {
-    if (run < need && run + c[j] >= need) {
-      *t_out = hi_bin - j;
-      *above_out = run;
+    if (owns && run < need && run + cnt[j] >= need) {
+      sh.misc[0] = (uint32_t)(hi - j);
+      sh.misc[1] = run;
     }
-    run += c[j];
+    run += cnt[j];
   }
   __syncthreads();
 }
 
-__global__ __launch_bounds__(kHistThreads) void topk_zero_kernel(RowWs ws) {
-  const int row = blockIdx.x;
-  for (int i = threadIdx.x; i < kBins; i += kHistThreads) {
-    ws.hist1[(size_t)row * kBins + i] = 0;
-    ws.hist2[(size_t)row * kBins + i] = 0;
-  }
-  if (threadIdx.x < 4) ws.cnt[row * 4 + threadIdx.x] = 0;
-}
-
-__global__ __launch_bounds__(kHistThreads) void topk_hist1_kernel(const float* __restrict__ scores,
-                                                                  const int32_t* __restrict__ row_len,
-                                                                  int64_t ld, int k, RowWs ws) {
-  __shared__ uint32_t h[kBins];
-  const int row = blockIdx.y;
-  const int L = (int)min((int64_t)row_len[row], ld);   // row_len <= ld is a precondition
-  const int t0 = blockIdx.x * kChunk;
-  if (L <= k || t0 >= L) return;
-  for (int i = threadIdx.x; i < kBins; i += kHistThreads) h[i] = 0;
-  __syncthreads();
-  const float* s = scores + (size_t)row * ld;
-  const int t1 = min(t0 + kChunk, L);
-  float v[kPerThread];   // all of the chunk's loads in flight at once
-#pragma unroll
-  for (int u = 0; u < kPerThread; ++u) v[u] = s[min(t0 + (int)threadIdx.x + u * kHistThreads, t1 - 1)];
-#pragma unroll
-  for (int u = 0; u < kPerThread; ++u)
-    if (t0 + (int)threadIdx.x + u * kHistThreads < t1) atomicAdd(&h[order_key(v[u]) >> 20], 1u);
-  __syncthreads();
-  uint32_t* g = ws.hist1 + (size_t)row * kBins;
-  for (int i = threadIdx.x; i < kBins; i += kHistThreads)
-    if (h[i]) atomicAdd(&g[i], h[i]);
-}
-
-__global__ __launch_bounds__(kHistThreads) void topk_hist2_kernel(const float* __restrict__ scores,
-                                                                  const int32_t* __restrict__ row_len,
-                                                                  int64_t ld, int k, RowWs ws) {
-  __shared__ uint32_t h[kBins];
-  __shared__ uint32_t s_wave[kHistThreads / 64];
-  __shared__ int s_t1;
-  __shared__ uint32_t s_a1;
-  const int row = blockIdx.y;
-  const int L = (int)min((int64_t)row_len[row], ld);   // row_len <= ld is a precondition
-  const int t0 = blockIdx.x * kChunk;
-  if (L <= k || t0 >= L) return;
-  for (int i = threadIdx.x; i < kBins; i += kHistThreads) h[i] = 0;
-  find_threshold_4096(ws.hist1 + (size_t)row * kBins, (uint32_t)k, s_wave, &s_t1, &s_a1);
-  const uint32_t T1 = (uint32_t)s_t1;
-  const float* s = scores + (size_t)row * ld;
-  const int t1 = min(t0 + kChunk, L);
-  float v[kPerThread];
-#pragma unroll
-  for (int u = 0; u < kPerThread; ++u) v[u] = s[min(t0 + (int)threadIdx.x + u * kHistThreads, t1 - 1)];
-#pragma unroll
-  for (int u = 0; u < kPerThread; ++u) {
-    const uint32_t key = order_key(v[u]);
-    if (t0 + (int)threadIdx.x + u * kHistThreads < t1 && (key >> 20) == T1) atomicAdd(&h[(key >> 8) & 0xfffu], 1u);
-  }
-  __syncthreads();
-  uint32_t* g = ws.hist2 + (size_t)row * kBins;
-  for (int i = threadIdx.x; i < kBins; i += kHistThreads)
-    if (h[i]) atomicAdd(&g[i], h[i]);
-}
-
-__global__ __launch_bounds__(kHistThreads) void topk_collect_kernel(const float* __restrict__ scores,
-                                                                    const int32_t* __restrict__ row_len,
-                                                                    int64_t ld, int k, RowWs ws) {
-  __shared__ uint32_t s_wave[kHistThreads / 64];
-  __shared__ int s_t1, s_t2;
-  __shared__ uint32_t s_a1, s_a2;
-  __shared__ int32_t l_sel[kChunk];
-  __shared__ uint2 l_cand[kChunk];
-  __shared__ uint32_t s_n[2], s_base[2];
-  const int row = blockIdx.y;
-  const int L = (int)min((int64_t)row_len[row], ld);   // row_len <= ld is a precondition
-  const int t0 = blockIdx.x * kChunk;
-  if (L <= k || t0 >= L) return;
-  find_threshold_4096(ws.hist1 + (size_t)row * kBins, (uint32_t)k, s_wave, &s_t1, &s_a1);
-  find_threshold_4096(ws.hist2 + (size_t)row * kBins, (uint32_t)k - s_a1, s_wave, &s_t2, &s_a2);
-  const uint32_t prefix = ((uint32_t)s_t1 << 12) | (uint32_t)s_t2;  // key bits 31..8
-  const float* s = scores + (size_t)row * ld;
-  int32_t* sel = ws.sel + (size_t)row * k;
-  uint2* cand = ws.cand + (size_t)row * ld;
-  uint32_t* cnt = ws.cnt + row * 4;
-  const int t1 = min(t0 + kChunk, L);
-  // the chunk's selections and candidates are gathered in LDS first; one
-  // global atomic per list and workgroup then reserves their place
-  if (threadIdx.x < 2) s_n[threadIdx.x] = 0;
-  float v[kPerThread];
-#pragma unroll
-  for (int u = 0; u < kPerThread; ++u) v[u] = s[min(t0 + (int)threadIdx.x + u * kHistThreads, t1 - 1)];
-  __syncthreads();
-  // whole waves iterate together so the ballots see every lane
-#pragma unroll
-  for (int u = 0; u < kPerThread; ++u) {
-    const int t = t0 + (int)threadIdx.x + u * kHistThreads;
-    const bool valid = t < t1;
-    const uint32_t key = order_key(v[u]);
-    const uint32_t top = key >> 8;
-    const bool is_sel = valid && top > prefix;
-    const bool is_cand = valid && top == prefix;
-    const uint32_t ps = wave_append(is_sel, &s_n[0]);
-    if (is_sel) l_sel[ps] = t;
-    const uint32_t pc = wave_append(is_cand, &s_n[1]);
-    if (is_cand) l_cand[pc] = make_uint2(key, (uint32_t)t);
-  }
-  __syncthreads();
-  if (threadIdx.x < 2) s_base[threadIdx.x] = s_n[threadIdx.x] ? atomicAdd(&cnt[threadIdx.x], s_n[threadIdx.x]) : 0u;
-  __syncthreads();
-  for (uint32_t i = threadIdx.x; i < s_n[0]; i += kHistThreads)
-    if (s_base[0] + i < (uint32_t)k) sel[s_base[0] + i] = l_sel[i];
-  for (uint32_t i = threadIdx.x; i < s_n[1]; i += kHistThreads)
-    if (s_base[1] + i < (uint32_t)ld) cand[s_base[1] + i] = l_cand[i];
-}
-
-// Composite rank of a candidate: key bits 7..0, then ~position (lower
-// position ranks higher).  40 bits; bits above are equal for all candidates.
-__device__ __forceinline__ uint64_t cand_rank(uint2 c) {
-  return ((uint64_t)(c.x & 0xffu) << 32) | (uint64_t)(~c.y);
-}
-
-template <bool kInLds>
-__device__ void select_candidates(const uint2* cand_g, const uint64_t* cand_l, int n_cand, uint32_t m,
-                                  uint32_t* hist, int32_t* out, uint32_t* out_cnt, uint32_t* s_misc) {
-  // s_misc[0] = chosen digit, s_misc[1] = count above, s_misc[2] = count equal
-  uint64_t prefix = 0;
-  int shift = 40;
-  uint32_t m_rem = m;
-  const int tid = threadIdx.x;
-  while (shift > 0) {
-    const int nshift = shift - 8;
-    for (int i = tid; i < 256; i += kFinThreads) hist[i] = 0;
-    __syncthreads();
-    for (int i = tid; i < n_cand; i += kFinThreads) {
-      const uint64_t c = kInLds ? cand_l[i] : cand_rank(cand_g[i]);
-      if ((c >> shift) == (prefix >> shift)) atomicAdd(&hist[(c >> nshift) & 0xffu], 1u);
-    }
-    __syncthreads();
-    if (tid < 64) {
-      // lane owns bins 255-4*lane .. 252-4*lane (descending)
-      uint32_t c4[4];
-      uint32_t tot = 0;
-      for (int j = 0; j < 4; ++j) {
-        c4[j] = hist[255 - 4 * tid - j];
-        tot += c4[j];
-      }
-      const uint32_t inc = wave_incl_scan_dpp(tot);
-      uint32_t run = inc - tot;
-      for (int j = 0; j < 4; ++j) {
-        if (run < m_rem && run + c4[j] >= m_rem) {
-          s_misc[0] = 255 - 4 * tid - j;
-          s_misc[1] = run;
-          s_misc[2] = c4[j];
-        }
-        run += c4[j];
-      }
-    }
-    __syncthreads();
-    const uint32_t digit = s_misc[0];
-    m_rem -= s_misc[1];
-    const uint32_t eq = s_misc[2];
-    __syncthreads();
-    prefix |= (uint64_t)digit << nshift;
-    shift = nshift;
-    if (eq == m_rem) break;   // every candidate on this prefix is kept
-  }
-  for (int i = tid; i < n_cand; i += kFinThreads) {
-    const uint64_t c = kInLds ? cand_l[i] : cand_rank(cand_g[i]);
-    if ((c >> shift) >= (prefix >> shift)) {
-      const uint32_t slot = atomicAdd(out_cnt, 1u);
-      if (slot < (uint32_t)kMaxK) out[slot] = (int32_t)(~(uint32_t)c);
-    }
-  }
-  __syncthreads();
-}
-
-// Ascending bitonic sort of list[0, 256*E), E elements per thread in
-// registers (threads 0..255 hold data; every thread of the block must call
-// it, for the barriers).  Strides below E are swaps inside a thread, strides
-// below 64*E lane exchanges inside a wave, and only strides of a wave's whole
-// span or more go through LDS (two barriers each: 3 of the 66 stages at 2048
-// elements, instead of a barrier per stage).
-template <int E>
-__device__ void sort_regs(int32_t* list) {
-  constexpr int P = 256 * E;
-  constexpr int WE = 64 * E;
-  const int tid = threadIdx.x;
-  const bool act = tid < 256;
-  const int lane = tid & 63;
-  const int base = (tid >> 6) * WE + lane * E;
-  int32_t a[E];
-  if (act) {
-#pragma unroll
-    for (int e = 0; e < E; ++e) a[e] = list[base + e];
-  }
-#pragma unroll
-  for (int size = 2; size <= P; size <<= 1) {
-#pragma unroll
-    for (int stride = size / 2; stride > 0; stride >>= 1) {
-      if (stride >= WE) {
-        // element i keeps min(a_i, a_{i^stride}) if it is the lower index of
-        // an ascending block or the upper index of a descending one, else max
-        if (act) {
-#pragma unroll
-          for (int e = 0; e < E; ++e) list[base + e] = a[e];
-        }
-        __syncthreads();
-        if (act) {
-#pragma unroll
-          for (int e = 0; e < E; ++e) {
-            const int i = base + e;
-            const int32_t p = list[i ^ stride];
-            a[e] = (((i & stride) == 0) == ((i & size) == 0)) ? min(a[e], p) : max(a[e], p);
-          }
-        }
-        __syncthreads();
-      } else if (stride >= E) {
-        if (act) {
-          const int lx = stride / E;
-#pragma unroll
-          for (int e = 0; e < E; ++e) {
-            const int i = base + e;
-            const int32_t p = __shfl_xor(a[e], lx, 64);
-            a[e] = (((i & stride) == 0) == ((i & size) == 0)) ? min(a[e], p) : max(a[e], p);
-          }
-        }
-      } else if (act) {
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          if ((e & stride) == 0) {
-            const int32_t x = a[e], y = a[e | stride];
-            const bool asc = ((base + e) & size) == 0;
-            a[e] = asc ? min(x, y) : max(x, y);
-            a[e | stride] = asc ? max(x, y) : min(x, y);
-          }
-        }
-      }
-    }
-  }
-  if (act) {
-#pragma unroll
-    for (int e = 0; e < E; ++e) list[base + e] = a[e];
-  }
-  __syncthreads();
-}
-
-__global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const int32_t* __restrict__ row_len, int k,
-                                                                  int32_t* __restrict__ idx, RowWs ws,
-                                                                  int64_t ld) {
-  __shared__ int32_t list[kMaxK];
-  __shared__ uint64_t cand_l[kCandCap];
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t s_misc[4];
-  __shared__ uint32_t s_cnt;
+__global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const int32_t* __restrict__ row_len, int64_t ld,
+                                                                  int k, int32_t* __restrict__ idx, PipeWs ws) {
+  extern __shared__ __align__(16) unsigned char fin_smem[];
+  FinShared& sh = *reinterpret_cast<FinShared*>(fin_smem);
+  int32_t* sel = reinterpret_cast<int32_t*>(fin_smem + kFinListsOff);
+  int32_t* chosen = sel + kMaxK;
+  uint2* cand_l = reinterpret_cast<uint2*>(chosen + kMaxK);
+  int32_t* stage = reinterpret_cast<int32_t*>(cand_l);   // output row, once the candidates are used
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
+  const int wave = tid >> 6;
   const int L = (int)min((int64_t)row_len[row], ld);   // row_len <= ld is a precondition
   int32_t* dst = idx + (size_t)row * k;
   if (L <= k) {
     for (int i = tid; i < k; i += kFinThreads) dst[i] = i < L ? i : -1;
     return;
   }
-  // counts are bounded by construction; the clamps only keep a broken
-  // precondition (row_len > ld) from writing out of bounds
-  const uint32_t n_sel = min(ws.cnt[row * 4 + 0], (uint32_t)k - 1u);
-  const int n_cand = (int)min((int64_t)ws.cnt[row * 4 + 1], ld);
-  const uint32_t m = (uint32_t)k - n_sel;
-  const int32_t* sel = ws.sel + (size_t)row * k;
-  const uint2* cand = ws.cand + (size_t)row * ld;
-  for (uint32_t i = tid; i < n_sel; i += kFinThreads) list[i] = sel[i];
-  if (tid == 0) s_cnt = n_sel;
-  if (n_cand <= kCandCap) {
-    for (int i = tid; i < n_cand; i += kFinThreads) cand_l[i] = cand_rank(cand[i]);
-    __syncthreads();
-    select_candidates<true>(cand, cand_l, n_cand, m, hist, list, &s_cnt, s_misc);
-  } else {
-    __syncthreads();
-    select_candidates<false>(cand, cand_l, n_cand, m, hist, list, &s_cnt, s_misc);
+  const int C = (int)(((int64_t)L + ws.chunk - 1) / ws.chunk);
+  const uint2* counts = ws.counts + (size_t)row * ws.chunks;
+  // exclusive prefix sums of the chunk counts; thread t owns chunks
+  // [t*per, t*per + per)
+  const int per = (C + kFinThreads - 1) / kFinThreads;   // <= 4
+  uint32_t a[4], c[4], ta = 0, tc = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int ch = tid * per + j;
+    const uint2 n = (j < per && ch < C) ? counts[ch] : make_uint2(0u, 0u);
+    a[j] = n.x;
+    c[j] = n.y;
+    ta += n.x;
+    tc += n.y;
   }
-  // bitonic sort of the k kept positions, ascending (in registers when k > 1024)
-  int P = 1;
-  while (P < k) P <<= 1;
-  for (int i = k + tid; i < P; i += kFinThreads) list[i] = 0x7fffffff;
+  const uint32_t ia = wave_incl_scan_dpp(ta), ic = wave_incl_scan_dpp(tc);
+  if (lane_id() == 63) {
+    sh.wa[wave] = ia;
+    sh.wb[wave] = ic;
+  }
   __syncthreads();
-  if (P == 2048) {
-    sort_regs<8>(list);
-  } else if (P == 4096) {
-    sort_regs<16>(list);
-  } else if (P == 8192) {
-    sort_regs<32>(list);
-  } else {
-    for (int size = 2; size <= P; size <<= 1) {
-      for (int stride = size >> 1; stride > 0; stride >>= 1) {
-        for (int i = tid; i < P / 2; i += kFinThreads) {
-          const int lo = 2 * i - (i & (stride - 1));
-          const int hi = lo + stride;
-          const bool up = (lo & size) == 0;
-          const int32_t a = list[lo], b = list[hi];
-          if ((a > b) == up) {
-            list[lo] = b;
-            list[hi] = a;
-          }
-        }
-        __syncthreads();
-      }
+  uint32_t ra = ia - ta, rc = ic - tc, A1 = 0, NC = 0;
+#pragma unroll
+  for (int w = 0; w < kFinWaves; ++w) {
+    ra += w < wave ? sh.wa[w] : 0u;
+    rc += w < wave ? sh.wb[w] : 0u;
+    A1 += sh.wa[w];
+    NC += sh.wb[w];
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int ch = tid * per + j;
+    if (j < per && ch < C) {
+      sh.sel_off[ch] = ra;
+      sh.cand_off[ch] = rc;
+    }
+    ra += a[j];
+    rc += c[j];
+  }
+  // the counts are exact by construction (A1 < k <= A1 + NC); the clamps
+  // only keep broken preconditions (NaN scores) inside the buffers
+  A1 = min(A1, (uint32_t)k - 1u);
+  const uint32_t need = (uint32_t)k - A1;
+  const size_t region0 = (size_t)row * ws.chunks * ws.chunk;
+  const int32_t* sel_g = ws.sel + region0;
+  const uint2* cand_g = ws.cand + region0;
+  constexpr uint32_t kDigitMask = (1u << kRadix) - 1u;
+  for (int i = tid; i < (1 << kRadix); i += kFinThreads) sh.hist[i] = 0;
+  __syncthreads();
+  const bool in_lds = NC <= (uint32_t)kCandLds;
+  const int topC = 1 << (31 - __clz(C));   // highest power of two <= C
+  auto cand_at_g = [&](uint32_t i) -> uint2 {
+    int ch, unused;
+    chunk_of2(sh.cand_off, i, sh.cand_off, i, C, topC, ch, unused);
+    return cand_g[(size_t)ch * ws.chunk + (i - sh.cand_off[ch])];
+  };
+  // one pass gathers both lists into LDS (their lookups and loads in flight
+  // together) and histograms the candidates' first low digit (bits 17..9)
+  const uint32_t n_pass = max(A1, in_lds ? NC : 0u);
+  for (uint32_t i = tid; i < n_pass; i += kFinThreads) {
+    int cs, cc;
+    chunk_of2(sh.sel_off, i, sh.cand_off, i, C, topC, cs, cc);
+    const int32_t sv = i < A1 ? sel_g[(size_t)cs * ws.chunk + (i - sh.sel_off[cs])] : 0;
+    const uint2 cv = (in_lds && i < NC) ? cand_g[(size_t)cc * ws.chunk + (i - sh.cand_off[cc])] : make_uint2(0u, 0u);
+    if (i < A1) sel[i] = sv;
+    if (in_lds && i < NC) {
+      cand_l[i] = cv;
+      atomicAdd(&sh.hist[((cv.x & kLowMask) >> kRadix) & kDigitMask], 1u);
     }
   }
-  for (int i = tid; i < k; i += kFinThreads) dst[i] = list[i];
+  if (!in_lds)
+    for (uint32_t i = tid; i < NC; i += kFinThreads)
+      atomicAdd(&sh.hist[((cand_at_g(i).x & kLowMask) >> kRadix) & kDigitMask], 1u);
+  __syncthreads();
+  auto cand_at = [&](uint32_t i) -> uint2 { return in_lds ? cand_l[i] : cand_at_g(i); };
+  // radix select on the low key bits: digit 1 = bits 17..9, digit 2 = 8..0
+  fin_find_digit(sh, need);
+  uint32_t low_thr = sh.misc[0] << kRadix, above = sh.misc[1];
+  __syncthreads();
+  for (int i = tid; i < (1 << kRadix); i += kFinThreads) sh.hist[i] = 0;
+  __syncthreads();
+  for (uint32_t i = tid; i < NC; i += kFinThreads) {
+    const uint32_t low = cand_at(i).x & kLowMask;
+    if ((low >> kRadix) == (low_thr >> kRadix)) atomicAdd(&sh.hist[low & kDigitMask], 1u);
+  }
+  __syncthreads();
+  fin_find_digit(sh, need - above);
+  low_thr |= sh.misc[0];
+  above += sh.misc[1];
+  __syncthreads();
+  // candidates above the threshold are kept, and of those equal to it the
+  // first need - above in list (= position) order
+  const uint32_t need_eq = need - above;
+  uint32_t eq_seen = 0, taken = 0;
+  for (uint32_t t0 = 0; t0 < NC && taken < need; t0 += kFinThreads) {
+    const uint32_t i = t0 + tid;
+    const uint2 x = i < NC ? cand_at(i) : make_uint2(0u, 0u);
+    const uint32_t low = x.x & kLowMask;
+    const bool gt = i < NC && low > low_thr;
+    const bool eq = i < NC && low == low_thr;
+    uint32_t n_eq, n_take;
+    const uint32_t er = eq_seen + fin_rank(eq, sh.wa, &n_eq);
+    const bool take = gt || (eq && er < need_eq);
+    const uint32_t slot = taken + fin_rank(take, sh.wb, &n_take);
+    if (take && slot < need) chosen[slot] = (int32_t)x.y;
+    eq_seen += n_eq;
+    taken += n_take;
+  }
+  __syncthreads();
+  // merge: a position's slot is its index in its own list plus the number of
+  // entries of the other list below it (the lists are disjoint).  Both
+  // searches of a thread run in one fixed-step loop (independent LDS reads).
+  const int na = (int)A1, nb = (int)min(taken, need);
+  const int nmax = max(na, nb);
+  const int top = nmax > 0 ? 1 << (31 - __clz(nmax)) : 0;
+  for (int i = tid; i < nmax; i += kFinThreads) {
+    const bool va = i < na, vb = i < nb;
+    const int32_t xa = va ? sel[i] : 0, xb = vb ? chosen[i] : 0;
+    int pa = 0, pb = 0;   // entries of the other list below xa / xb
+    for (int step = top; step > 0; step >>= 1) {
+      const int ja = pa + step, jb = pb + step;
+      const int32_t ca = chosen[max(min(ja, nb) - 1, 0)], cb = sel[max(min(jb, na) - 1, 0)];
+      pa = (ja <= nb && ca < xa) ? ja : pa;
+      pb = (jb <= na && cb < xb) ? jb : pb;
+    }
+    if (va) stage[i + pa] = xa;
+    if (vb) stage[i + pb] = xb;
+  }
+  __syncthreads();
+  if ((reinterpret_cast<uintptr_t>(dst) & 15u) == 0) {
+    const int k4 = k & ~3;
+    for (int i = tid * 4; i < k4; i += kFinThreads * 4)
+      *reinterpret_cast<uint4*>(dst + i) = *reinterpret_cast<const uint4*>(stage + i);
+    for (int i = k4 + tid; i < k; i += kFinThreads) dst[i] = stage[i];
+  } else {
+    for (int i = tid; i < k; i += kFinThreads) dst[i] = stage[i];
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -449,6 +553,7 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const int32_t*
 // position range, ballots give in-order ranks) writes them.  Either way equal
 // keys are taken lowest position first and no sort is needed.
 // ---------------------------------------------------------------------------
+constexpr int kBins = 4096;
 constexpr int kOneThreads = 1024;
 constexpr int kOneWaves = kOneThreads / 64;
 constexpr int kOneLdsKeys = 35840;       // 140 KiB of keys
@@ -760,7 +865,7 @@ size_t one_lds_bytes() { return align_up(sizeof(OneShared), 16) + (size_t)kOneLd
 extern "C" size_t dsa_topk_workspace_size(int B, int R, int64_t ld, int k) {
   if (B < 1 || R < 1 || ld < 1 || k < 1) return 0;
   if (ld <= dsa::kOneMaxLd) return 0;
-  return dsa::ws_bytes(B * R, ld, k, nullptr, nullptr);
+  return dsa::ws_bytes(B * R, ld, nullptr, nullptr);
 }
 
 extern "C" dsa_status dsa_topk(const float* scores, const int32_t* row_len, int B, int R, int64_t ld, int k,
@@ -787,16 +892,21 @@ extern "C" dsa_status dsa_topk(const float* scores, const int32_t* row_len, int 
     hipLaunchKernelGGL(kern, dim3(rows), dim3(kOneThreads), lds, s, scores, row_len, ld, k, idx);
     return launch_status("dsa_topk");
   }
-  const size_t need = ws_bytes(rows, ld, k, nullptr, nullptr);
+  const size_t need = ws_bytes(rows, ld, nullptr, nullptr);
   DSA_REQUIRE(workspace && workspace_bytes >= need, DSA_ERR_WORKSPACE,
               "dsa_topk: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
-  RowWs ws;
-  ws_bytes(rows, ld, k, &ws, static_cast<char*>(workspace));
-  const unsigned chunks = (unsigned)((ld + kChunk - 1) / kChunk);
-  hipLaunchKernelGGL(topk_zero_kernel, dim3(rows), dim3(kHistThreads), 0, s, ws);
-  hipLaunchKernelGGL(topk_hist1_kernel, dim3(chunks, rows), dim3(kHistThreads), 0, s, scores, row_len, ld, k, ws);
-  hipLaunchKernelGGL(topk_hist2_kernel, dim3(chunks, rows), dim3(kHistThreads), 0, s, scores, row_len, ld, k, ws);
-  hipLaunchKernelGGL(topk_collect_kernel, dim3(chunks, rows), dim3(kHistThreads), 0, s, scores, row_len, ld, k, ws);
-  hipLaunchKernelGGL(topk_finish_kernel, dim3(rows), dim3(kFinThreads), 0, s, row_len, k, idx, ws, ld);
+  PipeWs ws;
+  ws_bytes(rows, ld, &ws, static_cast<char*>(workspace));
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(topk_finish_kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kFinLds) != hipSuccess) {
+    set_error("dsa_topk: %zu bytes of LDS not available", kFinLds);
+    return DSA_ERR_HIP;
+  }
+  const int vec = (reinterpret_cast<uintptr_t>(scores) & 15u) == 0 && (ld & 3) == 0;
+  const dim3 grid((unsigned)ws.chunks, (unsigned)rows);
+  hipLaunchKernelGGL(topk_zero_kernel, dim3(rows), dim3(kPassThreads), 0, s, ws);
+  hipLaunchKernelGGL(topk_hist_kernel, grid, dim3(kPassThreads), 0, s, scores, row_len, ld, k, vec, ws);
+  hipLaunchKernelGGL(topk_collect_kernel, grid, dim3(kPassThreads), 0, s, scores, row_len, ld, k, vec, ws);
+  hipLaunchKernelGGL(topk_finish_kernel, dim3(rows), dim3(kFinThreads), kFinLds, s, row_len, ld, k, idx, ws);
   return launch_status("dsa_topk");
 }

@@ -557,7 +557,10 @@ constexpr int kBins = 4096;
 constexpr int kOneThreads = 1024;
 constexpr int kOneWaves = kOneThreads / 64;
 constexpr int kOneLdsKeys = 35840;       // 140 KiB of keys
-constexpr int kOneMaxLd = kOneLdsKeys;
+#ifndef DSA_TOPK_ONE_MAX_LD
+#define DSA_TOPK_ONE_MAX_LD kOneLdsKeys
+#endif
+constexpr int kOneMaxLd = DSA_TOPK_ONE_MAX_LD;   // longest row the one-workgroup path takes
 
 constexpr int kOneCand = kBins / 4;    // threshold-bin candidates resolved in LDS (first half of hist)
 constexpr int kOneWords = (kOneLdsKeys + 63) / 64;   // kept-position bitmap (second half of hist)

@@ -163,9 +163,13 @@ dsa_status launch_index_t(const void* q, const float* w, const void* kidx, const
                           int max_pages, int64_t ld, hipStream_t stream) {
   constexpr int kBlockPos = kThreads / 64 * 16 * TILES;
   // Positions per workgroup: whole steps, sized so that a long row still
-  // spreads over about 2048 workgroups.
+  // spreads over about 4096 workgroups (2048: 0.5-2 us slower at 2^20 and on
+  // the 16-sequence batch).
+#ifndef DSA_INDEX_TARGET_WGS
+#define DSA_INDEX_TARGET_WGS 4096
+#endif
   const int64_t steps = (ld + kBlockPos - 1) / kBlockPos;
-  int per = (int)((steps * B + 2047) / 2048);
+  int per = (int)((steps * B + DSA_INDEX_TARGET_WGS - 1) / DSA_INDEX_TARGET_WGS);
   per = per < 1 ? 1 : per > 8 ? 8 : per;
   const bool rowt = per > 1;
   const size_t lds = (size_t)R * MB * KS * 64 * 16 + (size_t)R * MB * 16 * sizeof(float) +
@@ -191,13 +195,13 @@ template <int KS, int MB>
 dsa_status launch_index(const void* q, const float* w, const void* kidx, const int32_t* bt,
                         const int32_t* row_len, float* scores, int B, int R, int H, int page,
                         int max_pages, int64_t ld, hipStream_t stream) {
-  // small problems: one 16-position tile per wave step, so more workgroups
+  // small problems: one 16-position tile per wave step, so more workgroups;
+  // otherwise two (eight key loads in flight per lane; four tiles per step
+  // measured 2-4 us slower at 2^20 and on the 16-sequence batch)
   const int64_t total = ld * (int64_t)B;
   if (total <= (1 << 18))
     return launch_index_t<KS, MB, 1>(q, w, kidx, bt, row_len, scores, B, R, H, page, max_pages, ld, stream);
-  if (total <= (1 << 20))
-    return launch_index_t<KS, MB, 2>(q, w, kidx, bt, row_len, scores, B, R, H, page, max_pages, ld, stream);
-  return launch_index_t<KS, MB, 4>(q, w, kidx, bt, row_len, scores, B, R, H, page, max_pages, ld, stream);
+  return launch_index_t<KS, MB, 2>(q, w, kidx, bt, row_len, scores, B, R, H, page, max_pages, ld, stream);
 }
 
 // ---------------------------------------------------------------------------

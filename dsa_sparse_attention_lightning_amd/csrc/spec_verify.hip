@@ -43,7 +43,10 @@ constexpr int kStatStep = kStatThreads * 4;     // logits per load round of a wo
 constexpr int kArgThreads = 256;                // greedy argmax pass: workgroup shape
 constexpr int kArgU = 4;
 constexpr int kArgStep = kArgThreads * 4;
-constexpr int kStatTargetWgs = 512;
+#ifndef DSA_VERIFY_STAT_TARGET_WGS
+#define DSA_VERIFY_STAT_TARGET_WGS 512
+#endif
+constexpr int kStatTargetWgs = DSA_VERIFY_STAT_TARGET_WGS;
 constexpr size_t kStreamBytes = (size_t)256 << 20;   // above this, logits are streamed non-temporally
 constexpr int kTile = 256;           // logits per wave step (64 lanes x 4)
 constexpr int kMaxV = 1 << 20;

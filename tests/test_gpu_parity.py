@@ -161,6 +161,25 @@ def test_topk_small_k_and_k_ge_L(ld):
     _topk_case(s, [ld, ld - 1, ld // 2], 1)                          # k = 1
 
 
+def test_topk_workspace_needs_no_initialisation():
+    """One workspace, filled with 0xff bytes, serves calls of different
+    shapes in turn (more rows, then a longer row, then fewer rows): every
+    call clears or writes what it reads, so stale histograms, counts and
+    lists of the previous call never reach the result."""
+    import torch
+    rng = np.random.default_rng(7)
+    shapes = [(3, 50000, [50000, 40000, 36001]), (1, 300000, [300000]), (5, 40000, [40000, 39999, 5, 38000, 37000])]
+    need = max(dsa.topk_workspace_size(B, 1, ld, 2048) for B, ld, _ in shapes)
+    ws = torch.full((need,), 0xff, dtype=torch.uint8, device="cuda:0")
+    for B, ld, lens in shapes * 2:
+        s = (rng.standard_normal((B, ld)) * 35 + 144).astype(np.float32)
+        log("topk reused workspace", B, ld, lens)
+        got = dsa.topk(to_dev(s.reshape(B, 1, ld)), to_dev(np.asarray(lens, np.int32).reshape(B, 1)), 2048,
+                       workspace=ws).cpu().numpy()[:, 0]
+        for b in range(B):
+            np.testing.assert_array_equal(got[b], O.topk(s[b].astype(np.float64), lens[b], 2048))
+
+
 @pytest.mark.parametrize("k", [1, 7, 64, 1500, 2048, 3000, 8192])
 @pytest.mark.parametrize("ld", [30000, 50000, 180000])
 def test_topk_various_k(k, ld):

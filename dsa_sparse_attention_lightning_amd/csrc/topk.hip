@@ -157,7 +157,8 @@ __global__ __launch_bounds__(kPassThreads) void topk_hist_kernel(const float* __
   for (int i = tid; i < kFine / 4; i += kPassThreads) reinterpret_cast<uint4*>(h)[i] = make_uint4(0u, 0u, 0u, 0u);
   __syncthreads();
   const float* s = scores + (size_t)row * ld;
-  for (int b = (int)c0; b < t_end; b += kBlock) {
+  for (int64_t bb = c0; bb < t_end; bb += kBlock) {   // 64-bit: bb + kBlock may pass 2^31 - 1
+    const int b = (int)bb;
     uint4 kq[kQuads];
 #pragma unroll
     for (int u = 0; u < kQuads; ++u) kq[u] = load_keys4(s, vec != 0, b + (u * kPassThreads + tid) * 4, L);
@@ -243,8 +244,9 @@ __global__ __launch_bounds__(kPassThreads) void topk_collect_kernel(const float*
   int32_t* sel = ws.sel + region;
   uint2* cand = ws.cand + region;
   uint32_t n_sel = 0, n_cand = 0;   // this chunk's running counts (block-uniform)
-  for (int b = (int)c0; b < t_end; b += kBlock) {
-    if (b != (int)c0) {
+  for (int64_t bb = c0; bb < t_end; bb += kBlock) {   // 64-bit: bb + kBlock may pass 2^31 - 1
+    const int b = (int)bb;
+    if (bb != c0) {
 #pragma unroll
       for (int u = 0; u < kQuads; ++u) kq[u] = load_keys4(s, vec != 0, b + (u * kPassThreads + tid) * 4, L);
     }
@@ -561,6 +563,7 @@ constexpr int kOneLdsKeys = 35840;       // 140 KiB of keys
 #define DSA_TOPK_ONE_MAX_LD kOneLdsKeys
 #endif
 constexpr int kOneMaxLd = DSA_TOPK_ONE_MAX_LD;   // longest row the one-workgroup path takes
+static_assert(kOneMaxLd <= kOneLdsKeys, "the one-workgroup path holds a whole row of keys in LDS");
 
 constexpr int kOneCand = kBins / 4;    // threshold-bin candidates resolved in LDS (first half of hist)
 constexpr int kOneWords = (kOneLdsKeys + 63) / 64;   // kept-position bitmap (second half of hist)

@@ -659,7 +659,8 @@ extern "C" dsa_status dsa_index_scores(const void* q, const float* w, const void
   DSA_REQUIRE(H_I <= 64, DSA_ERR_UNSUPPORTED, "dsa_index_scores: H_I=%d > 64", H_I);
   DSA_REQUIRE(R <= 8, DSA_ERR_UNSUPPORTED, "dsa_index_scores: R=%d > 8", R);
   DSA_REQUIRE(B <= 65535, DSA_ERR_UNSUPPORTED, "dsa_index_scores: B=%d > 65535", B);
-  DSA_REQUIRE(ld <= ((int64_t)1 << 31) - 1, DSA_ERR_UNSUPPORTED, "dsa_index_scores: ld too large");
+  DSA_REQUIRE(ld <= DSA_MAX_LD, DSA_ERR_UNSUPPORTED, "dsa_index_scores: ld=%lld > %lld", (long long)ld,
+              (long long)DSA_MAX_LD);
   DSA_REQUIRE(aligned16(q) && aligned16(k_index), DSA_ERR_INVALID_ARG,
               "dsa_index_scores: q and k_index must be 16-byte aligned");
   const int MB = (H_I + 15) / 16;

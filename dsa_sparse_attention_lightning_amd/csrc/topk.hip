@@ -882,7 +882,8 @@ extern "C" dsa_status dsa_topk(const float* scores, const int32_t* row_len, int 
   DSA_REQUIRE(B >= 1 && R >= 1 && ld >= 1 && k >= 1, DSA_ERR_INVALID_ARG,
               "dsa_topk: sizes must be positive (B=%d R=%d ld=%lld k=%d)", B, R, (long long)ld, k);
   DSA_REQUIRE(k <= kMaxK, DSA_ERR_UNSUPPORTED, "dsa_topk: k=%d > %d", k, kMaxK);
-  DSA_REQUIRE(ld <= ((int64_t)1 << 31) - 1, DSA_ERR_UNSUPPORTED, "dsa_topk: ld too large");
+  DSA_REQUIRE(ld <= DSA_MAX_LD, DSA_ERR_UNSUPPORTED, "dsa_topk: ld=%lld > %lld", (long long)ld,
+              (long long)DSA_MAX_LD);
   DSA_REQUIRE((int64_t)B * R <= 65535, DSA_ERR_UNSUPPORTED, "dsa_topk: B*R=%lld rows > 65535", (long long)B * R);
   const int rows = B * R;
   hipStream_t s = static_cast<hipStream_t>(stream);

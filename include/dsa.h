@@ -42,6 +42,10 @@ extern "C" {
 
 #define DSA_ABI_VERSION 1
 
+/* Longest score row (ld) dsa_index_scores and dsa_topk accept: positions are
+ * int32 inside the kernels, with headroom for whole tile steps past the end. */
+#define DSA_MAX_LD (((int64_t)1 << 31) - 65536)
+
 typedef enum {
   DSA_OK = 0,
   DSA_ERR_INVALID_ARG = 1,   /* null pointer, non-positive size, bad stride */

@@ -56,6 +56,7 @@ def test_index_scores_validation():
     assert _scores_call(R=9) == _lib.DSA_ERR_UNSUPPORTED
     assert _scores_call(B=65536) == _lib.DSA_ERR_UNSUPPORTED          # grid limit
     assert _scores_call(q=MISALIGNED) == _lib.DSA_ERR_INVALID_ARG
+    assert _scores_call(ld=(1 << 31) - 65536 + 1) == _lib.DSA_ERR_UNSUPPORTED   # past DSA_MAX_LD
 
 
 def test_topk_validation():
@@ -69,6 +70,8 @@ def test_topk_validation():
     assert lib.dsa_topk(FAKE, FAKE, 2, 1, 200000, 64, FAKE, FAKE, ws - 1, None) == _lib.DSA_ERR_WORKSPACE
     assert lib.dsa_topk(FAKE, FAKE, 2, 1, 200000, 64, FAKE, None, ws, None) == _lib.DSA_ERR_WORKSPACE
     assert lib.dsa_topk(FAKE, FAKE, 8192, 8, 100, 8, FAKE, FAKE, ws, None) == _lib.DSA_ERR_UNSUPPORTED   # B*R > 65535
+    max_ld = (1 << 31) - 65536                                          # DSA_MAX_LD
+    assert lib.dsa_topk(FAKE, FAKE, 1, 1, max_ld + 1, 8, FAKE, FAKE, ws, None) == _lib.DSA_ERR_UNSUPPORTED
     assert lib.dsa_topk_workspace_size(1, 1, 35840, 64) == 0            # keys fit in LDS: one launch
     assert lib.dsa_topk_workspace_size(1, 1, 35841, 64) > 0
 

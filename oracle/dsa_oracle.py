@@ -246,7 +246,7 @@ def icdf(weights, u):
     Returns the smallest i with sum_{t <= i} w_t > u * sum_t w_t, scanning the
     vocabulary in ascending index order, plus the draw's float64 margin: the
     distance of u*W to the nearest cumulative boundary of the chosen index,
-    relative to W (used to judge near-boundary cases).
+    relative to W (tells near-boundary draws apart from clear ones).
     """
     w = np.asarray(weights, dtype=np.float64)
     c = np.cumsum(w)

@@ -180,6 +180,18 @@ def test_topk_workspace_needs_no_initialisation():
             np.testing.assert_array_equal(got[b], O.topk(s[b].astype(np.float64), lens[b], 2048))
 
 
+def test_topk_rows_longer_than_4096_chunks():
+    """A row over 4096 x 4096 positions doubles the chunk size, so every pass
+    workgroup loops over several 4096-position blocks (positions, counts and
+    list offsets carried across them)."""
+    rng = np.random.default_rng(11)
+    ld = (1 << 24) + 5000
+    s = (rng.standard_normal((1, ld)) * 35 + 144).astype(np.float32)
+    for L, k in ((ld, 2048), (ld - 3, 8192), ((1 << 24) + 1, 1)):
+        log("topk long row", ld, L, k)
+        _topk_case(s, [L], k)
+
+
 @pytest.mark.parametrize("k", [1, 7, 64, 1500, 2048, 3000, 8192])
 @pytest.mark.parametrize("ld", [30000, 50000, 180000])
 def test_topk_various_k(k, ld):

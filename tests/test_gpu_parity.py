@@ -180,6 +180,35 @@ def test_topk_workspace_needs_no_initialisation():
             np.testing.assert_array_equal(got[b], O.topk(s[b].astype(np.float64), lens[b], 2048))
 
 
+@pytest.mark.parametrize("seed", range(12))
+def test_topk_random_shapes(seed):
+    """Seeded random shapes over both top-k paths: 1-6 rows, ld from 1,000 to
+    300,000, ragged row lengths (some <= k), k from 1 to 8192, and one of five
+    score distributions (normal, small-integer ties, indexer-like, uniform,
+    a few clustered spikes)."""
+    rng = np.random.default_rng(1000 + seed)
+    B = int(rng.integers(1, 7))
+    ld = int(rng.integers(1000, 300001))
+    k = int(rng.choice([1, 7, 64, 257, 2048, 3000, 8192]))
+    lens = [int(x) for x in rng.integers(0, ld + 1, size=B)]
+    lens[0] = ld
+    kind = seed % 5
+    if kind == 0:
+        s = rng.standard_normal((B, ld))
+    elif kind == 1:
+        s = rng.integers(-50, 50, (B, ld)).astype(np.float64)
+    elif kind == 2:
+        s = rng.standard_normal((B, ld)) * 35 + 144
+    elif kind == 3:
+        s = rng.random((B, ld))
+    else:
+        s = np.full((B, ld), 1.0)
+        for b in range(B):
+            s[b, rng.choice(ld, size=min(ld, 3 * k), replace=False)] = rng.integers(2, 6, size=min(ld, 3 * k))
+    log("topk random", seed, B, ld, k, kind, lens)
+    _topk_case(s.astype(np.float32), lens, k)
+
+
 def test_topk_rows_longer_than_4096_chunks():
     """A row over 4096 x 4096 positions doubles the chunk size, so every pass
     workgroup loops over several 4096-position blocks (positions, counts and

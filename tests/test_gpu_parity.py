@@ -279,6 +279,34 @@ def test_sparse_attn_matches_oracle(case):
     _attn_vs_oracle(d, dd, idx2)
 
 
+@pytest.mark.parametrize("seed", range(10))
+def test_sparse_attn_random_shapes(seed):
+    """Seeded random per-head-KV shapes: 1-5 sequences with ragged lengths,
+    head dims 64 or 128, GQA groups 1/2/4 (the instantiated set; other
+    groups are refused with DSA_ERR_UNSUPPORTED), k from 1 to 12,000 (k > L rows
+    included), shuffled or identity pages, and index sets with -1 entries
+    scattered through them."""
+    rng = np.random.default_rng(2000 + seed)
+    B = int(rng.integers(1, 6))
+    D = int(rng.choice([64, 128]))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    H = Hkv * int(rng.choice([1, 2, 4]))
+    lens = [int(x) for x in rng.integers(1, 20000, size=B)]
+    k = int(rng.choice([1, 17, 256, 2048, 5000, 12000]))
+    log("sparse_attn random", seed, B, H, Hkv, D, k, lens)
+    d = I.draft_inputs(3000 + seed, lens, H_I=4, D_I=32, H_q=H, H_kv=Hkv, D_qk=D, D_v=D, k=k, page=64,
+                       shuffle_pages=bool(seed % 2), G=1)
+    dd = DraftDev(d)
+    idx = np.full((B, k), -1, np.int64)
+    for b in range(B):
+        n = min(k, lens[b])
+        sel = rng.choice(lens[b], n, replace=False)
+        sel[rng.random(n) < 0.05] = -1          # scattered absent entries
+        idx[b, :n] = sel
+        rng.shuffle(idx[b])
+    _attn_vs_oracle(d, dd, idx)
+
+
 def test_sparse_attn_k_covers_context_equals_dense():
     d = I.draft_inputs(12, [700, 333], H_I=4, D_I=32, H_q=8, H_kv=8, D_qk=128, D_v=128, k=1024, G=1)
     dd = DraftDev(d)

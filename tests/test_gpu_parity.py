@@ -540,6 +540,24 @@ def test_spec_verify_draw_at_the_top_of_the_cdf(V):
     assert ref_em[0, 0] == V - 1 and np.all(em[np.arange(B), n] >= 0)
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_spec_verify_random_shapes(seed):
+    """Seeded random verification shapes: 1-40 sequences, 1-32 drafts,
+    vocabularies from 1,000 to 160,000 (odd sizes included), logit scales 0.3 to 8,
+    in-kernel Philox or caller-supplied uniforms; decisions and tokens must
+    equal the oracle's except near-margin cases (at most one per 64
+    sequences, plus one)."""
+    rng = np.random.default_rng(4000 + seed)
+    B = int(rng.integers(1, 41))
+    G = int(rng.integers(1, 33))
+    V = int(rng.integers(1000, 160001))
+    std = float(rng.choice([0.3, 1.0, 2.0, 4.0, 8.0]))
+    log("spec_verify random", seed, B, G, V, std)
+    vi = I.verify_inputs(5000 + seed, B, G, V, std)
+    _, _, near = _verify_case(vi, bool(seed % 2))
+    assert near <= B // 64 + 1
+
+
 @pytest.mark.parametrize("std", [0.5, 2.0])
 def test_spec_verify_block16(std):
     """Block-16 layout: G = 15 drafts plus the bonus position."""

@@ -68,6 +68,37 @@ def test_index_scores_exact(case):
             assert np.all(got[b, r, n:] == -7.0)   # untouched beyond row_len
 
 
+@pytest.mark.parametrize("seed", range(10))
+def test_index_scores_random_shapes(seed):
+    """Seeded random indexer shapes on exact integer inputs: 1-4 sequences,
+    1-8 rows with different visible prefixes, 1-64 heads, D_I 32/64/128, pages
+    of 16 or 64 (shuffled), contexts up to 300,000; every score bit-exact."""
+    rng = np.random.default_rng(6000 + seed)
+    B = int(rng.integers(1, 5))
+    R = int(rng.integers(1, 9))
+    H = int(rng.integers(1, 65))
+    D = int(rng.choice([32, 64, 128]))
+    page = int(rng.choice([16, 64]))
+    hi = 300000 if B == 1 else 60000
+    lens = [int(x) for x in rng.integers(1, hi, size=B)]
+    log("index_scores random", seed, B, R, H, D, page, lens)
+    d = I.draft_inputs(7000 + seed, lens, H_I=H, D_I=D, H_q=4, H_kv=4, D_qk=64, D_v=64, k=64, R=R, page=page,
+                       shuffle_pages=True, integer_indexer=True)
+    row_len = d.row_len.copy()
+    for r in range(R):
+        row_len[:, r] = np.maximum(d.lens - int(rng.integers(0, 100)) * r, 0)
+    dd = DraftDev(d)
+    out = torch.full((d.B, d.R, dd.ld), -7.0, device=DEV)
+    dsa.index_scores(dd.q_index, dd.w, dd.kidx, dd.bt, to_dev(row_len), page=d.page, out=out)
+    got = out.cpu().numpy()
+    for b in range(d.B):
+        ref = O.index_scores(d.q_index[b], d.w[b].astype(np.float64), d.keys[b], row_len[b])
+        for r in range(d.R):
+            n = row_len[b, r]
+            np.testing.assert_array_equal(got[b, r, :n], ref[r, :n].astype(np.float32))
+            assert np.all(got[b, r, n:] == -7.0)
+
+
 def test_index_scores_bf16_normal_bound():
     """Continuous N(0,1) bf16 inputs: error within the fp32 accumulation bound."""
     d = I.draft_inputs(8, [4000], H_I=64, D_I=128, H_q=4, H_kv=4, D_qk=64, D_v=64, k=64)

@@ -31,6 +31,14 @@ namespace {
 #endif
 constexpr int kWaves = DSA_ATTN_WAVES;      // waves per per-head-KV workgroup
 constexpr int kThreads = kWaves * 64;
+// A streamed gather (one query row per sequence, larger than the last-level
+// cache) with one query head per KV head runs 16 waves per workgroup, so one
+// workgroup holds all k = 2048 tokens of a (sequence, head group) and the
+// call needs no split-k combine launch (8 waves: 2 splits plus the combine).
+#ifndef DSA_ATTN_STREAM_WAVES
+#define DSA_ATTN_STREAM_WAVES 16
+#endif
+constexpr int kStreamWaves = DSA_ATTN_STREAM_WAVES;
 
 // Split-k plan: aim for about kTargetGroups workgroups, each with at least
 // kMinTokens selected tokens (tunable at build time).
@@ -88,6 +96,7 @@ struct WaveRows {
   int nw;          // tokens of this wave
 };
 static_assert(kMaxTokPerSplit <= 128 * kWaves, "a wave's tokens fit in two offsets per lane");
+constexpr int kStreamTokPerSplit = 128 * kStreamWaves;   // tokens per split of the 16-wave streamed gather
 
 __device__ __forceinline__ int64_t row_off(const WaveRows& r, int j) {   // j wave-uniform
   const int jj = min(j, max(r.nw - 1, 0));
@@ -184,13 +193,14 @@ __device__ __forceinline__ void consume(const WaveRows& wr, int j, const int64_t
   }
 }
 
-template <int D, int GQ, int U, bool NT>
-__global__ __launch_bounds__(kThreads) void mha_attn_kernel(AttnArgs a) {
+template <int D, int GQ, int U, bool NT, int W = kWaves>
+__global__ __launch_bounds__(W * 64) void mha_attn_kernel(AttnArgs a) {
   constexpr int SLOT = D / 8;            // lanes per KV row
   constexpr int NSLOT = 64 / SLOT;       // KV heads per wave
   constexpr int NH = NSLOT * GQ;         // query heads per workgroup
-  __shared__ float s_ml[kWaves][NH][2];
-  __shared__ float s_o[kWaves][NH][D];
+  constexpr int NTH = W * 64;
+  __shared__ float s_ml[W][NH][2];
+  __shared__ float s_o[W][NH][D];
 
   int split, hg, bs;
   if (a.row_grouped) {
@@ -225,17 +235,17 @@ __global__ __launch_bounds__(kThreads) void mha_attn_kernel(AttnArgs a) {
   const int g = hg * NSLOT + slot;                   // KV head of this lane
   const bool head_ok = g < a.H_kv;
 
-  // Row offsets of this wave's tokens (split-local w, w + kWaves, ...),
+  // Row offsets of this wave's tokens (split-local w, w + W, ...),
   // resolved through the page table once, two per lane; no barrier.
   const int32_t* idx = a.idx + ((size_t)b * a.idx_rows + (a.idx_rows > 1 ? s : 0)) * a.k;
   const int32_t* bt = a.bt + (size_t)b * a.max_pages;
   const int t_lo = split * a.tok_per_split;
   const int ntok = min(a.tok_per_split, a.k - t_lo);
   WaveRows wr;
-  wr.nw = wave < ntok ? (ntok - wave + kWaves - 1) / kWaves : 0;
+  wr.nw = wave < ntok ? (ntok - wave + W - 1) / W : 0;
   auto resolve = [&](int j) -> int64_t {
     if (j >= wr.nw) return -1;
-    const int t = idx[t_lo + wave + j * kWaves];
+    const int t = idx[t_lo + wave + j * W];
     // positions outside the block table (outside the contract) count as absent
     return (t >= 0 && t / a.page < a.max_pages)
                ? (int64_t)bt[t / a.page] * a.page_stride + (int64_t)(t % a.page) * a.row_stride
@@ -258,7 +268,7 @@ __global__ __launch_bounds__(kThreads) void mha_attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
   }
-  // Wave w takes split-local tokens w, w + kWaves, ... (its local tokens
+  // Wave w takes split-local tokens w, w + W, ... (its local tokens
   // 0, 1, ...); loads run one U-token stage ahead.  Padding heads
   // (g >= H_kv) read the last real head; their results are dropped.
   const uint32_t lane_bytes = (uint32_t)(((int64_t)min(g, a.H_kv - 1) * a.head_stride + sub * 8) * 2);
@@ -287,7 +297,7 @@ __global__ __launch_bounds__(kThreads) void mha_attn_kernel(AttnArgs a) {
     for (int e = 0; e < 8; ++e) s_o[wave][slot * GQ + j][sub * 8 + e] = acc[j][e];
   }
   __syncthreads();
-  for (int p = tid; p < NH * D; p += kThreads) {
+  for (int p = tid; p < NH * D; p += NTH) {
     const int hj = p / D;
     const int d = p % D;
     const int gg = hg * NSLOT + hj / GQ;
@@ -295,11 +305,11 @@ __global__ __launch_bounds__(kThreads) void mha_attn_kernel(AttnArgs a) {
     const int h = gg * GQ + hj % GQ;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_ml[w][hj][0]);
+    for (int w = 0; w < W; ++w) M = fmaxf(M, s_ml[w][hj][0]);
     float Lsum = 0.f, O = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
+      for (int w = 0; w < W; ++w) {
         const float c = fast_exp2(s_ml[w][hj][0] - M);
         Lsum += c * s_ml[w][hj][1];
         O += c * s_o[w][hj][d];
@@ -643,6 +653,12 @@ bool streams_kv(int B, int S_q, int H_kv, int D, int k) {
   return S_q == 1 && (double)B * k * H_kv * D * 2 * 2 > (double)kAttnStreamBytes;
 }
 
+// The streamed gather runs kStreamWaves per workgroup when each KV head has
+// one query head (the per-wave merge buffers then fit in LDS).
+bool wide_stream(int B, int S_q, int H_q, int H_kv, int D, int k) {
+  return H_q == H_kv && streams_kv(B, S_q, H_kv, D, k);
+}
+
 Plan make_plan(int B, int S_q, int H_q, int H_kv, int D_qk, int D_v, int k) {
   Plan p{};
   const bool latent = is_latent(H_q, H_kv, D_qk, D_v);
@@ -658,7 +674,8 @@ Plan make_plan(int B, int S_q, int H_q, int H_kv, int D_qk, int D_v, int k) {
   int ns = (int)((target + base - 1) / base);
   const int max_ns = (k + min_tok - 1) / min_tok;
   if (ns > max_ns) ns = max_ns;
-  const int min_ns = (k + kMaxTokPerSplit - 1) / kMaxTokPerSplit;
+  const int max_tok = (!latent && wide_stream(B, S_q, H_q, H_kv, D_qk, k)) ? kStreamTokPerSplit : kMaxTokPerSplit;
+  const int min_ns = (k + max_tok - 1) / max_tok;
   if (ns < min_ns) ns = min_ns;
   if (ns > max_split) ns = max_split;
   if (ns < 1) ns = 1;
@@ -691,10 +708,19 @@ void launch_mha(AttnArgs a, const Plan& p, int B, hipStream_t s) {
     // streams (non-temporal loads, four tokens per stage, about 256
     // workgroups); smaller ones stay cacheable, since the draft steps that
     // share the index set re-read the same rows
-    if (streams_kv(B, a.S_q, a.H_kv, D, a.k))
+    if (streams_kv(B, a.S_q, a.H_kv, D, a.k)) {
+      if constexpr (GQ == 1) {
+        // 16 waves: one workgroup per (sequence, head group) for k <= 2048
+        if (wide_stream(B, a.S_q, a.H_q, a.H_kv, D, a.k)) {
+          hipLaunchKernelGGL((mha_attn_kernel<D, GQ, DSA_ATTN_UNROLL_NT, true, kStreamWaves>), grid,
+                             dim3(kStreamWaves * 64), 0, s, a);
+          return;
+        }
+      }
       hipLaunchKernelGGL((mha_attn_kernel<D, GQ, DSA_ATTN_UNROLL_NT, true>), grid, dim3(kThreads), 0, s, a);
-    else
+    } else {
       hipLaunchKernelGGL((mha_attn_kernel<D, GQ, DSA_ATTN_UNROLL, false>), grid, dim3(kThreads), 0, s, a);
+    }
   }
 }
 

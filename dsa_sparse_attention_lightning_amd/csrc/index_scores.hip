@@ -414,9 +414,11 @@ __global__ __launch_bounds__(kSuperThreads) __attribute__((amdgpu_waves_per_eu(2
   constexpr int EPS = 16 / KS16;                       // epilogue elements per MFMA slot
   constexpr int PF = kSuperPF;                         // stages in flight
   extern __shared__ __align__(16) unsigned char s_k[];   // [2][kSuperPos][KROW]
-  // byte offset of each chunk position's key row; the PF + 1 stages past the
-  // chunk (read ahead, never used) repeat the last position's row
-  __shared__ int64_t s_off[kMaxChunkPositions + (PF + 1) * kSuperPos];
+  // byte offset of each chunk position's key row; the slots past the chunk
+  // (the PF + 1 stages read ahead and never used, and the rounding to whole
+  // fill rounds) hold the chunk's first row
+  constexpr int kTable = (kMaxChunkPositions + (PF + 1) * kSuperPos + NT - 1) / NT * NT;
+  __shared__ int64_t s_off[kTable];
 
   const int b = blockIdx.y;
   const int tid = threadIdx.x;
@@ -424,60 +426,85 @@ __global__ __launch_bounds__(kSuperThreads) __attribute__((amdgpu_waves_per_eu(2
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
-  // Q fragments and weights first (they do not depend on the chunk bounds),
-  // then the row lengths and the block-table entries.  Every load reads a
-  // clamped, valid address and the value is selected afterwards, so the loads
-  // of each group are in flight together (a load under a branch of its own is
-  // waited for before the next one issues).
-  bf16x8_t qa[MBW][KS16];
-  float wr[MBW][16];   // w/2 of the heads this lane's accumulator registers hold
+  // Start-up: every load of the prologue (Q fragments, weights, row lengths,
+  // the block-table entries of this thread's table slots and of its stage-0
+  // key pieces) reads a clamped, valid address and is issued before any of
+  // them is used; the scheduling fence keeps the compiler from pairing each
+  // load with its use, which would wait for the loads one at a time.
+  // Block-table entries are read before the chunk bounds are known; slots
+  // past the chunk's end are replaced below by the chunk's first row.
   const int wrow = b * R + min(wave, R - 1);
+  const int cap = (int)min(ld, (int64_t)max_pages * page);
+  const int t_begin = blockIdx.x * chunk;
+  const int32_t* bt = block_table + (size_t)b * max_pages;
+  constexpr int kFill = kTable / NT;
+  auto pos_c = [&](int t) __attribute__((always_inline)) { return min(t, cap - 1); };
+  // Rows past R and heads past H take a valid row's or head's query (finite
+  // scores) with weight 0, so they add exactly +0.
+  bf16x8_t qa[MBW][KS16];
+  float wraw[MBW][16];
 #pragma unroll
   for (int mb = 0; mb < MBW; ++mb) {
     const int h = mb * 32 + l32;
-    const bool ok = wave < R && h < H;
     const uint16_t* src = q + ((size_t)wrow * H + min(h, H - 1)) * D + hi * 8;
 #pragma unroll
-    for (int ks = 0; ks < KS16; ++ks) {
-      const bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(src + ks * 16);
-      qa[mb][ks] = ok ? v : bf16x8_t{};
-    }
+    for (int ks = 0; ks < KS16; ++ks) qa[mb][ks] = *reinterpret_cast<const bf16x8_t*>(src + ks * 16);
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int hv = mb * 32 + (v / 4) * 8 + hi * 4 + v % 4;
-      const float x = w[(size_t)wrow * H + min(hv, H - 1)];
-      wr[mb][v] = (wave < R && hv < H) ? 0.5f * x : 0.f;
+      wraw[mb][v] = w[(size_t)wrow * H + min(hv, H - 1)];
     }
   }
   const int my_len = row_len[wrow];
-  const int cap = (int)min(ld, (int64_t)max_pages * page);
   int rl[8];
 #pragma unroll
   for (int r = 0; r < 8; ++r) rl[r] = row_len[b * R + min(r, R - 1)];
+  int pbt[kFill];   // this thread's table slots
+#pragma unroll
+  for (int k = 0; k < kFill; ++k) pbt[k] = bt[pos_c(t_begin + tid + k * NT) / page];
+  int sbt[PER];     // this thread's stage-0 key pieces
+#pragma unroll
+  for (int j = 0; j < PER; ++j) sbt[j] = bt[pos_c(t_begin + (tid + j * NT) / (D / 8)) / page];
+  const int fbt = bt[pos_c(t_begin) / page];
+  __builtin_amdgcn_sched_barrier(0);
+
+  float wr[MBW][16];   // w/2 of the heads this lane's accumulator registers hold
+#pragma unroll
+  for (int mb = 0; mb < MBW; ++mb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int hv = mb * 32 + (v / 4) * 8 + hi * 4 + v % 4;
+      wr[mb][v] = (wave < R && hv < H) ? 0.5f * wraw[mb][v] : 0.f;
+    }
+  auto row_at = [&](int e, int t) __attribute__((always_inline)) {
+    return (int)((uint32_t)e * (uint32_t)page + (uint32_t)(pos_c(t) % page));
+  };
+  const int first_row = row_at(fbt, t_begin);
+  int64_t poff[kFill];   // byte offsets of the table slots' rows, selected below
+#pragma unroll
+  for (int k = 0; k < kFill; ++k) poff[k] = (int64_t)row_at(pbt[k], t_begin + tid + k * NT) * (D * 2);
+  int64_t soff[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) soff[j] = (int64_t)row_at(sbt[j], t_begin + (tid + j * NT) / (D / 8)) * (D * 2);
   int lmax = 0;
 #pragma unroll
   for (int r = 0; r < 8; ++r) lmax = max(lmax, min(rl[r], cap));
-  const int t_begin = blockIdx.x * chunk;
-  if (t_begin >= lmax) return;
-  const int t_end = min(t_begin + chunk, lmax);
-  const int32_t* bt = block_table + (size_t)b * max_pages;
-  {
-    constexpr int kFill = (kMaxChunkPositions + (PF + 1) * kSuperPos + NT - 1) / NT;
-    const int len = t_end - t_begin;
-    const int n_pad = ((len + kSuperPos - 1) / kSuperPos + PF + 1) * kSuperPos;
-    int prow[kFill];
+  // No early exit here: a branch on the row lengths is hoisted by the
+  // compiler above the other loads and would serialize two round trips.  A
+  // chunk past every row (only when ld exceeds all row lengths) instead runs
+  // one stage on keys read from the start of q (valid memory; its block-table
+  // entries may not be) and stores nothing.
+  const bool empty = t_begin >= lmax;
+  const int t_end = empty ? t_begin : min(t_begin + chunk, lmax);
+  const int len = t_end - t_begin;
+  const int64_t first_off = empty ? 0 : (int64_t)first_row * (D * 2);
 #pragma unroll
-    for (int k = 0; k < kFill; ++k) {
-      const int t = t_begin + min(tid + k * NT, len - 1);
-      prow[k] = bt[t / page] * page + t % page;
-    }
-#pragma unroll
-    for (int k = 0; k < kFill; ++k)
-      if (tid + k * NT < n_pad) s_off[tid + k * NT] = (int64_t)prow[k] * (D * 2);
+  for (int k = 0; k < kFill; ++k) {
+    const int i = tid + k * NT;
+    s_off[i] = i < len ? poff[k] : first_off;
   }
   // wave w owns row w; after the cross-half sum the low lane half stores it
-  const int t_lim = (wave < R && hi == 0) ? min(t_end, my_len) : 0;
-  __syncthreads();   // s_off ready
+  const int t_lim = (!empty && wave < R && hi == 0) ? min(t_end, my_len) : 0;
 
   struct Slot {
     uint4 v[PER];
@@ -485,7 +512,9 @@ __global__ __launch_bounds__(kSuperThreads) __attribute__((amdgpu_waves_per_eu(2
   // key-row byte offsets of the stage fetched next, read one stage ahead of
   // use; a thread's 16-byte piece of a row is the same in every load
   static_assert(NT % (D / 8) == 0, "each thread keeps one piece of the key rows");
-  const unsigned char* kbase = reinterpret_cast<const unsigned char*>(kidx) + (tid % (D / 8)) * 16;
+  const unsigned char* kbase =
+      reinterpret_cast<const unsigned char*>(empty ? static_cast<const void*>(q) : static_cast<const void*>(kidx)) +
+      (tid % (D / 8)) * 16;
   int64_t koff[PER];
   auto read_rows = [&](int st) __attribute__((always_inline)) {
 #pragma unroll
@@ -497,6 +526,13 @@ __global__ __launch_bounds__(kSuperThreads) __attribute__((amdgpu_waves_per_eu(2
     for (int j = 0; j < PER; ++j) out.v[j] = *reinterpret_cast<const uint4*>(kbase + koff[j]);
     return out;
   };
+  // stage 0's key pieces are fetched from the block-table entries directly,
+  // without waiting for the table
+#pragma unroll
+  for (int j = 0; j < PER; ++j)
+    koff[j] = (tid + j * NT) / (D / 8) < len ? soff[j] : first_off;
+  Slot pre0 = fetch();
+  __syncthreads();   // s_off ready
   const f32x16_t zero{};
   auto epilogue_store = [&](float p, int g) __attribute__((always_inline)) {
     // head sum across the lane halves: lane l gets p(l) + p(l ^ 32)
@@ -579,16 +615,12 @@ __global__ __launch_bounds__(kSuperThreads) __attribute__((amdgpu_waves_per_eu(2
   };
   using first_stage = std::integral_constant<bool, true>;
   using later_stage = std::integral_constant<bool, false>;
-  const int n_st = (t_end - t_begin + kSuperPos - 1) / kSuperPos;
+  const int n_st = max(1, (len + kSuperPos - 1) / kSuperPos);
   if constexpr (PF == 1) {
-    read_rows(0);
-    Slot pre = fetch();
     read_rows(1);
-    pre = step(first_stage{}, pre, 0);
+    Slot pre = step(first_stage{}, pre0, 0);
     for (int st = 1; st < n_st; ++st) pre = step(later_stage{}, pre, st);
   } else {
-    read_rows(0);
-    Slot pre0 = fetch();
     read_rows(1);
     Slot pre1 = fetch();
     read_rows(2);

@@ -99,6 +99,32 @@ def test_index_scores_random_shapes(seed):
             assert np.all(got[b, r, n:] == -7.0)
 
 
+def test_index_scores_chunks_past_every_row():
+    """Score rows far longer than every row length (most workgroups see no
+    position of any row) and a sequence whose rows are all empty: the
+    visible prefixes are bit-exact and nothing past row_len is written, on
+    the one-row, 2-4-row and 5-8-row kernels."""
+    for R in (1, 3, 8):
+        d = I.draft_inputs(71, [3000, 2500], H_I=64, D_I=128, H_q=4, H_kv=4, D_qk=64, D_v=64, k=64, R=R,
+                           page=64, shuffle_pages=True, integer_indexer=True)
+        row_len = d.row_len.copy()
+        for r in range(R):
+            row_len[0, r] = 3000 - 37 * r
+        row_len[1, :] = 0
+        log("index_scores past every row", R, row_len.tolist())
+        dd = DraftDev(d)
+        ld = 60000
+        out = torch.full((d.B, d.R, ld), -7.0, device=DEV)
+        dsa.index_scores(dd.q_index, dd.w, dd.kidx, dd.bt, to_dev(row_len), page=d.page, out=out)
+        got = out.cpu().numpy()
+        for b in range(d.B):
+            ref = O.index_scores(d.q_index[b], d.w[b].astype(np.float64), d.keys[b], row_len[b])
+            for r in range(d.R):
+                n = row_len[b, r]
+                np.testing.assert_array_equal(got[b, r, :n], ref[r, :n].astype(np.float32))
+                assert np.all(got[b, r, n:] == -7.0)
+
+
 def test_index_scores_bf16_normal_bound():
     """Continuous N(0,1) bf16 inputs: error within the fp32 accumulation bound."""
     d = I.draft_inputs(8, [4000], H_I=64, D_I=128, H_q=4, H_kv=4, D_qk=64, D_v=64, k=64)

@@ -88,25 +88,40 @@ __global__ __launch_bounds__(kThreads) void index_scores_kernel(
       // Q fragments in A-operand order (issued after the first key loads so
       // the two round trips overlap): fragment (r, mb, ks), lane l holds head
       // mb*16 + l%16, dims ks*32 + (l/16)*8 .. +8.  Heads >= H are zero.
-      const int nfrag = R * MB * KS * 64;
-      for (int i = tid; i < nfrag; i += kThreads) {
-        const int fl = i & 63;
-        const int f = i >> 6;
-        const int ks = f % KS;
-        const int mb = (f / KS) % MB;
-        const int r = f / (KS * MB);
-        const int h = mb * 16 + (fl & 15);
-        bf16x8_t v = {};
-        if (h < H) {
-          const uint16_t* src = q + ((size_t)(b * R + r) * H + h) * D + ks * 32 + (fl >> 4) * 8;
-          v = *reinterpret_cast<const bf16x8_t*>(src);
+      // Each row's loads read clamped, valid addresses and are masked with
+      // bit operations afterwards, so they are all in flight at once (a load
+      // under a branch or select of its own is waited for before the next).
+      constexpr int kQ = MB * KS * 64;   // fragment slots of one row
+      constexpr int kQPer = (kQ + kThreads - 1) / kThreads;
+      constexpr int kW = MB * 16;
+      for (int r = 0; r < R; ++r) {
+        uint4 v[kQPer];
+        uint32_t keep[kQPer];
+#pragma unroll
+        for (int j = 0; j < kQPer; ++j) {
+          const int i = min(tid + j * kThreads, kQ - 1);
+          const int fl = i & 63;
+          const int f = i >> 6;
+          const int ks = f % KS;
+          const int mb = f / KS;
+          const int h = mb * 16 + (fl & 15);
+          keep[j] = h < H ? ~0u : 0u;
+          v[j] = *reinterpret_cast<const uint4*>(q + ((size_t)(b * R + r) * H + min(h, H - 1)) * D + ks * 32 +
+                                                 (fl >> 4) * 8);
         }
-        qs[i] = v;
-      }
-      for (int i = tid; i < R * MB * 16; i += kThreads) {
-        const int r = i / (MB * 16);
-        const int h = i % (MB * 16);
-        wl[i] = h < H ? w[(size_t)(b * R + r) * H + h] : 0.f;
+        const int wh = tid % kW;
+        const float wv = w[(size_t)(b * R + r) * H + min(wh, H - 1)];
+        __builtin_amdgcn_sched_barrier(0);   // every load above is issued before any is used
+#pragma unroll
+        for (int j = 0; j < kQPer; ++j) {
+          const int i = tid + j * kThreads;
+          if (kQ % kThreads == 0 || i < kQ) {
+            const uint4 m = make_uint4(v[j].x & keep[j], v[j].y & keep[j], v[j].z & keep[j], v[j].w & keep[j]);
+            reinterpret_cast<uint4*>(qs)[r * kQ + i] = m;
+          }
+        }
+        // threads tid, tid + kW, ... store the same weight into the same slot
+        wl[r * kW + wh] = __uint_as_float(__float_as_uint(wv) & (wh < H ? ~0u : 0u));
       }
       __syncthreads();
     }

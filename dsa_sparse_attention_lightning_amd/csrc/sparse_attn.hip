@@ -243,23 +243,35 @@ __global__ __launch_bounds__(W * 64) void mha_attn_kernel(AttnArgs a) {
   const int ntok = min(a.tok_per_split, a.k - t_lo);
   WaveRows wr;
   wr.nw = wave < ntok ? (ntok - wave + W - 1) / W : 0;
-  auto resolve = [&](int j) -> int64_t {
-    if (j >= wr.nw) return -1;
-    const int t = idx[t_lo + wave + j * W];
-    // positions outside the block table (outside the contract) count as absent
-    return (t >= 0 && t / a.page < a.max_pages)
-               ? (int64_t)bt[t / a.page] * a.page_stride + (int64_t)(t % a.page) * a.row_stride
-               : (int64_t)-1;
-  };
-  wr.o0 = resolve(lane);
-  wr.o1 = resolve(lane + 64);
-
-  uint4 qv[GQ];   // this lane's 8 query dims per head, packed bf16 pairs
+  // Both of the lane's tokens at once: the two index loads (clamped inside
+  // the index row) and the query loads, then the two block-table loads
+  // (entry 0 for an absent token), so the start-up is two round trips, not
+  // two per token.  Absent tokens, and positions outside the block table
+  // (outside the contract), resolve to -1.
+  const int ja = t_lo + wave + lane * W;
+  const int jb = ja + 64 * W;
+  const int ta = idx[min(ja, a.k - 1)];
+  const int tb = idx[min(jb, a.k - 1)];
+  uint4 qv[GQ];   // this lane's 8 query dims per head, packed bf16 pairs (0 for a padding head)
+  const uint32_t qkeep = head_ok ? ~0u : 0u;
 #pragma unroll
   for (int j = 0; j < GQ; ++j) {
-    qv[j] = make_uint4(0, 0, 0, 0);
-    if (head_ok) qv[j] = *reinterpret_cast<const uint4*>(a.q + ((size_t)bs * a.H_q + g * GQ + j) * D + sub * 8);
+    const uint4 v =
+        *reinterpret_cast<const uint4*>(a.q + ((size_t)bs * a.H_q + min(g, a.H_kv - 1) * GQ + j) * D + sub * 8);
+    qv[j] = make_uint4(v.x & qkeep, v.y & qkeep, v.z & qkeep, v.w & qkeep);
   }
+  // page and in-page row of each token, computed unconditionally (unsigned)
+  const uint32_t ua = (uint32_t)max(ta, 0), ub = (uint32_t)max(tb, 0);
+  const uint32_t pga = ua / (uint32_t)a.page, pgb = ub / (uint32_t)a.page;
+  const uint32_t ina = ua - pga * (uint32_t)a.page, inb = ub - pgb * (uint32_t)a.page;
+  const bool oka = lane < wr.nw && ta >= 0 && pga < (uint32_t)a.max_pages;
+  const bool okb = lane + 64 < wr.nw && tb >= 0 && pgb < (uint32_t)a.max_pages;
+  const int pa = bt[oka ? pga : 0u];
+  const int pb = bt[okb ? pgb : 0u];
+  const int64_t offa = (int64_t)pa * a.page_stride + (int64_t)ina * a.row_stride;
+  const int64_t offb = (int64_t)pb * a.page_stride + (int64_t)inb * a.row_stride;
+  wr.o0 = oka ? offa : (int64_t)-1;
+  wr.o1 = okb ? offb : (int64_t)-1;
   float m[GQ], l[GQ], acc[GQ][8];
 #pragma unroll
   for (int j = 0; j < GQ; ++j) {

@@ -384,15 +384,19 @@ __global__ __launch_bounds__(NWAVE * 64) __attribute__((amdgpu_waves_per_eu(DSA_
 }
 
 // Five to eight rows: eight waves, one query row each (Q fragments 64 VGPRs,
-// head weights 32, two accumulator sets 64), two waves per SIMD.  Key tiles
+// head weights 16, two accumulator sets 64), two waves per SIMD.  Key tiles
 // are staged in LDS four at a time (128 positions per barrier; the next
 // stage's loads are in flight in registers while the current one is used:
 // one stage ahead measured 2 % faster than two, with 24 fewer VGPRs), and
 // each wave software-pipelines its tiles: the
 // MFMAs of tile i issue while its VALU runs the epilogue of tile i-1 out of
 // the other accumulator set, with the weights in registers (no LDS access in
-// the epilogue).  Same arithmetic, in the same order, as
-// index_scores_rows_kernel.
+// the epilogue).  The contraction runs on v_mfma_f32_16x16x32_bf16 (four
+// 16-head blocks x two 16-position blocks per 32-position tile): on
+// full-mantissa operands, where the chip clocks down under MFMA load, it
+// sustains 10-20 % more than the 32x32x16 form (register-only loops), and
+// this kernel runs about 1-2 % faster with it.  Same ReLU * w epilogue as
+// index_scores_rows_kernel; the head sum is taken in a different order.
 #ifndef DSA_INDEX_SUPER_WGS
 #define DSA_INDEX_SUPER_WGS 256
 #endif
@@ -418,15 +422,18 @@ __global__ __launch_bounds__(kSuperThreads) __attribute__((amdgpu_waves_per_eu(2
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ row_len, float* __restrict__ scores,
     int R, int H, int page, int max_pages, int64_t ld, int chunk) {
   constexpr int NT = kSuperThreads;
-  constexpr int MBW = 2;                               // 32-head M blocks of the wave's row
+  constexpr int MB = 4;                                // 16-head M blocks of the wave's row
+  constexpr int NB = kRowsTile / 16;                   // 16-position N blocks of a tile
   constexpr int D = KS16 * 16;
+  constexpr int KS = D / 32;                           // 32-wide K steps
+  static_assert(KS >= 1, "D_I is a multiple of 32");
   constexpr int KROW = D * 2 + 16;                     // padded LDS row (bytes)
   constexpr int CHUNKS = kSuperPos * D / 8;            // 16-byte pieces per stage
   static_assert(CHUNKS % NT == 0, "stage pieces must divide evenly");
   static_assert(kSuperTiles == 2 || kSuperTiles == 4 || kSuperTiles == 8, "2, 4 or 8 tiles per stage");
   static_assert(kMaxChunkPositions % kSuperPos == 0, "chunks are whole stages");
   constexpr int PER = CHUNKS / NT;
-  constexpr int EPS = 16 / KS16;                       // epilogue elements per MFMA slot
+  constexpr int EPS = 32 / (KS * NB * MB);             // epilogue elements per MFMA slot
   constexpr int PF = kSuperPF;                         // stages in flight
   extern __shared__ __align__(16) unsigned char s_k[];   // [2][kSuperPos][KROW]
   // byte offset of each chunk position's key row; the slots past the chunk
@@ -439,8 +446,8 @@ __global__ __launch_bounds__(kSuperThreads) __attribute__((amdgpu_waves_per_eu(2
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
-  const int l32 = lane & 31;
-  const int hi = lane >> 5;
+  const int l16 = lane & 15;   // 16x16x32 layout: A row / B column / C column
+  const int g4 = lane >> 4;    // K group (A, B) and C row group
   // Start-up: every load of the prologue (Q fragments, weights, row lengths,
   // the block-table entries of this thread's table slots and of its stage-0
   // key pieces) reads a clamped, valid address and is issued before any of
@@ -456,19 +463,18 @@ __global__ __launch_bounds__(kSuperThreads) __attribute__((amdgpu_waves_per_eu(2
   auto pos_c = [&](int t) __attribute__((always_inline)) { return min(t, cap - 1); };
   // Rows past R and heads past H take a valid row's or head's query (finite
   // scores) with weight 0, so they add exactly +0.
-  bf16x8_t qa[MBW][KS16];
-  float wraw[MBW][16];
+  // A fragment (mb, ks): lane l holds head mb*16 + l%16, dims ks*32 +
+  // (l/16)*8 .. +8.  C register i of block mb holds head mb*16 + (l/16)*4 + i.
+  bf16x8_t qa[MB][KS];
+  float wraw[MB][4];
 #pragma unroll
-  for (int mb = 0; mb < MBW; ++mb) {
-    const int h = mb * 32 + l32;
-    const uint16_t* src = q + ((size_t)wrow * H + min(h, H - 1)) * D + hi * 8;
+  for (int mb = 0; mb < MB; ++mb) {
+    const int h = mb * 16 + l16;
+    const uint16_t* src = q + ((size_t)wrow * H + min(h, H - 1)) * D + g4 * 8;
 #pragma unroll
-    for (int ks = 0; ks < KS16; ++ks) qa[mb][ks] = *reinterpret_cast<const bf16x8_t*>(src + ks * 16);
+    for (int ks = 0; ks < KS; ++ks) qa[mb][ks] = *reinterpret_cast<const bf16x8_t*>(src + ks * 32);
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int hv = mb * 32 + (v / 4) * 8 + hi * 4 + v % 4;
-      wraw[mb][v] = w[(size_t)wrow * H + min(hv, H - 1)];
-    }
+    for (int i = 0; i < 4; ++i) wraw[mb][i] = w[(size_t)wrow * H + min(mb * 16 + g4 * 4 + i, H - 1)];
   }
   const int my_len = row_len[wrow];
   int rl[8];
@@ -483,13 +489,13 @@ __global__ __launch_bounds__(kSuperThreads) __attribute__((amdgpu_waves_per_eu(2
   const int fbt = bt[pos_c(t_begin) / page];
   __builtin_amdgcn_sched_barrier(0);
 
-  float wr[MBW][16];   // w/2 of the heads this lane's accumulator registers hold
+  float wr[MB][4];   // w/2 of the heads this lane's accumulator registers hold
 #pragma unroll
-  for (int mb = 0; mb < MBW; ++mb)
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int hv = mb * 32 + (v / 4) * 8 + hi * 4 + v % 4;
-      wr[mb][v] = (wave < R && hv < H) ? 0.5f * wraw[mb][v] : 0.f;
+    for (int i = 0; i < 4; ++i) {
+      const int hv = mb * 16 + g4 * 4 + i;
+      wr[mb][i] = (wave < R && hv < H) ? 0.5f * wraw[mb][i] : 0.f;
     }
   auto row_at = [&](int e, int t) __attribute__((always_inline)) {
     return (int)((uint32_t)e * (uint32_t)page + (uint32_t)(pos_c(t) % page));
@@ -518,8 +524,10 @@ __global__ __launch_bounds__(kSuperThreads) __attribute__((amdgpu_waves_per_eu(2
     const int i = tid + k * NT;
     s_off[i] = i < len ? poff[k] : first_off;
   }
-  // wave w owns row w; after the cross-half sum the low lane half stores it
-  const int t_lim = (!empty && wave < R && hi == 0) ? min(t_end, my_len) : 0;
+  // wave w owns row w; after the head sum, lane groups 0 and 2 store the
+  // tile's two 16-position blocks
+  const int tpos = (g4 >> 1) * 16 + l16;
+  const int t_lim = (!empty && wave < R && (g4 & 1) == 0) ? min(t_end, my_len) : 0;
 
   struct Slot {
     uint4 v[PER];
@@ -548,55 +556,69 @@ __global__ __launch_bounds__(kSuperThreads) __attribute__((amdgpu_waves_per_eu(2
     koff[j] = (tid + j * NT) / (D / 8) < len ? soff[j] : first_off;
   Slot pre0 = fetch();
   __syncthreads();   // s_off ready
-  const f32x16_t zero{};
-  auto epilogue_store = [&](float p, int g) __attribute__((always_inline)) {
-    // head sum across the lane halves: lane l gets p(l) + p(l ^ 32)
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p), __float_as_uint(p), false, false);
-    const float v = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    const int t = t_begin + g * kRowsTile + l32;
+  const f32x4_t zero{};
+  // p0, p1: this lane's partial head sums (16 heads) of positions l%16 of
+  // the tile's two blocks; the four lane groups hold disjoint heads
+  auto epilogue_store = [&](float p0, float p1, int g) __attribute__((always_inline)) {
+    // lanes 0-31 add groups (0,2) and (1,3) of block 0, lanes 32-63 those of
+    // block 1; then lane l adds lane l ^ 16: all four groups
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p1), false, false);
+    float v = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    v += __shfl_xor(v, 16, 64);
+    const int t = t_begin + g * kRowsTile + tpos;
     // scores are not re-read here: non-temporal stores (measured 4-5 % faster
     // than stores that allocate in the last-level cache)
     if (t < t_lim) __builtin_nontemporal_store(v, &scores[(size_t)(b * R + wave) * ld + t]);
   };
-  auto epi_elem = [&](const f32x16_t (&accP)[MBW], int e, float& p) __attribute__((always_inline)) {
-    const int mb = e / 16, v = e % 16;
-    const float x = accP[mb][v];
+  // element e of a tile's accumulators: block nb = e/16, head block
+  // mb = (e/4)%4, register e%4
+  auto epi_elem = [&](const f32x4_t (&accP)[NB * MB], int e, float& p0, float& p1) __attribute__((always_inline)) {
+    const int nb = e / 16, mb = (e / 4) % MB, i = e % 4;
+    const float x = accP[nb * MB + mb][i];
     // (x + |x|) * (w/2) equals w * ReLU(x) exactly
-    p = fmaf(wr[mb][v], x + fabsf(x), p);
+    if (nb == 0) p0 = fmaf(wr[mb][i], x + fabsf(x), p0);
+    else p1 = fmaf(wr[mb][i], x + fabsf(x), p1);
   };
-  // B fragments of a stage are read in order f = u * KS16 + ks (tile u,
-  // k step ks) through a ring, BPF fragments ahead of their MFMAs
+  // B fragments of a stage are read in order f = (u * KS + ks) * NB + nb
+  // (tile u, k step ks, block nb) through a ring, BPF fragments ahead of
+  // their MFMAs; fragment (nb, ks): lane l holds position nb*16 + l%16,
+  // dims ks*32 + (l/16)*8 .. +8
   constexpr int BPF = 2;
-  constexpr int NF = kSuperTiles * KS16;
+  constexpr int NF = kSuperTiles * KS * NB;
   bf16x8_t kf[BPF + 1];
   auto frag = [&](const unsigned char* bbase, int f) __attribute__((always_inline)) {
-    return *reinterpret_cast<const bf16x8_t*>(bbase + (f / KS16) * kRowsTile * KROW + (f % KS16) * 32);
+    const int u = f / (KS * NB), ks = (f / NB) % KS, nb = f % NB;
+    return *reinterpret_cast<const bf16x8_t*>(bbase + (u * kRowsTile + nb * 16) * KROW + ks * 64);
   };
   // tile U of the stage (global tile g): MFMAs into accC and, interleaved
   // with them, the epilogue of tile g-1 out of accP
-  auto tile = [&](auto has_prev, auto u_c, const unsigned char* bbase, int g, f32x16_t (&accC)[MBW],
-                  f32x16_t (&accP)[MBW]) __attribute__((always_inline)) {
+  auto tile = [&](auto has_prev, auto u_c, const unsigned char* bbase, int g, f32x4_t (&accC)[NB * MB],
+                  f32x4_t (&accP)[NB * MB]) __attribute__((always_inline)) {
     constexpr bool EPI = decltype(has_prev)::value;
     constexpr int U = decltype(u_c)::value;
-    float p = 0.f;
+    float p0 = 0.f, p1 = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < KS16; ++ks) {
-      const int f = U * KS16 + ks;
-      if (f + BPF < NF) kf[(f + BPF) % (BPF + 1)] = frag(bbase, f + BPF);
+    for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-      for (int mb = 0; mb < MBW; ++mb) {
-        accC[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mb][ks], kf[f % (BPF + 1)], ks == 0 ? zero : accC[mb], 0, 0, 0);
-        if constexpr (EPI) {
+      for (int nb = 0; nb < NB; ++nb) {
+        const int f = (U * KS + ks) * NB + nb;
+        if (f + BPF < NF) kf[(f + BPF) % (BPF + 1)] = frag(bbase, f + BPF);
 #pragma unroll
-          for (int e = 0; e < EPS; ++e) epi_elem(accP, (ks * MBW + mb) * EPS + e, p);
+        for (int mb = 0; mb < MB; ++mb) {
+          accC[nb * MB + mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mb][ks], kf[f % (BPF + 1)],
+                                                                        ks == 0 ? zero : accC[nb * MB + mb], 0, 0, 0);
+          if constexpr (EPI) {
+#pragma unroll
+            for (int e = 0; e < EPS; ++e) epi_elem(accP, ((ks * NB + nb) * MB + mb) * EPS + e, p0, p1);
+          }
         }
       }
     }
-    if constexpr (EPI) epilogue_store(p, g - 1);
+    if constexpr (EPI) epilogue_store(p0, p1, g - 1);
   };
   using no_prev = std::integral_constant<bool, false>;
   using with_prev = std::integral_constant<bool, true>;
-  f32x16_t accA[MBW], accB[MBW];
+  f32x4_t accA[NB * MB], accB[NB * MB];
   // one stage: store it to LDS, prefetch PF stages ahead, run its four tiles
   // (even tiles in set A, odd in set B)
   auto step = [&](auto first, Slot slot, int st) __attribute__((always_inline)) {
@@ -609,7 +631,7 @@ __global__ __launch_bounds__(kSuperThreads) __attribute__((amdgpu_waves_per_eu(2
     __syncthreads();
     const Slot next = fetch();   // stage st + PF (rows read last step)
     read_rows(st + PF + 1);
-    const unsigned char* bbase = buf + l32 * KROW + hi * 16;
+    const unsigned char* bbase = buf + l16 * KROW + g4 * 16;
 #pragma unroll
     for (int f = 0; f < BPF; ++f) kf[f] = frag(bbase, f);
     const int g = st * kSuperTiles;
@@ -648,10 +670,10 @@ __global__ __launch_bounds__(kSuperThreads) __attribute__((amdgpu_waves_per_eu(2
     if (st < n_st) step(later_stage{}, pre1, st);
   }
   // the last tile (odd index) is still in set B
-  float p = 0.f;
+  float p0 = 0.f, p1 = 0.f;
 #pragma unroll
-  for (int e = 0; e < MBW * 16; ++e) epi_elem(accB, e, p);
-  epilogue_store(p, n_st * kSuperTiles - 1);
+  for (int e = 0; e < 32; ++e) epi_elem(accB, e, p0, p1);
+  epilogue_store(p0, p1, n_st * kSuperTiles - 1);
 }
 
 template <int KS16>

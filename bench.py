@@ -230,8 +230,9 @@ def measure_peaks(reps=10):
     if not os.path.exists(path):
         return {}
     lib = ctypes.CDLL(path)
-    lib.dsa_bench_mfma_peak.restype = ctypes.c_int
-    lib.dsa_bench_mfma_peak.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    for fn in (lib.dsa_bench_mfma_peak, lib.dsa_bench_mfma16_peak):
+        fn.restype = ctypes.c_int
+        fn.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.dsa_bench_stream.restype = ctypes.c_int
     lib.dsa_bench_stream.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_longlong,
                                      ctypes.c_int, ctypes.c_void_p]
@@ -254,14 +255,24 @@ def measure_peaks(reps=10):
     blocks, iters = 256 * 8, 4096
     out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda:0")
 
-    def mfma():
+    def mfma32():
         assert lib.dsa_bench_mfma_peak(out.data_ptr(), blocks, iters, cur()) == 0
 
+    blocks16, iters16 = 256, 1024   # 512-thread workgroups, one per CU
+
+    def mfma16():
+        assert lib.dsa_bench_mfma16_peak(out.data_ptr(), blocks16, iters16, cur()) == 0
+
     flops = blocks * 4 * iters * 4 * 2 * 32 * 32 * 16
-    peaks["mfma_bf16_TFLOPs"] = flops / time_warm(mfma, reps=reps, inner=1) / 1e6
+    flops16 = blocks16 * 8 * iters16 * 32 * 2 * 16 * 16 * 32
+    peaks["mfma_bf16_32x32x16_TFLOPs"] = flops / time_warm(mfma32, reps=reps, inner=1) / 1e6
+    peaks["mfma_bf16_16x16x32_TFLOPs"] = flops16 / time_warm(mfma16, reps=reps, inner=1) / 1e6
+    peaks["mfma_bf16_TFLOPs"] = max(peaks["mfma_bf16_32x32x16_TFLOPs"], peaks["mfma_bf16_16x16x32_TFLOPs"])
     peaks["probes"] = ("libdsa_bench.so: 2 GiB stream, 16-byte non-temporal loads (copy: and stores), 2048 "
-                       "workgroups each on a contiguous chunk; register-only v_mfma_f32_32x32x16_bf16 loop on "
-                       "pseudo-random full-mantissa bf16 operands, 4 chains per wave, 8 waves per CU")
+                       "workgroups each on a contiguous chunk; register-only v_mfma_f32_32x32x16_bf16 and "
+                       "v_mfma_f32_16x16x32_bf16 loops on pseudo-random full-mantissa bf16 operands, 4 chains "
+                       "per wave, 8 waves per CU, accumulators in AGPRs and in ArchVGPRs respectively "
+                       "(mfma_bf16_TFLOPs: the higher of the two)")
     torch.cuda.empty_cache()
     return peaks
 

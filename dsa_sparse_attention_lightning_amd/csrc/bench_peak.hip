@@ -1,8 +1,10 @@
 // Measurement probes for the benchmark (libdsa_bench.so; not part of the
 // draft-and-verify path and not linked into libdsa.so):
 //   * the dense bf16 MFMA rate this chip sustains on full-mantissa operands,
-//     from a register-only loop of v_mfma_f32_32x32x16_bf16 with four
-//     independent accumulation chains per wave and no memory traffic;
+//     from register-only loops of v_mfma_f32_32x32x16_bf16 and of
+//     v_mfma_f32_16x16x32_bf16, four independent accumulation chains per
+//     wave and no memory traffic (the 16x16x32 form sustains more on such
+//     data, where the chip clocks down under MFMA load);
 //   * the HBM read and copy bandwidth it sustains: every workgroup streams
 //     its own contiguous chunk with 16-byte non-temporal loads (and stores).
 // The benchmark reports each kernel's rate against these measured peaks next
@@ -50,6 +52,34 @@ __global__ __launch_bounds__(kThreads) void mfma_peak_kernel(float* __restrict__
   out[(size_t)blockIdx.x * kThreads + threadIdx.x] = s;
 }
 
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+
+// 16x16x32: eight waves per workgroup, two per SIMD, accumulators in
+// ArchVGPRs (the form the kernels use; the AGPR form sustains less here),
+// eight distinct A and B operands cycling over four chains.
+constexpr int kThreads16 = 512;
+__global__ __launch_bounds__(kThreads16) __attribute__((amdgpu_waves_per_eu(2, 2))) void mfma16_peak_kernel(
+    float* __restrict__ out, int iters) {
+  bf16x8_t a[8], b[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t h = mix(threadIdx.x * 131u + blockIdx.x * 7919u + j * 17u + e);
+      a[j][e] = (__bf16)(((float)(h & 0xffffu) / 32768.f - 1.f) * 1.7f);
+      b[j][e] = (__bf16)(((float)(h >> 16) / 32768.f - 1.f) * 1.3f);
+    }
+  f32x4_t c[4] = {};
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int j = 0; j < 32; ++j) c[j % 4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[(j + j % 4) & 7], b[(j / 4) & 7], c[j % 4], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) s += (c[k][0] + c[k][1]) + (c[k][2] + c[k][3]);
+  out[(size_t)blockIdx.x * kThreads16 + threadIdx.x] = s;
+}
+
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kStreamThreads = 256;
 constexpr int kStreamU = 8;     // 16-byte loads in flight per thread
@@ -91,6 +121,15 @@ extern "C" int dsa_bench_stream(const void* src, void* dst, void* out, long long
   hipLaunchKernelGGL(stream_kernel, dim3(blocks), dim3(kStreamThreads), 0, static_cast<hipStream_t>(stream),
                      static_cast<const u32x4_t*>(src), static_cast<u32x4_t*>(dst), static_cast<uint32_t*>(out), n,
                      per_wg);
+  return (int)hipGetLastError();
+}
+
+// FLOPs of one call: blocks * 8 waves * iters * 32 MFMAs * 2*16*16*32.
+// out: fp32 [blocks * 512] device buffer.  Returns a hipError_t code.
+extern "C" int dsa_bench_mfma16_peak(float* out, int blocks, int iters, void* stream) {
+  if (!out || blocks < 1 || iters < 1) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(mfma16_peak_kernel, dim3(blocks), dim3(kThreads16), 0, static_cast<hipStream_t>(stream), out,
+                     iters);
   return (int)hipGetLastError();
 }
 

@@ -160,15 +160,17 @@ __global__ __launch_bounds__(kStatThreads) void verify_stats_kernel(VerifyArgs a
     for (int u = 0; u < kStatU; ++u) bm = fmaxf(bm, fmaxf(fmaxf(x[u].x, x[u].y), fmaxf(x[u].z, x[u].w)));
     const float M = fmaxf(m, bm);
     if (M == -INFINITY) continue;   // nothing but -inf logits so far
-    // exp(x - M) as 2^((x - M) log2 e): the difference is formed first, so
-    // the largest terms (x near M) carry no rounding from the scaling
+    // exp(x - M) as 2^(x log2 e - M log2 e), one FMA per logit (the
+    // exponent carries at most half an ulp of M log2 e: a relative error
+    // below 3e-6 for |M| < 100)
+    const float Mc = M * kLog2e;
     float t = 0.f;
 #pragma unroll
     for (int u = 0; u < kStatU; ++u) {
-      t += fast_exp2((x[u].x - M) * kLog2e);
-      t += fast_exp2((x[u].y - M) * kLog2e);
-      t += fast_exp2((x[u].z - M) * kLog2e);
-      t += fast_exp2((x[u].w - M) * kLog2e);
+      t += fast_exp2(fmaf(x[u].x, kLog2e, -Mc));
+      t += fast_exp2(fmaf(x[u].y, kLog2e, -Mc));
+      t += fast_exp2(fmaf(x[u].z, kLog2e, -Mc));
+      t += fast_exp2(fmaf(x[u].w, kLog2e, -Mc));
     }
     s = s * fast_exp2((m - M) * kLog2e) + t;
     m = M;
@@ -189,23 +191,35 @@ __global__ __launch_bounds__(kStatThreads) void verify_stats_kernel(VerifyArgs a
   }
 }
 
-// Weight of logit e of the sampled row (0 beyond V).
+// Weight of logit e of the sampled row (0 beyond V): p = softmax(t)_e and
+// q = softmax(d)_e as 2^(x log2 e - o) with o = max * log2 e + log2(sum of
+// exp(x - max)), one FMA and one exp2 each (the offsets are computed once per
+// sequence).
 struct RowWeights {
   const float* t;   // target row
   const float* d;   // draft row (residual) or nullptr (plain softmax of t)
-  float mt, inv_zt, md, inv_zd;
+  float ot, od;     // log2-domain offsets of the two rows
   __device__ __forceinline__ float w(float tv, float dv) const {
-    const float p = __expf(tv - mt) * inv_zt;
+    const float p = fast_exp2(fmaf(tv, kLog2e, -ot));
     if (!d) return p;
-    const float q = __expf(dv - md) * inv_zd;
+    const float q = fast_exp2(fmaf(dv, kLog2e, -od));
     return fmaxf(p - q, 0.f);
   }
 };
+
+__device__ __forceinline__ float row_offset(float m, float z) { return m * kLog2e + log2f(z); }
 
 __device__ __forceinline__ float wave_incl_scan(float v) { return wave_incl_scan_dpp(v); }
 
 __device__ __forceinline__ void weights4(const RowWeights& rw, const float4& tv, const float4& dv, int e, int V,
                                          float wv[4]) {
+  if (e + 3 < V) {   // whole quad inside the row: no per-logit checks
+    wv[0] = rw.w(tv.x, dv.x);
+    wv[1] = rw.w(tv.y, dv.y);
+    wv[2] = rw.w(tv.z, dv.z);
+    wv[3] = rw.w(tv.w, dv.w);
+    return;
+  }
   wv[0] = e + 0 < V ? rw.w(tv.x, dv.x) : 0.f;
   wv[1] = e + 1 < V ? rw.w(tv.y, dv.y) : 0.f;
   wv[2] = e + 2 < V ? rw.w(tv.z, dv.z) : 0.f;
@@ -228,8 +242,8 @@ __device__ __forceinline__ void tile_weights(const RowWeights& rw, int e, int V,
 struct Decision {
   int jstar;
   float us;
-  float mt, inv_zt, md, inv_zd;
-  int pad0, pad1;
+  float ot, od;     // RowWeights offsets of the sampled rows
+  int pad0, pad1, pad2, pad3;
 };
 
 constexpr int kDecideThreads = 256;
@@ -333,15 +347,12 @@ __device__ __forceinline__ RowWeights sampled_row(const VerifyArgs& a, int b, in
                                                   const float* s_z) {
   RowWeights rw;
   rw.t = a.tl + ((size_t)b * (a.G + 1) + jstar) * a.V;
-  rw.mt = s_m[jstar];
-  rw.inv_zt = 1.f / s_z[jstar];
+  rw.ot = row_offset(s_m[jstar], s_z[jstar]);
   rw.d = nullptr;
-  rw.md = 0.f;
-  rw.inv_zd = 0.f;
+  rw.od = 0.f;
   if (jstar < a.G) {
     rw.d = a.dl + ((size_t)b * a.G + jstar) * a.V;
-    rw.md = s_m[a.G + 1 + jstar];
-    rw.inv_zd = 1.f / s_z[a.G + 1 + jstar];
+    rw.od = row_offset(s_m[a.G + 1 + jstar], s_z[a.G + 1 + jstar]);
   }
   return rw;
 }
@@ -434,11 +445,9 @@ __global__ __launch_bounds__(kDecideThreads) void verify_decide_kernel(VerifyArg
     Decision dd;
     dd.jstar = s_jstar;
     dd.us = s_us;
-    dd.mt = rw.mt;
-    dd.inv_zt = rw.inv_zt;
-    dd.md = rw.md;
-    dd.inv_zd = rw.inv_zd;
-    dd.pad0 = dd.pad1 = 0;
+    dd.ot = rw.ot;
+    dd.od = rw.od;
+    dd.pad0 = dd.pad1 = dd.pad2 = dd.pad3 = 0;
     ws.dec[b] = dd;
   }
 }
@@ -447,11 +456,9 @@ __global__ __launch_bounds__(kDecideThreads) void verify_decide_kernel(VerifyArg
 __device__ __forceinline__ RowWeights decided_row(const VerifyArgs& a, const Decision& dd, int b) {
   RowWeights rw;
   rw.t = a.tl + ((size_t)b * (a.G + 1) + dd.jstar) * a.V;
-  rw.mt = dd.mt;
-  rw.inv_zt = dd.inv_zt;
+  rw.ot = dd.ot;
   rw.d = dd.jstar < a.G ? a.dl + ((size_t)b * a.G + dd.jstar) * a.V : nullptr;
-  rw.md = dd.md;
-  rw.inv_zd = dd.inv_zd;
+  rw.od = dd.od;
   return rw;
 }
 
@@ -476,11 +483,9 @@ __global__ __launch_bounds__(kMassThreads) void verify_mass_kernel(VerifyArgs a,
       Decision dd;
       dd.jstar = s_jstar;
       dd.us = s_us;
-      dd.mt = rw.mt;
-      dd.inv_zt = rw.inv_zt;
-      dd.md = rw.md;
-      dd.inv_zd = rw.inv_zd;
-      dd.pad0 = dd.pad1 = 0;
+      dd.ot = rw.ot;
+      dd.od = rw.od;
+      dd.pad0 = dd.pad1 = dd.pad2 = dd.pad3 = 0;
       ws.dec[b] = dd;
     }
   } else {

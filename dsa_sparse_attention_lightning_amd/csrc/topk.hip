@@ -572,6 +572,12 @@ constexpr int kOneMaxLd = DSA_TOPK_ONE_MAX_LD;   // longest row the one-workgrou
 static_assert(kOneMaxLd <= kOneLdsKeys, "the one-workgroup path holds a whole row of keys in LDS");
 
 constexpr int kOneCand = kBins / 4;    // threshold-bin candidates resolved in LDS (first half of hist)
+// The candidates are ranked pairwise (one thread each against all), which
+// costs O(n^2): past 256 another 12-bit histogram pass is cheaper (a 32K row
+// of N(0,1) scores leaves ~500 in its first threshold bin: 40.4 -> 24.2 us
+// with the extra pass; indexer scores, whose bins are small, are unchanged).
+constexpr int kOneFast = 256;
+static_assert(kOneFast <= kOneCand, "the fast path's candidates fit");
 constexpr int kOneWords = (kOneLdsKeys + 63) / 64;   // kept-position bitmap (second half of hist)
 static_assert(kOneCand * 8 + kOneWords * 8 <= kBins * 4, "candidates and bitmap share the histogram");
 static_assert(kOneWords <= kOneThreads, "one bitmap word per thread");
@@ -713,7 +719,7 @@ __global__ __launch_bounds__(kOneThreads) void topk_one_kernel(const float* __re
     const uint32_t cnt = sh.count;
     __syncthreads();
     if (cnt == need) break;
-    if (cnt <= (uint32_t)kOneCand) {
+    if (cnt <= (uint32_t)kOneFast) {
       fast = true;
       break;
     }

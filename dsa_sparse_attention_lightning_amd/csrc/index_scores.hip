@@ -461,8 +461,8 @@ __global__ __launch_bounds__(kSuperThreads) __attribute__((amdgpu_waves_per_eu(2
   const int32_t* bt = block_table + (size_t)b * max_pages;
   constexpr int kFill = kTable / NT;
   auto pos_c = [&](int t) __attribute__((always_inline)) { return min(t, cap - 1); };
-  // Rows past R and heads past H take a valid row's or head's query (finite
-  // scores) with weight 0, so they add exactly +0.
+  // Rows past R read a valid row's query (never stored); heads past H read a
+  // valid head's query, zeroed after the fence, with weight 0.
   // A fragment (mb, ks): lane l holds head mb*16 + l%16, dims ks*32 +
   // (l/16)*8 .. +8.  C register i of block mb holds head mb*16 + (l/16)*4 + i.
   bf16x8_t qa[MB][KS];
@@ -491,12 +491,19 @@ __global__ __launch_bounds__(kSuperThreads) __attribute__((amdgpu_waves_per_eu(2
 
   float wr[MB][4];   // w/2 of the heads this lane's accumulator registers hold
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
+  for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int hv = mb * 16 + g4 * 4 + i;
       wr[mb][i] = (wave < R && hv < H) ? 0.5f * wraw[mb][i] : 0.f;
     }
+    const uint32_t keep = mb * 16 + l16 < H ? ~0u : 0u;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint4 v = __builtin_bit_cast(uint4, qa[mb][ks]);
+      qa[mb][ks] = __builtin_bit_cast(bf16x8_t, make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep));
+    }
+  }
   auto row_at = [&](int e, int t) __attribute__((always_inline)) {
     return (int)((uint32_t)e * (uint32_t)page + (uint32_t)(pos_c(t) % page));
   };

@@ -125,6 +125,33 @@ def test_index_scores_chunks_past_every_row():
                 assert np.all(got[b, r, n:] == -7.0)
 
 
+def test_index_scores_overflow_with_padding_heads():
+    """A key row whose dot products overflow fp32 (its scores are +inf in the
+    oracle's float64-then-float32 result) with H_I = 20, so every kernel pads
+    heads inside its head blocks: the padding heads must add exactly 0, never
+    0 * inf = NaN; on the one-row, 2-4-row and 5-8-row kernels."""
+    for R in (1, 3, 8):
+        d = I.draft_inputs(73, [600], H_I=20, D_I=128, H_q=4, H_kv=4, D_qk=64, D_v=64, k=64, R=R, page=64,
+                           shuffle_pages=True, integer_indexer=True)
+        log("index_scores overflow", R)
+        d.q_index_bits[...] = 0x3F80                   # every query component 1.0
+        d.q_index[...] = 1.0
+        d.w[...] = np.maximum(d.w, np.float32(1 / 64))   # positive weights
+        t = 100
+        d.keys[0][t, :] = 2.0 ** 126                    # 128 * 2^126 = 2^133 overflows fp32
+        d.kidx_bits[d.block_table[0, t // d.page], t % d.page, :] = 0x7E80
+        dd = DraftDev(d)
+        out = torch.full((d.B, d.R, dd.ld), -7.0, device=DEV)
+        dsa.index_scores(dd.q_index, dd.w, dd.kidx, dd.bt, dd.row_len, page=d.page, out=out)
+        got = out.cpu().numpy()
+        with np.errstate(over="ignore"):
+            ref = O.index_scores(d.q_index[0], d.w[0].astype(np.float64), d.keys[0], d.row_len[0]).astype(np.float32)
+        for r in range(d.R):
+            n = d.row_len[0, r]
+            assert np.isposinf(got[0, r, t]) and np.isposinf(ref[r, t])
+            np.testing.assert_array_equal(got[0, r, :n], ref[r, :n])
+
+
 def test_index_scores_bf16_normal_bound():
     """Continuous N(0,1) bf16 inputs: error within the fp32 accumulation bound."""
     d = I.draft_inputs(8, [4000], H_I=64, D_I=128, H_q=4, H_kv=4, D_qk=64, D_v=64, k=64)

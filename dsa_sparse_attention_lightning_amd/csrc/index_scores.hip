@@ -568,10 +568,13 @@ __global__ __launch_bounds__(kSuperThreads) __attribute__((amdgpu_waves_per_eu(2
   // the tile's two blocks; the four lane groups hold disjoint heads
   auto epilogue_store = [&](float p0, float p1, int g) __attribute__((always_inline)) {
     // lanes 0-31 add groups (0,2) and (1,3) of block 0, lanes 32-63 those of
-    // block 1; then lane l adds lane l ^ 16: all four groups
+    // block 1; then lane l adds lane l ^ 16: all four groups.  Both
+    // exchanges are VALU lane swaps (a shuffle through the LDS crossbar
+    // would wait for the fragment reads in flight).
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p1), false, false);
-    float v = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    v += __shfl_xor(v, 16, 64);
+    const float v1 = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    const auto sw16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v1), __float_as_uint(v1), false, false);
+    const float v = __uint_as_float(sw16[0]) + __uint_as_float(sw16[1]);
     const int t = t_begin + g * kRowsTile + tpos;
     // scores are not re-read here: non-temporal stores (measured 4-5 % faster
     // than stores that allocate in the last-level cache)

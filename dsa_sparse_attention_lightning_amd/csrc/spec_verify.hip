@@ -26,6 +26,9 @@
 //           then the token inside the tile.
 // Uniforms come from the caller or from Philox4x64-10 (Salmon, Moraes, Dror,
 // Shaw, SC'11) evaluated in-kernel at counter (offset, b, j, stream).
+#include <cstdlib>
+#include <cstring>
+
 #include "dsa_common.h"
 
 namespace dsa {
@@ -47,6 +50,23 @@ constexpr int kArgStep = kArgThreads * 4;
 #define DSA_VERIFY_STAT_TARGET_WGS 512
 #endif
 constexpr int kStatTargetWgs = DSA_VERIFY_STAT_TARGET_WGS;
+// Early-exit (phased) verification: one launch per position, each reading
+// only the rows of the sequences whose chain is still accepted.  It replaces
+// the one-pass stats when the batch's logits reach this size (G more
+// launches against the rows after each first rejection left unread).
+#ifndef DSA_VERIFY_PHASED_MIN_MB
+#define DSA_VERIFY_PHASED_MIN_MB 1024
+#endif
+constexpr size_t kPhasedMinBytes = (size_t)DSA_VERIFY_PHASED_MIN_MB << 20;
+#ifndef DSA_VERIFY_PHASE_U
+#define DSA_VERIFY_PHASE_U 4
+#endif
+constexpr int kPhaseU = DSA_VERIFY_PHASE_U;     // float4 loads in flight per thread in a phase
+#ifndef DSA_VERIFY_PHASE_TARGET_WGS
+#define DSA_VERIFY_PHASE_TARGET_WGS 2048
+#endif
+constexpr int kPhaseTargetWgs = DSA_VERIFY_PHASE_TARGET_WGS;   // workgroups of a phase when all sequences run
+constexpr int kPhaseFoldMax = 4;   // chunk partials per lane in a phase's accept test (up to 64 chunks a row)
 constexpr size_t kStreamBytes = (size_t)256 << 20;   // above this, logits are streamed non-temporally
 constexpr int kTile = 256;           // logits per wave step (64 lanes x 4)
 constexpr int kMaxV = 1 << 20;
@@ -264,9 +284,12 @@ struct VerifyWs {
   Decision* dec;     // [B]
   float* cmass;      // [B][nmass]
   float* tmass;      // [B][ntiles]: tile masses of the sampled row
+  int* reach;        // phased: [G+1][B], 1 where the chain reached position j
+  float* dlog;       // phased: [B][G][2], target and draft logit of drafted token j
   int nmass;
   int ntiles;
   int chunk_tiles;   // 256-logit tiles per mass chunk
+  bool phased;
 };
 
 // Folds chunk partials (chunk order) and runs the accept tests for sequence
@@ -341,6 +364,31 @@ __device__ void decide(const VerifyArgs& a, const VerifyWs& ws, int b, float* s_
     }
   }
   __syncthreads();
+}
+
+// Uniform of stream `st` (0 = accept test, 1 = sample) at position j.
+__device__ __forceinline__ float verify_uniform(const VerifyArgs& a, int b, int j, int st) {
+  return a.uniforms ? a.uniforms[((size_t)b * (a.G + 1) + j) * 2 + st] : philox_uniform(a.seed, a.offset, b, j, st);
+}
+
+// (max, sum) of row r of sequence b from its chunk partials, folded by a
+// 16-lane group: lane i merges chunks i, i + 16, ... in that order, then a
+// butterfly.  Every lane of the group, and every workgroup that folds the
+// same row, gets the same bits.  All 64 lanes of the wave take part.
+__device__ __forceinline__ void fold_row16(const VerifyArgs& a, int b, int r, int i16, float& M, float& S) {
+  M = -INFINITY;
+  S = 0.f;
+  const float2* p = a.part + ((size_t)b * (2 * a.G + 1) + r) * a.nchunks;
+  for (int c = i16; c < a.nchunks; c += 16) {
+    const float2 v = p[c];
+    ms_merge(M, S, v.x, v.y);
+  }
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) {
+    const float m2 = __shfl_xor(M, o, 64);
+    const float s2 = __shfl_xor(S, o, 64);
+    ms_merge(M, S, m2, s2);
+  }
 }
 
 __device__ __forceinline__ RowWeights sampled_row(const VerifyArgs& a, int b, int jstar, const float* s_m,
@@ -433,6 +481,154 @@ __device__ int wave_first_crossing(const float* v, int n, float x, float* before
   return has ? __shfl(last_pos, 63 - __clzll((long long)has), 64) : -1;
 }
 
+// Early-exit verification, phase j = 0..G (one launch each).  The protocol
+// stops at the first rejection, so a sequence's rows past it are never read.
+// Grid (chunk, sequence, row): row 0 = target row j, row 1 = draft row j
+// (the bonus phase j = G has the target row only).  Wave 0 of every
+// workgroup first runs the accept test of position j - 1 from the previous
+// phase's partials (all workgroups of a sequence get the same bits; a chain
+// that stopped earlier skips the arithmetic).  Workgroups of a chain that is
+// no longer accepted exit; the others fold their chunk into (max, sum) as
+// the stats pass does, and the one whose chunk holds drafted token j records
+// its logit for the next phase's test.  The chunk-0 target workgroup records
+// the outcome (reach flag, diagnostics, and the decision record on a
+// rejection).
+template <bool NT>
+__global__ __launch_bounds__(kStatThreads) void verify_phase_kernel(VerifyArgs a, VerifyWs ws, int j) {
+  __shared__ float2 s_w[kStatThreads / 64];
+  __shared__ int s_go;
+  const int c = blockIdx.x;
+  const int b = blockIdx.y;
+  const int which = blockIdx.z;
+  const int G = a.G, B = a.B;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int r = which == 0 ? j : G + 1 + j;
+  const float* row = row_ptr(a, b, r);
+  const int e0 = c * a.chunk;
+  const int e1 = min(e0 + a.chunk, a.V);
+  const bool lead = c == 0 && which == 0;
+  const float4 ninf = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+  // a batch of the chunk's logits (clamped inside it, masked when used)
+  auto load_batch = [&](int e, float4 (&x)[kPhaseU]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < kPhaseU; ++u) {
+      const int ee = e + u * kStatStep;
+      if (a.vec) {
+        const float4 v = ld16<NT>(row + (min(ee, e1 - 1) & ~3));
+        x[u] = ee < e1 ? v : ninf;
+      } else {
+        x[u] = ee < e1 ? load4(row, ee, e1, false) : ninf;
+      }
+    }
+  };
+  float4 x[kPhaseU];
+  const int eb = e0 + tid * 4;
+  const int dj = j < G ? min(max(a.drafts[(size_t)b * G + j], 0), a.V - 1) : 0;
+  if (tid < 64) {
+    bool go = true;
+    if (j > 0) {
+      const int jp = j - 1;
+      // every load of the test is issued together with the reach flag (all
+      // addresses are valid whatever it says)
+      const bool reached = ws.reach[(size_t)jp * B + b] != 0;
+      const float tv = ws.dlog[((size_t)b * G + jp) * 2 + 0];
+      const float dv = ws.dlog[((size_t)b * G + jp) * 2 + 1];
+      const float2* pt = a.part + ((size_t)b * (2 * G + 1) + (lane < 16 ? jp : G + 1 + jp)) * a.nchunks;
+      float2 pv[kPhaseFoldMax];
+#pragma unroll
+      for (int k = 0; k < kPhaseFoldMax; ++k) pv[k] = pt[min((lane & 15) + 16 * k, a.nchunks - 1)];
+      const float ua_in = a.uniforms ? a.uniforms[((size_t)b * (G + 1) + jp) * 2] : 0.f;
+      bool accept = false;
+      float M = -INFINITY, S = 0.f, Md = -INFINITY, Sd = 0.f, p = NAN, q = NAN, ua = NAN;
+      if (reached) {   // wave-uniform: a stopped chain skips the arithmetic
+        // lanes 0-15 fold the target row, the others the draft row (the
+        // order of fold_row16)
+#pragma unroll
+        for (int k = 0; k < kPhaseFoldMax; ++k)
+          if ((lane & 15) + 16 * k < a.nchunks) ms_merge(M, S, pv[k].x, pv[k].y);
+#pragma unroll
+        for (int o = 8; o >= 1; o >>= 1) {
+          const float m2 = __shfl_xor(M, o, 64);
+          const float s2 = __shfl_xor(S, o, 64);
+          ms_merge(M, S, m2, s2);
+        }
+        Md = __shfl(M, 16, 64);
+        Sd = __shfl(S, 16, 64);
+        ua = a.uniforms ? ua_in : philox_uniform(a.seed, a.offset, b, jp, 0);
+        p = expf(tv - M) / S;
+        q = expf(dv - Md) / Sd;
+        accept = ua * q < p;
+      }
+      go = reached && accept;
+      if (lead && lane == 0) {
+        ws.reach[(size_t)j * B + b] = go ? 1 : 0;
+        float us = NAN;
+        if (reached && !accept) {
+          Decision dd;
+          dd.jstar = jp;
+          dd.us = us = verify_uniform(a, b, jp, 1);
+          dd.ot = row_offset(M, S);
+          dd.od = row_offset(Md, Sd);
+          dd.pad0 = dd.pad1 = dd.pad2 = dd.pad3 = 0;
+          ws.dec[b] = dd;
+        }
+        if (a.diag) {
+          float* dg = a.diag + ((size_t)b * (G + 1) + jp) * 4;
+          dg[0] = reached ? p : NAN;
+          dg[1] = reached ? q : NAN;
+          dg[2] = reached ? ua : NAN;
+          dg[3] = us;
+        }
+      }
+    } else if (lead && lane == 0) {
+      ws.reach[b] = 1;
+    }
+    if (lane == 0) s_go = go ? 1 : 0;
+  }
+  __syncthreads();
+  if (!s_go) return;
+  load_batch(eb, x);
+  if (j < G && tid == 0 && dj >= e0 && dj < e1) ws.dlog[((size_t)b * G + j) * 2 + which] = row[dj];
+  float m = -INFINITY, s = 0.f;
+  for (int e = eb;;) {
+    float bm = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kPhaseU; ++u) bm = fmaxf(bm, fmaxf(fmaxf(x[u].x, x[u].y), fmaxf(x[u].z, x[u].w)));
+    const float M = fmaxf(m, bm);
+    if (M != -INFINITY) {
+      const float Mc = M * kLog2e;
+      float t = 0.f;
+#pragma unroll
+      for (int u = 0; u < kPhaseU; ++u) {
+        t += fast_exp2(fmaf(x[u].x, kLog2e, -Mc));
+        t += fast_exp2(fmaf(x[u].y, kLog2e, -Mc));
+        t += fast_exp2(fmaf(x[u].z, kLog2e, -Mc));
+        t += fast_exp2(fmaf(x[u].w, kLog2e, -Mc));
+      }
+      s = s * fast_exp2((m - M) * kLog2e) + t;
+      m = M;
+    }
+    e += kPhaseU * kStatStep;
+    if (e >= e1) break;
+    load_batch(e, x);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float m2 = __shfl_xor(m, o, 64);
+    const float s2 = __shfl_xor(s, o, 64);
+    ms_merge(m, s, m2, s2);
+  }
+  const int wave = tid >> 6;
+  if (lane == 0) s_w[wave] = make_float2(m, s);
+  __syncthreads();
+  if (tid == 0) {
+    float M = s_w[0].x, S = s_w[0].y;
+    for (int w = 1; w < kStatThreads / 64; ++w) ms_merge(M, S, s_w[w].x, s_w[w].y);
+    a.part[((size_t)b * (2 * G + 1) + r) * a.nchunks + c] = make_float2(M, S);
+  }
+}
+
 // Kernel 2: the decision of each sequence.
 __global__ __launch_bounds__(kDecideThreads) void verify_decide_kernel(VerifyArgs a, VerifyWs ws) {
   __shared__ float s_m[2 * kMaxG + 1], s_z[2 * kMaxG + 1];
@@ -462,18 +658,55 @@ __device__ __forceinline__ RowWeights decided_row(const VerifyArgs& a, const Dec
   return rw;
 }
 
+// How the mass kernel learns the decision of its sequence.
+constexpr int kMassRecord = 0;   // the decide kernel's record
+constexpr int kMassDecide = 1;   // runs the decision itself (a few sequences)
+constexpr int kMassPhased = 2;   // early-exit phases: their record, or the bonus draw of a chain that reached G
+
 // Kernel 3: the mass of one chunk (CT tiles) of the sampled row (sum of its
-// tile masses in tile order).  With DECIDE (a few sequences, where one launch
-// costs more than the repeated work) every workgroup runs the decision itself
-// from the chunk partials, chunk 0 records it for the pick kernel, and the
-// separate decide launch is skipped; the decision is the same bits either way.
-template <int CT, bool NT, bool DECIDE>
+// tile masses in tile order).  With kMassDecide (a few sequences, where one
+// launch costs more than the repeated work) every workgroup runs the
+// decision itself from the chunk partials, chunk 0 records it for the pick
+// kernel, and the separate decide launch is skipped; the decision is the
+// same bits either way.  With kMassPhased, a chain that reached position G
+// draws its bonus token from p_G, whose statistics every workgroup folds
+// from the last phase's partials (chunk 0 records the decision).
+template <int CT, bool NT, int MODE>
 __global__ __launch_bounds__(kMassThreads) void verify_mass_kernel(VerifyArgs a, VerifyWs ws) {
   __shared__ float s_tile[CT];
   const int c = blockIdx.x;
   const int b = blockIdx.y;
   RowWeights rw;
-  if constexpr (DECIDE) {
+  if constexpr (MODE == kMassPhased) {
+    __shared__ Decision s_dd;
+    if (threadIdx.x < 64) {
+      const int lane = threadIdx.x;
+      const bool bonus = ws.reach[(size_t)a.G * a.B + b] != 0;
+      Decision dd = ws.dec[b];   // written by the phase that saw the rejection (unused for a bonus)
+      float M, S;
+      fold_row16(a, b, a.G, lane & 15, M, S);
+      if (bonus) {
+        dd.jstar = a.G;
+        dd.us = verify_uniform(a, b, a.G, 1);
+        dd.ot = row_offset(M, S);
+        dd.od = 0.f;
+        dd.pad0 = dd.pad1 = dd.pad2 = dd.pad3 = 0;
+      }
+      if (lane == 0) {
+        s_dd = dd;
+        if (c == 0) {
+          if (bonus) ws.dec[b] = dd;
+          if (a.diag) {
+            float* dg = a.diag + ((size_t)b * (a.G + 1) + a.G) * 4;
+            dg[0] = dg[1] = dg[2] = NAN;
+            dg[3] = bonus ? dd.us : NAN;
+          }
+        }
+      }
+    }
+    __syncthreads();
+    rw = decided_row(a, s_dd, b);
+  } else if constexpr (MODE == kMassDecide) {
     __shared__ float s_m[2 * kMaxG + 1], s_z[2 * kMaxG + 1];
     __shared__ int s_jstar;
     __shared__ float s_us;
@@ -633,23 +866,28 @@ __global__ __launch_bounds__(kPickThreads) void verify_pick_kernel(VerifyArgs a,
   if (tid == 0) a.acc_len[b] = jstar;
 }
 
-template <int CT, bool DECIDE>
+template <int CT, int MODE>
 void launch_mass(bool nt, dim3 grid, hipStream_t s, const VerifyArgs& a, const VerifyWs& ws) {
-  if (nt) hipLaunchKernelGGL((verify_mass_kernel<CT, true, DECIDE>), grid, dim3(kMassThreads), 0, s, a, ws);
-  else hipLaunchKernelGGL((verify_mass_kernel<CT, false, DECIDE>), grid, dim3(kMassThreads), 0, s, a, ws);
+  if (nt) hipLaunchKernelGGL((verify_mass_kernel<CT, true, MODE>), grid, dim3(kMassThreads), 0, s, a, ws);
+  else hipLaunchKernelGGL((verify_mass_kernel<CT, false, MODE>), grid, dim3(kMassThreads), 0, s, a, ws);
+}
+
+template <int MODE>
+void launch_mass_ct(int ct, bool nt, dim3 grid, hipStream_t s, const VerifyArgs& a, const VerifyWs& ws) {
+  if (ct == kBigChunkTiles) launch_mass<kBigChunkTiles, MODE>(nt, grid, s, a, ws);
+  else launch_mass<kSmallChunkTiles, MODE>(nt, grid, s, a, ws);
 }
 
 // Logits per stats workgroup: whole rows when the rows alone give about
 // kStatTargetWgs workgroups, else rows split into chunks of whole load
 // rounds so that about that many run.
-int chunk_for_rows(int64_t rows, int V, int step) {
+int chunk_for_rows(int64_t rows, int V, int step, int target = kStatTargetWgs, int64_t max_chunks = 1 << 30) {
   const int64_t steps = (V + step - 1) / step;
-  int64_t want = (kStatTargetWgs + rows - 1) / rows;   // chunks per row
+  int64_t want = (target + rows - 1) / rows;   // chunks per row
   want = want < 1 ? 1 : want > steps ? steps : want;
+  want = want > max_chunks ? max_chunks : want;
   return (int)((steps + want - 1) / want) * step;
 }
-
-int stats_chunk(int B, int G, int V) { return chunk_for_rows((int64_t)B * (2 * G + 1), V, kStatStep); }
 
 // Tiles per residual-mass chunk: 8K-logit chunks (kBigChunkTiles tiles)
 // when there are enough sequences to fill the GPU with them, else 4K.
@@ -658,27 +896,54 @@ int mass_chunk_tiles(int B, int V) {
   return (int64_t)B * big >= 1024 ? kBigChunkTiles : kSmallChunkTiles;
 }
 
-size_t verify_ws(int B, int G, int V, int* nchunks, VerifyWs* out, char* base) {
-  const int chunk = stats_chunk(B, G, V);
-  const int nc = (V + chunk - 1) / chunk;
+// The schedule: early exit from kPhasedMinBytes of logits on.  The
+// environment variable DSA_VERIFY_SCHEDULE = "phased" or "onepass" overrides
+// the size rule (both give the same decisions; for tests and tuning).
+bool phased_mode(int B, int G, int V) {
+  const char* e = getenv("DSA_VERIFY_SCHEDULE");
+  if (e && strcmp(e, "phased") == 0) return true;
+  if (e && strcmp(e, "onepass") == 0) return false;
+  return (double)B * (2 * G + 1) * V * sizeof(float) >= (double)kPhasedMinBytes;
+}
+
+// Logits per stats workgroup: the one-pass stats cover all 2G+1 rows at
+// once; a phase covers two rows per sequence.
+int stats_chunk(int B, int G, int V, bool phased) {
+  return phased ? chunk_for_rows((int64_t)B * 2, V, kStatStep, kPhaseTargetWgs, 16 * kPhaseFoldMax)
+                : chunk_for_rows((int64_t)B * (2 * G + 1), V, kStatStep);
+}
+
+// Workspace layout for the schedule `phased`; its size covers both
+// schedules, so that the size query does not depend on the choice.
+size_t verify_ws(int B, int G, int V, bool phased, int* nchunks, int* chunk, VerifyWs* out, char* base) {
+  const int ch = stats_chunk(B, G, V, phased);
+  const int nc = (V + ch - 1) / ch;
+  const int ch1 = stats_chunk(B, G, V, false), ch2 = stats_chunk(B, G, V, true);
+  const int nc_max = max((V + ch1 - 1) / ch1, (V + ch2 - 1) / ch2);
   const int ct = mass_chunk_tiles(B, V);
   const int nm = (V + ct * kTile - 1) / (ct * kTile);
   if (nchunks) *nchunks = nc;
-  const size_t part = align_up((size_t)B * (2 * G + 1) * nc * sizeof(float2), 256);
+  if (chunk) *chunk = ch;
+  const size_t part = align_up((size_t)B * (2 * G + 1) * nc_max * sizeof(float2), 256);
   const size_t dec = align_up((size_t)B * sizeof(Decision), 256);
   const size_t cm = align_up((size_t)B * nm * sizeof(float), 256);
   const int nt = (V + kTile - 1) / kTile;
   const size_t tm = align_up((size_t)B * nt * sizeof(float), 256);
+  const size_t rc = align_up((size_t)(G + 1) * B * sizeof(int), 256);
+  const size_t dl = align_up((size_t)B * G * 2 * sizeof(float), 256);
   if (out) {
     out->part = reinterpret_cast<float2*>(base);
     out->dec = reinterpret_cast<Decision*>(base + part);
     out->cmass = reinterpret_cast<float*>(base + part + dec);
     out->tmass = reinterpret_cast<float*>(base + part + dec + cm);
+    out->reach = reinterpret_cast<int*>(base + part + dec + cm + tm);
+    out->dlog = reinterpret_cast<float*>(base + part + dec + cm + tm + rc);
     out->nmass = nm;
     out->ntiles = nt;
     out->chunk_tiles = ct;
+    out->phased = phased;
   }
-  return part + dec + cm + tm;
+  return part + dec + cm + tm + rc + dl;
 }
 
 // ---------------------------------------------------------------------------
@@ -803,7 +1068,7 @@ size_t greedy_ws(int B, int G, int V, int* nchunks, int* chunk) {
 
 extern "C" size_t spec_verify_workspace_size(int B, int G, int V) {
   if (B < 1 || G < 1 || V < 1) return 0;
-  return dsa::verify_ws(B, G, V, nullptr, nullptr, nullptr);
+  return dsa::verify_ws(B, G, V, false, nullptr, nullptr, nullptr, nullptr);
 }
 
 extern "C" dsa_status spec_verify(const float* target_logits, const float* draft_logits,
@@ -820,8 +1085,9 @@ extern "C" dsa_status spec_verify(const float* target_logits, const float* draft
   DSA_REQUIRE(V <= kMaxV, DSA_ERR_UNSUPPORTED, "spec_verify: V=%d > %d", V, kMaxV);
   DSA_REQUIRE((int64_t)B * (2 * G + 1) <= 65535, DSA_ERR_UNSUPPORTED, "spec_verify: B*(2G+1)=%lld rows > 65535",
               (long long)B * (2 * G + 1));
-  int nchunks = 0;
-  const size_t need = verify_ws(B, G, V, &nchunks, nullptr, nullptr);
+  int nchunks = 0, chunk = 0;
+  const bool phased = phased_mode(B, G, V);
+  const size_t need = verify_ws(B, G, V, phased, &nchunks, &chunk, nullptr, nullptr);
   DSA_REQUIRE(workspace && workspace_bytes >= need, DSA_ERR_WORKSPACE,
               "spec_verify: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
   VerifyArgs a{};
@@ -832,7 +1098,7 @@ extern "C" dsa_status spec_verify(const float* target_logits, const float* draft
   a.G = G;
   a.V = V;
   a.nchunks = nchunks;
-  a.chunk = stats_chunk(B, G, V);
+  a.chunk = chunk;
   a.uniforms = uniforms;
   a.seed = seed;
   a.offset = offset;
@@ -840,15 +1106,32 @@ extern "C" dsa_status spec_verify(const float* target_logits, const float* draft
   a.emitted = emitted;
   a.diag = diag;
   VerifyWs ws;
-  verify_ws(B, G, V, nullptr, &ws, static_cast<char*>(workspace));
+  verify_ws(B, G, V, phased, nullptr, nullptr, &ws, static_cast<char*>(workspace));
   a.part = ws.part;
   a.vec = (V % 4 == 0) && aligned16(target_logits) && aligned16(draft_logits);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool nt = (size_t)B * (2 * G + 1) * V * sizeof(float) > kStreamBytes;
   const dim3 gs(nchunks, B * (2 * G + 1)), gm(ws.nmass, B);
+  dsa_status st;
+  if (ws.phased) {
+    // early exit: one launch per position, then the bonus draws' statistics
+    for (int j = 0; j <= G; ++j) {
+      const dim3 gp(nchunks, B, j < G ? 2 : 1);
+      if (nt) hipLaunchKernelGGL(verify_phase_kernel<true>, gp, dim3(kStatThreads), 0, s, a, ws, j);
+      else hipLaunchKernelGGL(verify_phase_kernel<false>, gp, dim3(kStatThreads), 0, s, a, ws, j);
+      st = launch_status("spec_verify(phase)");
+      if (st != DSA_OK) return st;
+    }
+    launch_mass_ct<kMassPhased>(ws.chunk_tiles, nt, gm, s, a, ws);
+    st = launch_status("spec_verify(mass)");
+    if (st != DSA_OK) return st;
+    if (nt) hipLaunchKernelGGL(verify_pick_kernel<true>, dim3(B), dim3(kPickThreads), 0, s, a, ws);
+    else hipLaunchKernelGGL(verify_pick_kernel<false>, dim3(B), dim3(kPickThreads), 0, s, a, ws);
+    return launch_status("spec_verify(pick)");
+  }
   if (nt) hipLaunchKernelGGL(verify_stats_kernel<true>, gs, dim3(kStatThreads), 0, s, a);
   else hipLaunchKernelGGL(verify_stats_kernel<false>, gs, dim3(kStatThreads), 0, s, a);
-  dsa_status st = launch_status("spec_verify(stats)");
+  st = launch_status("spec_verify(stats)");
   if (st != DSA_OK) return st;
 #ifndef DSA_VERIFY_FUSE_MAX_B
 #define DSA_VERIFY_FUSE_MAX_B 16
@@ -861,13 +1144,8 @@ extern "C" dsa_status spec_verify(const float* target_logits, const float* draft
     st = launch_status("spec_verify(decide)");
     if (st != DSA_OK) return st;
   }
-  if (ws.chunk_tiles == kBigChunkTiles) {
-    if (fuse) launch_mass<kBigChunkTiles, true>(nt, gm, s, a, ws);
-    else launch_mass<kBigChunkTiles, false>(nt, gm, s, a, ws);
-  } else {
-    if (fuse) launch_mass<kSmallChunkTiles, true>(nt, gm, s, a, ws);
-    else launch_mass<kSmallChunkTiles, false>(nt, gm, s, a, ws);
-  }
+  if (fuse) launch_mass_ct<kMassDecide>(ws.chunk_tiles, nt, gm, s, a, ws);
+  else launch_mass_ct<kMassRecord>(ws.chunk_tiles, nt, gm, s, a, ws);
   st = launch_status("spec_verify(mass)");
   if (st != DSA_OK) return st;
   if (nt) hipLaunchKernelGGL(verify_pick_kernel<true>, dim3(B), dim3(kPickThreads), 0, s, a, ws);

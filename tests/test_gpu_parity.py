@@ -624,6 +624,68 @@ def test_spec_verify_draw_at_the_top_of_the_cdf(V):
     assert ref_em[0, 0] == V - 1 and np.all(em[np.arange(B), n] >= 0)
 
 
+@pytest.mark.parametrize("B,G,V,std", [
+    (64, 7, 5003, 2.0),        # V not a multiple of 4 (no 16-byte loads)
+    (40, 7, 151552, 0.5),
+    (24, 15, 20000, 6.0),      # block-16 chain
+    (100, 1, 4096, 2.0),       # one draft: a phase for it and one for the bonus row
+    (3, 32, 4099, 2.0),        # the longest chain
+    (4, 7, 1 << 20, 2.0),      # the largest vocabulary: 64 chunks per row
+])
+def test_spec_verify_early_exit(B, G, V, std, monkeypatch):
+    """The early-exit schedule (one launch per position; rows past a
+    sequence's first rejection are never read), forced at sizes below its
+    threshold: decisions, tokens and the diagnostics of the evaluated
+    positions equal the oracle's, as for the one-pass schedule."""
+    monkeypatch.setenv("DSA_VERIFY_SCHEDULE", "phased")
+    log("spec_verify early exit", B, G, V, std)
+    vi = I.verify_inputs(B * 1000 + G, B, G, V, std)
+    n, _, near = _verify_case(vi, bool(B % 2))
+    assert near <= B // 64 + 1
+    assert 0 < n.mean() < G   # rejections and accepted positions both occur
+
+
+def test_spec_verify_early_exit_special_cases(monkeypatch):
+    """Early-exit schedule at the extremes: p == q accepts every draft (every
+    sequence runs all phases and draws its bonus token from p_G), and draft
+    mass only where the target has none rejects every chain at position 0
+    (no later phase reads a row)."""
+    monkeypatch.setenv("DSA_VERIFY_SCHEDULE", "phased")
+    rng = np.random.default_rng(11)
+    B, G, V = 16, 3, 30000
+    tl = (rng.standard_normal((B, G + 1, V)) * 2).astype(np.float32)
+    vi = I.VerifyInputs(tl, tl[:, :G].copy(), rng.integers(0, V, (B, G)).astype(np.int32), 12, 0)
+    n, em, _ = _verify_case(vi, True)
+    assert np.all(n == G)
+    tl[:, :, V // 2:] = -np.inf
+    dl = np.full((B, G, V), -np.inf, np.float32)
+    dl[:, :, V // 2:] = 0.0
+    dr = rng.integers(V // 2, V, (B, G)).astype(np.int32)
+    n, em, _ = _verify_case(I.VerifyInputs(tl, dl, dr, 13, 0), False)
+    assert np.all(n == 0) and np.all(em[:, 0] < V // 2)
+
+
+def test_spec_verify_schedules_agree(monkeypatch):
+    """Both schedules on the same batch: the same accepted lengths and
+    emitted tokens, except where a draw or test lies within the float32
+    rounding of its threshold (the schedules fold the softmax statistics in
+    different chunks)."""
+    vi = I.verify_inputs(77, 48, 7, 50000, 2.0)
+    out = {}
+    for sched in ("onepass", "phased"):
+        monkeypatch.setenv("DSA_VERIFY_SCHEDULE", sched)
+        n, em = dsa.spec_verify(to_dev(vi.target_logits), to_dev(vi.draft_logits), to_dev(vi.drafts),
+                                seed=vi.seed, offset=vi.offset)
+        out[sched] = (n.cpu().numpy(), em.cpu().numpy())
+    ua, us = I.verify_uniforms(vi.seed, vi.offset, 48, 7)
+    _, _, res = O.spec_verify(vi.target_logits, vi.draft_logits, vi.drafts, ua, us)
+    for b in range(48):
+        same = out["onepass"][0][b] == out["phased"][0][b] and np.array_equal(out["onepass"][1][b], out["phased"][1][b])
+        if not same:
+            r = res[b]
+            assert min(np.nanmin(r["accept_margin"]), r["sample_margin"]) < 1e-5, b
+
+
 @pytest.mark.parametrize("seed", range(8))
 def test_spec_verify_random_shapes(seed):
     """Seeded random verification shapes: 1-40 sequences, 1-32 drafts,

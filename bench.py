@@ -586,8 +586,25 @@ def _extra_verify(dsa, reps, peaks, cpu):
             dsa.spec_verify(v.target_logits, v.draft_logits, v.drafts, seed=v.seed, offset=v.offset,
                             accepted_len=n, emitted=em, workspace=ws)
 
+        # default schedule (early exit at this size): bytes it reads, from the
+        # accepted lengths: both rows of every position up to the first
+        # rejection (the target row of the bonus position after a full
+        # accept), then the sampled rows once more for the draw
         us_w, us_c = time_warm(call, reps, inner=2), time_flushed(call, max(5, reps // 2))
-        e = hbm_entry(vbytes, us_w, us_c, peaks)
+        nn = n.cpu().long()
+        rows = torch.where(nn < G, 2 * (nn + 1) + 2, 2 * G + 1 + 1)
+        e = hbm_entry(int(rows.sum()) * V * 4, us_w, us_c, peaks)
+        e["schedule"] = "early exit (rows past each chain's first rejection are not read)"
+        e["all_rows_bytes"] = vbytes
+        e["all_rows_GBps_flushed"] = vbytes / us_c / 1e3   # rate at which the batch's logits are consumed
+        # the one-pass schedule on the same batch: every row read once (the
+        # stats pass), the bandwidth figure of a full read
+        os.environ["DSA_VERIFY_SCHEDULE"] = "onepass"
+        try:
+            e1 = hbm_entry(vbytes, time_warm(call, reps, inner=2), time_flushed(call, max(5, reps // 2)), peaks)
+        finally:
+            del os.environ["DSA_VERIFY_SCHEDULE"]
+        e["onepass"] = e1
         e.update({"verified_positions_per_s_flushed": B * (G + 1) / (us_c * 1e-6),
                   "verified_positions_per_s_warm": B * (G + 1) / (us_w * 1e-6),
                   "mean_accepted_len": float(n.float().mean()),

@@ -981,18 +981,15 @@ struct GreedyArgs {
   int32_t* acc_len;
   int32_t* emitted;
   ArgMax* part;   // [B][G+1][nchunks]
+  int* reach;     // early exit: [G+1][B], 1 where the chain reached position j
   bool vec;
 };
 
-// Kernel 1: (max, argmax) of each chunk of each target row.
+// (max, argmax) of logits [e0, e1) of a row, reduced over the workgroup;
+// the result is valid in thread 0.
 template <bool NT>
-__global__ __launch_bounds__(kArgThreads) void greedy_argmax_kernel(GreedyArgs a) {
+__device__ ArgMax chunk_argmax(const GreedyArgs& a, const float* row, int e0, int e1) {
   __shared__ ArgMax s_w[kArgThreads / 64];
-  const int c = blockIdx.x;
-  const int rr = blockIdx.y;   // b * (G+1) + j
-  const float* row = a.tl + (size_t)rr * a.V;
-  const int e0 = c * a.chunk;
-  const int e1 = min(e0 + a.chunk, a.V);
   ArgMax best{-INFINITY, INT_MAX};
   for (int e = e0 + threadIdx.x * 4; e < e1; e += kArgU * kArgStep) {
     float4 x[kArgU];
@@ -1015,11 +1012,85 @@ __global__ __launch_bounds__(kArgThreads) void greedy_argmax_kernel(GreedyArgs a
   const int wave = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) s_w[wave] = best;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    ArgMax r = s_w[0];
-    for (int w = 1; w < kArgThreads / 64; ++w) r = am_pick(r, s_w[w]);
-    a.part[(size_t)rr * a.nchunks + c] = r;
+  ArgMax r = s_w[0];
+  for (int w = 1; w < kArgThreads / 64; ++w) r = am_pick(r, s_w[w]);
+  return r;
+}
+
+// Kernel 1: (max, argmax) of each chunk of each target row.
+template <bool NT>
+__global__ __launch_bounds__(kArgThreads) void greedy_argmax_kernel(GreedyArgs a) {
+  const int c = blockIdx.x;
+  const int rr = blockIdx.y;   // b * (G+1) + j
+  const float* row = a.tl + (size_t)rr * a.V;
+  const int e0 = c * a.chunk;
+  const int e1 = min(e0 + a.chunk, a.V);
+  const ArgMax r = chunk_argmax<NT>(a, row, e0, e1);
+  if (threadIdx.x == 0) a.part[(size_t)rr * a.nchunks + c] = r;
+}
+
+// Winner of the chunk partials of target row j of sequence b (wave 0, all
+// lanes; the pick is associative and commutative, so the order is free).  A
+// row of -inf only (or NaN, outside the domain) has no winner: token 0.
+__device__ __forceinline__ int row_argmax(const GreedyArgs& a, int b, int j) {
+  const int lane = threadIdx.x & 63;
+  const ArgMax* p = a.part + ((size_t)b * (a.G + 1) + j) * a.nchunks;
+  ArgMax best{-INFINITY, INT_MAX};
+  for (int c = lane; c < a.nchunks; c += 64) best = am_pick(best, p[c]);
+  best = am_wave(best);
+  return best.i == INT_MAX ? 0 : best.i;
+}
+
+// Emitted tokens and accepted length of a chain stopped at position jstar
+// with token `tok` (lanes 0..G of one wave).
+__device__ __forceinline__ void greedy_emit(const GreedyArgs& a, int b, int jstar, int tok) {
+  const int lane = threadIdx.x & 63;
+  if (lane <= a.G) {
+    int32_t v = -1;
+    if (lane < jstar) v = a.drafts[(size_t)b * a.G + lane];
+    else if (lane == jstar) v = tok;
+    a.emitted[(size_t)b * (a.G + 1) + lane] = v;
   }
+  if (lane == 0) a.acc_len[b] = jstar;
+}
+
+// Early-exit greedy verification (large batches), position j = 0..G+1, one
+// launch each: grid (chunk, sequence).  Wave 0 of every workgroup first
+// compares draft j - 1 with the argmax of target row j - 1 (from the
+// previous launch's partials); the chunk-0 workgroup of a chain that stops
+// there emits its tokens.  Workgroups of chains that stopped exit; the
+// others reduce their chunk of target row j (j <= G).  Launch G + 1 only
+// emits the bonus token of the chains that accepted every draft.
+template <bool NT>
+__global__ __launch_bounds__(kArgThreads) void greedy_phase_kernel(GreedyArgs a, int j) {
+  __shared__ int s_go;
+  const int c = blockIdx.x;
+  const int b = blockIdx.y;
+  const int G = a.G, B = a.B;
+  if (threadIdx.x < 64) {
+    bool go = true;
+    if (j > 0) {
+      const int jp = j - 1;
+      const bool reached = a.reach[(size_t)jp * B + b] != 0;
+      if (reached) {   // wave-uniform
+        const int arg = row_argmax(a, b, jp);
+        const bool accept = jp < G && a.drafts[(size_t)b * G + jp] == arg;
+        go = accept;
+        if (c == 0 && !accept) greedy_emit(a, b, jp, arg);
+      } else {
+        go = false;
+      }
+    }
+    if (c == 0 && (threadIdx.x & 63) == 0 && j <= G) a.reach[(size_t)j * B + b] = go ? 1 : 0;
+    if ((threadIdx.x & 63) == 0) s_go = go ? 1 : 0;
+  }
+  __syncthreads();
+  if (!s_go || j > G) return;
+  const float* row = a.tl + ((size_t)b * (G + 1) + j) * a.V;
+  const int e0 = c * a.chunk;
+  const int e1 = min(e0 + a.chunk, a.V);
+  const ArgMax r = chunk_argmax<NT>(a, row, e0, e1);
+  if (threadIdx.x == 0) a.part[((size_t)b * (G + 1) + j) * a.nchunks + c] = r;
 }
 
 // Kernel 2: one workgroup per sequence folds the chunk winners of its G+1
@@ -1055,12 +1126,30 @@ __global__ __launch_bounds__(kGreedyThreads) void greedy_decide_kernel(GreedyArg
   }
 }
 
-size_t greedy_ws(int B, int G, int V, int* nchunks, int* chunk) {
-  const int ch = chunk_for_rows((int64_t)B * (G + 1), V, kArgStep);
-  const int nc = (V + ch - 1) / ch;
-  if (nchunks) *nchunks = nc;
+// Greedy verification schedule: early exit (one launch per position) from
+// kPhasedMinBytes of target logits on, unless DSA_VERIFY_SCHEDULE says
+// otherwise (as for spec_verify).
+bool greedy_phased(int B, int G, int V) {
+  const char* e = getenv("DSA_VERIFY_SCHEDULE");
+  if (e && strcmp(e, "phased") == 0) return true;
+  if (e && strcmp(e, "onepass") == 0) return false;
+  return (double)B * (G + 1) * V * sizeof(float) >= (double)kPhasedMinBytes;
+}
+
+// Chunks: the one-pass schedule spreads all G+1 rows of every sequence over
+// about kStatTargetWgs workgroups, a phase one row per sequence over about
+// kPhaseTargetWgs.  The workspace covers both (its size does not depend on
+// the schedule): argmax partials [B][G+1][chunks], then the reach flags.
+size_t greedy_ws(int B, int G, int V, bool phased, int* nchunks, int* chunk, int** reach, char* base) {
+  const int ch1 = chunk_for_rows((int64_t)B * (G + 1), V, kArgStep);
+  const int ch2 = chunk_for_rows((int64_t)B, V, kArgStep, kPhaseTargetWgs);
+  const int ch = phased ? ch2 : ch1;
+  const int nc_max = max((V + ch1 - 1) / ch1, (V + ch2 - 1) / ch2);
+  if (nchunks) *nchunks = (V + ch - 1) / ch;
   if (chunk) *chunk = ch;
-  return align_up((size_t)B * (G + 1) * nc * sizeof(ArgMax), 256);
+  const size_t part = align_up((size_t)B * (G + 1) * nc_max * sizeof(ArgMax), 256);
+  if (reach) *reach = reinterpret_cast<int*>(base + part);
+  return part + align_up((size_t)(G + 1) * B * sizeof(int), 256);
 }
 
 }  // namespace
@@ -1155,7 +1244,7 @@ extern "C" dsa_status spec_verify(const float* target_logits, const float* draft
 
 extern "C" size_t spec_verify_greedy_workspace_size(int B, int G, int V) {
   if (B < 1 || G < 1 || V < 1) return 0;
-  return dsa::greedy_ws(B, G, V, nullptr, nullptr);
+  return dsa::greedy_ws(B, G, V, false, nullptr, nullptr, nullptr, nullptr);
 }
 
 extern "C" dsa_status spec_verify_greedy(const float* target_logits, const int32_t* draft_tokens, int B, int G,
@@ -1172,9 +1261,12 @@ extern "C" dsa_status spec_verify_greedy(const float* target_logits, const int32
   DSA_REQUIRE((int64_t)B * (G + 1) <= 65535, DSA_ERR_UNSUPPORTED, "spec_verify_greedy: B*(G+1)=%lld rows > 65535",
               (long long)B * (G + 1));
   int nchunks = 0, chunk = 0;
-  const size_t need = greedy_ws(B, G, V, &nchunks, &chunk);
+  int* reach = nullptr;
+  const bool phased = greedy_phased(B, G, V);
+  const size_t need = greedy_ws(B, G, V, phased, &nchunks, &chunk, nullptr, nullptr);
   DSA_REQUIRE(workspace && workspace_bytes >= need, DSA_ERR_WORKSPACE,
               "spec_verify_greedy: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  greedy_ws(B, G, V, phased, nullptr, nullptr, &reach, static_cast<char*>(workspace));
   GreedyArgs a{};
   a.tl = target_logits;
   a.drafts = draft_tokens;
@@ -1186,10 +1278,23 @@ extern "C" dsa_status spec_verify_greedy(const float* target_logits, const int32
   a.acc_len = accepted_len;
   a.emitted = emitted;
   a.part = static_cast<ArgMax*>(workspace);
+  a.reach = reach;
   a.vec = (V % 4 == 0) && aligned16(target_logits);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool nt = (size_t)B * (G + 1) * V * sizeof(float) > kStreamBytes;
+  if (phased) {
+    // early exit: positions 0..G, then the bonus tokens
+    for (int j = 0; j <= G + 1; ++j) {
+      const dim3 gp(j <= G ? nchunks : 1, B);
+      if (nt) hipLaunchKernelGGL(greedy_phase_kernel<true>, gp, dim3(kArgThreads), 0, s, a, j);
+      else hipLaunchKernelGGL(greedy_phase_kernel<false>, gp, dim3(kArgThreads), 0, s, a, j);
+      const dsa_status st = launch_status("spec_verify_greedy(phase)");
+      if (st != DSA_OK) return st;
+    }
+    return DSA_OK;
+  }
   const dim3 g1(nchunks, B * (G + 1));
-  if ((size_t)B * (G + 1) * V * sizeof(float) > kStreamBytes)
+  if (nt)
     hipLaunchKernelGGL(greedy_argmax_kernel<true>, g1, dim3(kArgThreads), 0, s, a);
   else
     hipLaunchKernelGGL(greedy_argmax_kernel<false>, g1, dim3(kArgThreads), 0, s, a);

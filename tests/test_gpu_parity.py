@@ -731,9 +731,13 @@ def _greedy_inputs(rng, B, G, V, integer):
     return tl, dr
 
 
+@pytest.mark.parametrize("schedule", ["onepass", "phased"])
 @pytest.mark.parametrize("G,V,integer", [(7, 1024, True), (7, 1024, False), (15, 1000, True), (15, 5003, False),
-                                          (7, 151552, True), (1, 4, False)])
-def test_greedy_verify(G, V, integer):
+                                          (7, 151552, True), (1, 4, False), (32, 3001, True)])
+def test_greedy_verify(G, V, integer, schedule, monkeypatch):
+    """Both schedules (one pass over every row; early exit, which reads a
+    row only while the chain is still accepted), bit-exact with the oracle."""
+    monkeypatch.setenv("DSA_VERIFY_SCHEDULE", schedule)
     rng = np.random.default_rng(G * 7 + V + integer)
     B = 6 if V > 100000 else 40
     tl, dr = _greedy_inputs(rng, B, G, V, integer)
@@ -743,7 +747,9 @@ def test_greedy_verify(G, V, integer):
     np.testing.assert_array_equal(em.cpu().numpy(), ref_em)
 
 
-def test_greedy_verify_special_rows():
+@pytest.mark.parametrize("schedule", ["onepass", "phased"])
+def test_greedy_verify_special_rows(schedule, monkeypatch):
+    monkeypatch.setenv("DSA_VERIFY_SCHEDULE", schedule)
     G, V = 3, 4099
     tl = np.zeros((3, G + 1, V), np.float32)
     tl[0] = -np.inf

@@ -66,6 +66,14 @@ constexpr int kPhaseU = DSA_VERIFY_PHASE_U;     // float4 loads in flight per th
 #define DSA_VERIFY_PHASE_TARGET_WGS 2048
 #endif
 constexpr int kPhaseTargetWgs = DSA_VERIFY_PHASE_TARGET_WGS;   // workgroups of a phase when all sequences run
+#ifndef DSA_VERIFY_PHASED_POSITIONS
+#define DSA_VERIFY_PHASED_POSITIONS 4
+#endif
+constexpr int kPhasedPositions = DSA_VERIFY_PHASED_POSITIONS;   // positions with a launch of their own
+#ifndef DSA_VERIFY_GREEDY_PHASED_POSITIONS
+#define DSA_VERIFY_GREEDY_PHASED_POSITIONS 2
+#endif
+constexpr int kGreedyPhasedPositions = DSA_VERIFY_GREEDY_PHASED_POSITIONS;   // the same for greedy verification
 constexpr int kPhaseFoldMax = 4;   // chunk partials per lane in a phase's accept test (up to 64 chunks a row)
 constexpr size_t kStreamBytes = (size_t)256 << 20;   // above this, logits are streamed non-temporally
 constexpr int kTile = 256;           // logits per wave step (64 lanes x 4)
@@ -290,6 +298,7 @@ struct VerifyWs {
   int ntiles;
   int chunk_tiles;   // 256-logit tiles per mass chunk
   bool phased;
+  int tail;          // phased: first position of the last launch (one pass over its rows)
 };
 
 // Folds chunk partials (chunk order) and runs the accept tests for sequence
@@ -369,26 +378,6 @@ __device__ void decide(const VerifyArgs& a, const VerifyWs& ws, int b, float* s_
 // Uniform of stream `st` (0 = accept test, 1 = sample) at position j.
 __device__ __forceinline__ float verify_uniform(const VerifyArgs& a, int b, int j, int st) {
   return a.uniforms ? a.uniforms[((size_t)b * (a.G + 1) + j) * 2 + st] : philox_uniform(a.seed, a.offset, b, j, st);
-}
-
-// (max, sum) of row r of sequence b from its chunk partials, folded by a
-// 16-lane group: lane i merges chunks i, i + 16, ... in that order, then a
-// butterfly.  Every lane of the group, and every workgroup that folds the
-// same row, gets the same bits.  All 64 lanes of the wave take part.
-__device__ __forceinline__ void fold_row16(const VerifyArgs& a, int b, int r, int i16, float& M, float& S) {
-  M = -INFINITY;
-  S = 0.f;
-  const float2* p = a.part + ((size_t)b * (2 * a.G + 1) + r) * a.nchunks;
-  for (int c = i16; c < a.nchunks; c += 16) {
-    const float2 v = p[c];
-    ms_merge(M, S, v.x, v.y);
-  }
-#pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) {
-    const float m2 = __shfl_xor(M, o, 64);
-    const float s2 = __shfl_xor(S, o, 64);
-    ms_merge(M, S, m2, s2);
-  }
 }
 
 __device__ __forceinline__ RowWeights sampled_row(const VerifyArgs& a, int b, int jstar, const float* s_m,
@@ -481,20 +470,23 @@ __device__ int wave_first_crossing(const float* v, int n, float x, float* before
   return has ? __shfl(last_pos, 63 - __clzll((long long)has), 64) : -1;
 }
 
-// Early-exit verification, phase j = 0..G (one launch each).  The protocol
-// stops at the first rejection, so a sequence's rows past it are never read.
-// Grid (chunk, sequence, row): row 0 = target row j, row 1 = draft row j
-// (the bonus phase j = G has the target row only).  Wave 0 of every
-// workgroup first runs the accept test of position j - 1 from the previous
-// phase's partials (all workgroups of a sequence get the same bits; a chain
-// that stopped earlier skips the arithmetic).  Workgroups of a chain that is
-// no longer accepted exit; the others fold their chunk into (max, sum) as
-// the stats pass does, and the one whose chunk holds drafted token j records
-// its logit for the next phase's test.  The chunk-0 target workgroup records
-// the outcome (reach flag, diagnostics, and the decision record on a
-// rejection).
+// Early-exit verification, one launch per position j = 0..P-1, then one
+// launch for the rest (positions P..G; P = kPhasedPositions, or G when the
+// chain is shorter).  The protocol stops at the first rejection, so a
+// sequence's rows past it are not read, while the few chains still accepted
+// after P positions read their remaining rows in one pass.  Grid (chunk,
+// sequence, row) over the rows of positions j..jl: target rows j..jl, then
+// draft rows j..min(jl, G-1).  Wave 0 of every workgroup first runs the
+// accept test of position j - 1 from the previous launch's partials (all
+// workgroups of a sequence get the same bits; a chain that stopped earlier
+// skips the arithmetic).  Workgroups of a chain that is no longer accepted
+// exit; the others fold their chunk into (max, sum) as the stats pass does,
+// and (for a single position) the one whose chunk holds drafted token j
+// records its logit for the next launch's test.  The chunk-0 workgroup of
+// the first row records the outcome (reach flag, diagnostics, and the
+// decision record on a rejection).  The mass kernel decides positions P..G.
 template <bool NT>
-__global__ __launch_bounds__(kStatThreads) void verify_phase_kernel(VerifyArgs a, VerifyWs ws, int j) {
+__global__ __launch_bounds__(kStatThreads) void verify_phase_kernel(VerifyArgs a, VerifyWs ws, int j, int jl) {
   __shared__ float2 s_w[kStatThreads / 64];
   __shared__ int s_go;
   const int c = blockIdx.x;
@@ -503,11 +495,13 @@ __global__ __launch_bounds__(kStatThreads) void verify_phase_kernel(VerifyArgs a
   const int G = a.G, B = a.B;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int r = which == 0 ? j : G + 1 + j;
+  const int ntr = jl - j + 1;   // target rows of the launch
+  const int r = which < ntr ? j + which : G + 1 + j + (which - ntr);
   const float* row = row_ptr(a, b, r);
   const int e0 = c * a.chunk;
   const int e1 = min(e0 + a.chunk, a.V);
   const bool lead = c == 0 && which == 0;
+  const bool single = jl == j;   // one position: record the drafted token's logit
   const float4 ninf = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
   // a batch of the chunk's logits (clamped inside it, masked when used)
   auto load_batch = [&](int e, float4 (&x)[kPhaseU]) __attribute__((always_inline)) {
@@ -524,7 +518,7 @@ __global__ __launch_bounds__(kStatThreads) void verify_phase_kernel(VerifyArgs a
   };
   float4 x[kPhaseU];
   const int eb = e0 + tid * 4;
-  const int dj = j < G ? min(max(a.drafts[(size_t)b * G + j], 0), a.V - 1) : 0;
+  const int dj = single && j < G ? min(max(a.drafts[(size_t)b * G + j], 0), a.V - 1) : 0;
   if (tid < 64) {
     bool go = true;
     if (j > 0) {
@@ -542,8 +536,8 @@ __global__ __launch_bounds__(kStatThreads) void verify_phase_kernel(VerifyArgs a
       bool accept = false;
       float M = -INFINITY, S = 0.f, Md = -INFINITY, Sd = 0.f, p = NAN, q = NAN, ua = NAN;
       if (reached) {   // wave-uniform: a stopped chain skips the arithmetic
-        // lanes 0-15 fold the target row, the others the draft row (the
-        // order of fold_row16)
+        // lanes 0-15 fold the target row, the others the draft row, in the
+        // order of decide() (the same bits)
 #pragma unroll
         for (int k = 0; k < kPhaseFoldMax; ++k)
           if ((lane & 15) + 16 * k < a.nchunks) ms_merge(M, S, pv[k].x, pv[k].y);
@@ -589,7 +583,7 @@ __global__ __launch_bounds__(kStatThreads) void verify_phase_kernel(VerifyArgs a
   __syncthreads();
   if (!s_go) return;
   load_batch(eb, x);
-  if (j < G && tid == 0 && dj >= e0 && dj < e1) ws.dlog[((size_t)b * G + j) * 2 + which] = row[dj];
+  if (single && j < G && tid == 0 && dj >= e0 && dj < e1) ws.dlog[((size_t)b * G + j) * 2 + which] = row[dj];
   float m = -INFINITY, s = 0.f;
   for (int e = eb;;) {
     float bm = -INFINITY;
@@ -661,16 +655,16 @@ __device__ __forceinline__ RowWeights decided_row(const VerifyArgs& a, const Dec
 // How the mass kernel learns the decision of its sequence.
 constexpr int kMassRecord = 0;   // the decide kernel's record
 constexpr int kMassDecide = 1;   // runs the decision itself (a few sequences)
-constexpr int kMassPhased = 2;   // early-exit phases: their record, or the bonus draw of a chain that reached G
+constexpr int kMassPhased = 2;   // early exit: the launch's record, or the decision of a chain that reached the last launch
 
 // Kernel 3: the mass of one chunk (CT tiles) of the sampled row (sum of its
 // tile masses in tile order).  With kMassDecide (a few sequences, where one
 // launch costs more than the repeated work) every workgroup runs the
 // decision itself from the chunk partials, chunk 0 records it for the pick
 // kernel, and the separate decide launch is skipped; the decision is the
-// same bits either way.  With kMassPhased, a chain that reached position G
-// draws its bonus token from p_G, whose statistics every workgroup folds
-// from the last phase's partials (chunk 0 records the decision).
+// same bits either way.  With kMassPhased, a chain that stopped before the
+// last early-exit launch has its record; one that reached it is decided
+// here over every position, as with kMassDecide.
 template <int CT, bool NT, int MODE>
 __global__ __launch_bounds__(kMassThreads) void verify_mass_kernel(VerifyArgs a, VerifyWs ws) {
   __shared__ float s_tile[CT];
@@ -678,34 +672,34 @@ __global__ __launch_bounds__(kMassThreads) void verify_mass_kernel(VerifyArgs a,
   const int b = blockIdx.y;
   RowWeights rw;
   if constexpr (MODE == kMassPhased) {
-    __shared__ Decision s_dd;
-    if (threadIdx.x < 64) {
-      const int lane = threadIdx.x;
-      const bool bonus = ws.reach[(size_t)a.G * a.B + b] != 0;
-      Decision dd = ws.dec[b];   // written by the phase that saw the rejection (unused for a bonus)
-      float M, S;
-      fold_row16(a, b, a.G, lane & 15, M, S);
-      if (bonus) {
-        dd.jstar = a.G;
-        dd.us = verify_uniform(a, b, a.G, 1);
-        dd.ot = row_offset(M, S);
-        dd.od = 0.f;
-        dd.pad0 = dd.pad1 = dd.pad2 = dd.pad3 = 0;
-      }
-      if (lane == 0) {
-        s_dd = dd;
-        if (c == 0) {
-          if (bonus) ws.dec[b] = dd;
-          if (a.diag) {
-            float* dg = a.diag + ((size_t)b * (a.G + 1) + a.G) * 4;
-            dg[0] = dg[1] = dg[2] = NAN;
-            dg[3] = bonus ? dd.us : NAN;
-          }
-        }
-      }
-    }
+    __shared__ float s_m[2 * kMaxG + 1], s_z[2 * kMaxG + 1];
+    __shared__ int s_jstar, s_reached;
+    __shared__ float s_us;
+    if (threadIdx.x == 0) s_reached = ws.reach[(size_t)ws.tail * a.B + b];
     __syncthreads();
-    rw = decided_row(a, s_dd, b);
+    if (s_reached) {
+      // the chain reached the last launch's first position: its decision
+      // over every position (the same bits as the per-position tests for
+      // the positions those already passed)
+      decide(a, ws, b, s_m, s_z, &s_jstar, &s_us, c == 0);
+      rw = sampled_row(a, b, s_jstar, s_m, s_z);
+      if (c == 0 && threadIdx.x == 0) {
+        Decision dd;
+        dd.jstar = s_jstar;
+        dd.us = s_us;
+        dd.ot = rw.ot;
+        dd.od = rw.od;
+        dd.pad0 = dd.pad1 = dd.pad2 = dd.pad3 = 0;
+        ws.dec[b] = dd;
+      }
+    } else {
+      rw = decided_row(a, ws.dec[b], b);
+      // positions the chain never reached (the per-position launches covered
+      // those before the last launch)
+      if (c == 0 && a.diag)
+        for (int i = threadIdx.x; i < (a.G + 1 - ws.tail) * 4; i += blockDim.x)
+          a.diag[((size_t)b * (a.G + 1) + ws.tail) * 4 + i] = NAN;
+    }
   } else if constexpr (MODE == kMassDecide) {
     __shared__ float s_m[2 * kMaxG + 1], s_z[2 * kMaxG + 1];
     __shared__ int s_jstar;
@@ -1054,13 +1048,15 @@ __device__ __forceinline__ void greedy_emit(const GreedyArgs& a, int b, int jsta
   if (lane == 0) a.acc_len[b] = jstar;
 }
 
-// Early-exit greedy verification (large batches), position j = 0..G+1, one
-// launch each: grid (chunk, sequence).  Wave 0 of every workgroup first
-// compares draft j - 1 with the argmax of target row j - 1 (from the
-// previous launch's partials); the chunk-0 workgroup of a chain that stops
-// there emits its tokens.  Workgroups of chains that stopped exit; the
-// others reduce their chunk of target row j (j <= G).  Launch G + 1 only
-// emits the bonus token of the chains that accepted every draft.
+// Early-exit greedy verification (large batches): one launch per position
+// j = 0..P-1, then one launch over target rows P..G (P =
+// kGreedyPhasedPositions, or G for a shorter chain); grid (chunk, sequence,
+// row).  Wave 0 of every workgroup first compares draft j - 1 with the
+// argmax of target row j - 1 (from the previous launch's partials); the
+// chunk-0 workgroup of a chain that stops there emits its tokens.
+// Workgroups of chains that stopped exit; the others reduce their chunk of
+// target row j + blockIdx.z.  greedy_decide_kernel then decides the chains
+// that reached P.
 template <bool NT>
 __global__ __launch_bounds__(kArgThreads) void greedy_phase_kernel(GreedyArgs a, int j) {
   __shared__ int s_go;
@@ -1074,33 +1070,37 @@ __global__ __launch_bounds__(kArgThreads) void greedy_phase_kernel(GreedyArgs a,
       const bool reached = a.reach[(size_t)jp * B + b] != 0;
       if (reached) {   // wave-uniform
         const int arg = row_argmax(a, b, jp);
-        const bool accept = jp < G && a.drafts[(size_t)b * G + jp] == arg;
+        const bool accept = a.drafts[(size_t)b * G + jp] == arg;
         go = accept;
-        if (c == 0 && !accept) greedy_emit(a, b, jp, arg);
+        if (c == 0 && blockIdx.z == 0 && !accept) greedy_emit(a, b, jp, arg);
       } else {
         go = false;
       }
     }
-    if (c == 0 && (threadIdx.x & 63) == 0 && j <= G) a.reach[(size_t)j * B + b] = go ? 1 : 0;
+    if (c == 0 && blockIdx.z == 0 && (threadIdx.x & 63) == 0) a.reach[(size_t)j * B + b] = go ? 1 : 0;
     if ((threadIdx.x & 63) == 0) s_go = go ? 1 : 0;
   }
   __syncthreads();
-  if (!s_go || j > G) return;
-  const float* row = a.tl + ((size_t)b * (G + 1) + j) * a.V;
+  if (!s_go) return;
+  const int jr = j + blockIdx.z;
+  const float* row = a.tl + ((size_t)b * (G + 1) + jr) * a.V;
   const int e0 = c * a.chunk;
   const int e1 = min(e0 + a.chunk, a.V);
   const ArgMax r = chunk_argmax<NT>(a, row, e0, e1);
-  if (threadIdx.x == 0) a.part[((size_t)b * (G + 1) + j) * a.nchunks + c] = r;
+  if (threadIdx.x == 0) a.part[((size_t)b * (G + 1) + jr) * a.nchunks + c] = r;
 }
 
 // Kernel 2: one workgroup per sequence folds the chunk winners of its G+1
 // rows and compares the drafts with them.
 constexpr int kGreedyThreads = 256;
 
-__global__ __launch_bounds__(kGreedyThreads) void greedy_decide_kernel(GreedyArgs a) {
+__global__ __launch_bounds__(kGreedyThreads) void greedy_decide_kernel(GreedyArgs a, int from) {
   __shared__ int s_arg[kMaxG + 1];
   const int b = blockIdx.x;
   const int G = a.G;
+  // early exit: only the chains that reached position `from` (the others
+  // were decided by the per-position launches)
+  if (from >= 0 && a.reach[(size_t)from * a.B + b] == 0) return;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   for (int j = wave; j <= G; j += kGreedyThreads / 64) {
@@ -1203,11 +1203,15 @@ extern "C" dsa_status spec_verify(const float* target_logits, const float* draft
   const dim3 gs(nchunks, B * (2 * G + 1)), gm(ws.nmass, B);
   dsa_status st;
   if (ws.phased) {
-    // early exit: one launch per position, then the bonus draws' statistics
-    for (int j = 0; j <= G; ++j) {
-      const dim3 gp(nchunks, B, j < G ? 2 : 1);
-      if (nt) hipLaunchKernelGGL(verify_phase_kernel<true>, gp, dim3(kStatThreads), 0, s, a, ws, j);
-      else hipLaunchKernelGGL(verify_phase_kernel<false>, gp, dim3(kStatThreads), 0, s, a, ws, j);
+    // early exit: one launch per position up to the tail, then the tail's
+    // rows in one launch
+    ws.tail = min(kPhasedPositions, G);
+    for (int j = 0; j <= ws.tail; ++j) {
+      const int jl = j < ws.tail ? j : G;
+      const int nrows = (jl - j + 1) + (min(jl, G - 1) - j + 1);
+      const dim3 gp(nchunks, B, nrows);
+      if (nt) hipLaunchKernelGGL(verify_phase_kernel<true>, gp, dim3(kStatThreads), 0, s, a, ws, j, jl);
+      else hipLaunchKernelGGL(verify_phase_kernel<false>, gp, dim3(kStatThreads), 0, s, a, ws, j, jl);
       st = launch_status("spec_verify(phase)");
       if (st != DSA_OK) return st;
     }
@@ -1283,15 +1287,18 @@ extern "C" dsa_status spec_verify_greedy(const float* target_logits, const int32
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool nt = (size_t)B * (G + 1) * V * sizeof(float) > kStreamBytes;
   if (phased) {
-    // early exit: positions 0..G, then the bonus tokens
-    for (int j = 0; j <= G + 1; ++j) {
-      const dim3 gp(j <= G ? nchunks : 1, B);
+    // early exit: positions 0..P-1 one launch each, rows P..G in one, then
+    // the decision of the chains that reached P
+    const int P = min(kGreedyPhasedPositions, G);
+    for (int j = 0; j <= P; ++j) {
+      const dim3 gp(nchunks, B, j < P ? 1 : G - P + 1);
       if (nt) hipLaunchKernelGGL(greedy_phase_kernel<true>, gp, dim3(kArgThreads), 0, s, a, j);
       else hipLaunchKernelGGL(greedy_phase_kernel<false>, gp, dim3(kArgThreads), 0, s, a, j);
       const dsa_status st = launch_status("spec_verify_greedy(phase)");
       if (st != DSA_OK) return st;
     }
-    return DSA_OK;
+    hipLaunchKernelGGL(greedy_decide_kernel, dim3(B), dim3(kGreedyThreads), 0, s, a, P);
+    return launch_status("spec_verify_greedy(decide)");
   }
   const dim3 g1(nchunks, B * (G + 1));
   if (nt)
@@ -1300,6 +1307,6 @@ extern "C" dsa_status spec_verify_greedy(const float* target_logits, const int32
     hipLaunchKernelGGL(greedy_argmax_kernel<false>, g1, dim3(kArgThreads), 0, s, a);
   const dsa_status st = launch_status("spec_verify_greedy(argmax)");
   if (st != DSA_OK) return st;
-  hipLaunchKernelGGL(greedy_decide_kernel, dim3(B), dim3(kGreedyThreads), 0, s, a);
+  hipLaunchKernelGGL(greedy_decide_kernel, dim3(B), dim3(kGreedyThreads), 0, s, a, -1);
   return launch_status("spec_verify_greedy(decide)");
 }

@@ -40,6 +40,10 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0     # MI355X datasheet, dense
 FLUSH_BYTES = 1 << 30              # read-modify-write before each cache-flushed launch
 METRIC = "draft-step sparse-attn context tokens/s + verified positions/s; % of HBM roofline"
 WORKLOADS = ("batched_16x16k_64k", "decode_32k")
+# positions with a launch of their own in the library's early-exit verify
+# schedules (rejection sampling, greedy); the rest is read in one launch
+VERIFY_PHASED_POSITIONS = 4
+GREEDY_PHASED_POSITIONS = 2
 EXTRA_GROUPS = ("peaks", "decode_32k", "verify", "indexer_1m", "long_1m", "cross_layer", "verify_pass", "topk")
 
 
@@ -587,12 +591,15 @@ def _extra_verify(dsa, reps, peaks, cpu):
                             accepted_len=n, emitted=em, workspace=ws)
 
         # default schedule (early exit at this size): bytes it reads, from the
-        # accepted lengths: both rows of every position up to the first
-        # rejection (the target row of the bonus position after a full
-        # accept), then the sampled rows once more for the draw
+        # accepted lengths.  Positions 0..P-1 have a launch each (both rows of
+        # a position are read while the chain is accepted); a chain that
+        # reaches P reads all its remaining rows in one launch; then the
+        # sampled rows are read once more for the draw.
         us_w, us_c = time_warm(call, reps, inner=2), time_flushed(call, max(5, reps // 2))
         nn = n.cpu().long()
-        rows = torch.where(nn < G, 2 * (nn + 1) + 2, 2 * G + 1 + 1)
+        P = min(VERIFY_PHASED_POSITIONS, G)
+        redraw = torch.where(nn < G, 2, 1)
+        rows = torch.where(nn < P, 2 * (nn + 1), 2 * G + 1) + redraw
         e = hbm_entry(int(rows.sum()) * V * 4, us_w, us_c, peaks)
         e["schedule"] = "early exit (rows past each chain's first rejection are not read)"
         e["all_rows_bytes"] = vbytes
@@ -622,11 +629,13 @@ def _extra_verify(dsa, reps, peaks, cpu):
             def gcall():
                 dsa.spec_verify_greedy(v.target_logits, gdr, accepted_len=n, emitted=em, workspace=gws)
 
-            # default schedule (early exit): target rows 0..accepted length
+            # default schedule (early exit): target rows 0..accepted length, or
+            # all G+1 once a chain reaches the one-pass tail
             gbytes = B * (G + 1) * V * 4
             us_gw, us_gc = time_warm(gcall, reps, inner=2), time_flushed(gcall, max(5, reps // 2))
             nn = n.cpu().long()
-            e = hbm_entry(int(torch.clamp(nn + 1, max=G + 1).sum()) * V * 4, us_gw, us_gc, peaks)
+            Pg = min(GREEDY_PHASED_POSITIONS, G)
+            e = hbm_entry(int(torch.where(nn < Pg, nn + 1, G + 1).sum()) * V * 4, us_gw, us_gc, peaks)
             e["schedule"] = "early exit (rows past each chain's first mismatch are not read)"
             e["all_rows_bytes"] = gbytes
             e["all_rows_GBps_flushed"] = gbytes / us_gc / 1e3

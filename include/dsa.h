@@ -207,6 +207,12 @@ dsa_status dsa_sparse_attn_noalloc(const void* q, const void* k_cache, const voi
  *                 as used (NaN where not evaluated)
  * Supported: 1 <= G <= 32, 1 <= V <= 2^20, B*(2G+1) <= 65535.  Any V;
  * rows are read with 16-byte loads when V % 4 == 0 and the bases are aligned.
+ * Schedule: batches with at least 1 GiB of logits stop reading a sequence's
+ * rows after its first rejection (one launch per early position); smaller
+ * ones read every row once.  The environment variable DSA_VERIFY_SCHEDULE
+ * ("phased" or "onepass") overrides the choice, for tests and tuning; both
+ * give the same decisions up to float32 rounding of the softmax statistics.
+ * spec_verify_greedy follows the same rule over its target rows.
  */
 size_t spec_verify_workspace_size(int B, int G, int V);
 dsa_status spec_verify(const float* target_logits, const float* draft_logits,

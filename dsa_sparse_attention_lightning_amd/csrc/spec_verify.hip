@@ -24,6 +24,13 @@
 //   pick    one workgroup per sequence draws by inverse CDF: the chunk that
 //           holds u * W, the tile inside it (from the stored tile masses),
 //           then the token inside the tile.
+// Batches of 1 GiB of logits or more take an early-exit schedule instead of
+// the stats and decide launches: the protocol stops at the first rejection,
+// so one launch per early position reads a position's two rows only for the
+// chains still accepted (each workgroup first runs the accept test of the
+// position before), and one last launch reads the remaining rows of the few
+// chains that got that far; the mass kernel decides those, and pick is
+// unchanged.  Greedy verification has the same two schedules.
 // Uniforms come from the caller or from Philox4x64-10 (Salmon, Moraes, Dror,
 // Shaw, SC'11) evaluated in-kernel at counter (offset, b, j, stream).
 #include <cstdlib>

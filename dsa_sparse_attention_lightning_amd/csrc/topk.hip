@@ -699,16 +699,24 @@ __global__ __launch_bounds__(kOneThreads) void topk_one_kernel(const float* __re
     const uint32_t mask = (1u << nb) - 1u;
     for (int i = tid; i < (1 << nb); i += kOneThreads) sh.hist[i] = 0;
     __syncthreads();
-    for (int tb = 0; tb < L; tb += kU * kOneThreads) {
-      uint32_t kv[kU];
+    // four consecutive keys per 16-byte LDS read (the counts do not depend
+    // on the order; keys past L up to the next multiple of 4 are read and
+    // masked, inside the staging area)
+    constexpr int kQ = kU / 4;
+    for (int tb = 0; tb < L; tb += kQ * kOneThreads * 4) {
+      uint4 kv[kQ];
 #pragma unroll
-      for (int u = 0; u < kU; ++u) kv[u] = key_at(min(tb + u * kOneThreads + tid, L - 1));
+      for (int u = 0; u < kQ; ++u)
+        kv[u] = *reinterpret_cast<const uint4*>(keys + min(tb + (u * kOneThreads + tid) * 4, (int)align_up(L, 4) - 4));
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int t = tb + u * kOneThreads + tid;
-        const uint32_t key = kv[u];
-        const bool hit = t < L && (shift >= 32 || (key >> shift) == (prefix >> shift));
-        if (hit) atomicAdd(&sh.hist[(key >> nshift) & mask], 1u);
+      for (int u = 0; u < kQ; ++u) {
+        const int t = tb + (u * kOneThreads + tid) * 4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t key = e == 0 ? kv[u].x : e == 1 ? kv[u].y : e == 2 ? kv[u].z : kv[u].w;
+          const bool hit = t + e < L && (shift >= 32 || (key >> shift) == (prefix >> shift));
+          if (hit) atomicAdd(&sh.hist[(key >> nshift) & mask], 1u);
+        }
       }
     }
     __syncthreads();

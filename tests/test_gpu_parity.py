@@ -574,7 +574,9 @@ def test_spec_verify_many_sequences(std):
     (17, 7, 2048),      # first batch size with the decision in a kernel of its own
     (8, 7, 600000),     # decision inside the mass kernel, logits past the last-level cache (streamed)
 ])
-def test_spec_verify_shape_edges(B, G, V):
+@pytest.mark.parametrize("schedule", ["onepass", "phased"])
+def test_spec_verify_shape_edges(B, G, V, schedule, monkeypatch):
+    monkeypatch.setenv("DSA_VERIFY_SCHEDULE", schedule)
     vi = I.verify_inputs(B * 100 + G, B, G, V, 2.0)
     _, _, near = _verify_case(vi, True)
     assert near <= 1
@@ -598,13 +600,16 @@ def test_spec_verify_special_cases():
     assert np.all(n == 0) and np.all(em[:, 0] < V // 2)
 
 
+@pytest.mark.parametrize("schedule", ["onepass", "phased"])
 @pytest.mark.parametrize("V", [2048, 5003, 151552])
-def test_spec_verify_draw_at_the_top_of_the_cdf(V):
+def test_spec_verify_draw_at_the_top_of_the_cdf(V, schedule, monkeypatch):
     """u_smp = 1 - 2^-24 puts u * W within rounding of the total residual
     mass W, where the crossing search may find no crossing and must fall back
     to the last positive entry at every level.  The residual is positive only
     in the last 768 tokens (the tiles before them have zero mass) and the
-    last token holds 1/768 of W, so the oracle's draw is the last token."""
+    last token holds 1/768 of W, so the oracle's draw is the last token.  Both
+    schedules."""
+    monkeypatch.setenv("DSA_VERIFY_SCHEDULE", schedule)
     B, G = 4, 7
     tl = np.zeros((B, G + 1, V), np.float32)
     tl[..., V - 768:] = 2.0

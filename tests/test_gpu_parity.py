@@ -902,6 +902,48 @@ def test_draft_block_graph_replays():
             assert torch.equal(a, b), f"replay {rep} differs"
 
 
+@pytest.mark.parametrize("schedule", ["onepass", "phased"])
+def test_verify_graph_replays(schedule, monkeypatch):
+    """Rejection-sampling and greedy verification captured in one HIP graph
+    (the early-exit schedule is G+3 and 4 dependent launches): every replay,
+    with eager work and synchronisation between replays, gives the eager
+    call's accepted lengths, tokens and diagnostics."""
+    monkeypatch.setenv("DSA_VERIFY_SCHEDULE", schedule)
+    B, G, V = 24, 7, 20000
+    vi = I.verify_inputs(31, B, G, V, 2.0)
+    tl, dl, dr = to_dev(vi.target_logits), to_dev(vi.draft_logits), to_dev(vi.drafts)
+    gdr = tl[:, :G].argmax(dim=-1).to(torch.int32)
+    gdr[::3, 2] = (gdr[::3, 2] + 1) % V            # some greedy chains stop at position 2
+    n = torch.empty(B, dtype=torch.int32, device=DEV)
+    em = torch.empty((B, G + 1), dtype=torch.int32, device=DEV)
+    dg = torch.empty((B, G + 1, 4), device=DEV)
+    gn = torch.empty(B, dtype=torch.int32, device=DEV)
+    gem = torch.empty((B, G + 1), dtype=torch.int32, device=DEV)
+    vws = torch.empty(dsa.spec_verify_workspace_size(B, G, V), dtype=torch.uint8, device=DEV)
+    gws = torch.empty(dsa.spec_verify_greedy_workspace_size(B, G, V), dtype=torch.uint8, device=DEV)
+
+    def call():
+        dsa.spec_verify(tl, dl, dr, seed=7, offset=3, accepted_len=n, emitted=em, diag=dg, workspace=vws)
+        dsa.spec_verify_greedy(tl, gdr, accepted_len=gn, emitted=gem, workspace=gws)
+
+    call()
+    torch.cuda.synchronize()
+    outs = (n, em, dg, gn, gem)
+    ref = [x.clone() for x in outs]
+    assert 0 < float(n.float().mean()) < G and 0 < float(gn.float().mean()) < G
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+        call()
+    for rep in range(4):
+        for x in outs:
+            x.zero_()                    # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outs, ref):
+            assert torch.equal(a.nan_to_num(-9.0), b.nan_to_num(-9.0)), f"replay {rep} differs"
+
+
 # ----------------------------------------------------------------------------
 # latent MQA attention (one 576-d KV row shared by 64 heads, V = first 512)
 # ----------------------------------------------------------------------------

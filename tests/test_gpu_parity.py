@@ -903,6 +903,39 @@ def test_draft_block_graph_replays():
 
 
 @pytest.mark.parametrize("schedule", ["onepass", "phased"])
+def test_emitted_tokens_follow_target_distribution(schedule, monkeypatch):
+    """The kernel preserves the target distribution (section "Rejection
+    sampling and a loss that optimizes acceptance directly"): over 13,000
+    independent chains with the same logits, drafts drawn from q and the
+    in-kernel Philox uniforms, the first emitted token follows p_1 and the
+    second (after an accepted first draft) p_2, by a chi-square test, and the
+    first draft's acceptance rate equals sum_x min(p_1, q_1)."""
+    from scipy import stats
+    monkeypatch.setenv("DSA_VERIFY_SCHEDULE", schedule)
+    rng = np.random.default_rng(44)
+    V, B, G = 10, 13000, 2
+    tl1 = (rng.standard_normal((G + 1, V)) * 1.2).astype(np.float32)
+    dl1 = (rng.standard_normal((G, V)) * 1.2).astype(np.float32)
+    p = [O.softmax(tl1[j].astype(np.float64)) for j in range(G + 1)]
+    q = [O.softmax(dl1[j].astype(np.float64)) for j in range(G)]
+    tl = np.ascontiguousarray(np.broadcast_to(tl1, (B, G + 1, V)))
+    dl = np.ascontiguousarray(np.broadcast_to(dl1, (B, G, V)))
+    dr = np.stack([rng.choice(V, size=B, p=q[j]) for j in range(G)], axis=1).astype(np.int32)
+    n, em = dsa.spec_verify(to_dev(tl), to_dev(dl), to_dev(dr), seed=123, offset=0)
+    n, em = n.cpu().numpy(), em.cpu().numpy()
+    # the first draft is accepted with probability sum_x min(p_1, q_1)
+    # (section "Kimi K3"), within five standard errors
+    alpha = float(np.minimum(p[0], q[0]).sum())
+    assert abs(float((n >= 1).mean()) - alpha) < 5 * math.sqrt(alpha * (1 - alpha) / B)
+    first = np.bincount(em[:, 0], minlength=V)
+    second = np.bincount(em[n >= 1, 1], minlength=V)
+    for counts, pj in ((first, p[0]), (second, p[1])):
+        exp = pj * counts.sum()
+        assert exp.min() >= 5
+        assert stats.chisquare(counts, exp).pvalue > 1e-3
+
+
+@pytest.mark.parametrize("schedule", ["onepass", "phased"])
 def test_verify_graph_replays(schedule, monkeypatch):
     """Rejection-sampling and greedy verification captured in one HIP graph
     (the early-exit schedule is G+3 and 4 dependent launches): every replay,

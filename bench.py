@@ -574,6 +574,25 @@ def _closed_form_mean_accepted(v):
     return float(torch.cumprod(alpha, dim=1).sum(dim=1).mean())
 
 
+class _schedule:
+    """Sets DSA_VERIFY_SCHEDULE (the library reads it per call) for a block,
+    then restores what was there."""
+
+    def __init__(self, name):
+        self.name, self.old = name, None
+
+    def __enter__(self):
+        self.old = os.environ.get("DSA_VERIFY_SCHEDULE")
+        os.environ["DSA_VERIFY_SCHEDULE"] = self.name
+
+    def __exit__(self, *exc):
+        if self.old is None:
+            os.environ.pop("DSA_VERIFY_SCHEDULE", None)
+        else:
+            os.environ["DSA_VERIFY_SCHEDULE"] = self.old
+        return False
+
+
 def _extra_verify(dsa, reps, peaks, cpu):
     import torch
     from dsa_inputs import device as DI
@@ -606,12 +625,9 @@ def _extra_verify(dsa, reps, peaks, cpu):
         e["all_rows_GBps_flushed"] = vbytes / us_c / 1e3   # rate at which the batch's logits are consumed
         # the one-pass schedule on the same batch: every row read once (the
         # stats pass), the bandwidth figure of a full read
-        os.environ["DSA_VERIFY_SCHEDULE"] = "onepass"
-        try:
-            e1 = hbm_entry(vbytes, time_warm(call, reps, inner=2), time_flushed(call, max(5, reps // 2)), peaks)
-        finally:
-            del os.environ["DSA_VERIFY_SCHEDULE"]
-        e["onepass"] = e1
+        with _schedule("onepass"):
+            e["onepass"] = hbm_entry(vbytes, time_warm(call, reps, inner=2), time_flushed(call, max(5, reps // 2)),
+                                     peaks)
         e.update({"verified_positions_per_s_flushed": B * (G + 1) / (us_c * 1e-6),
                   "verified_positions_per_s_warm": B * (G + 1) / (us_w * 1e-6),
                   "mean_accepted_len": float(n.float().mean()),
@@ -639,12 +655,9 @@ def _extra_verify(dsa, reps, peaks, cpu):
             e["schedule"] = "early exit (rows past each chain's first mismatch are not read)"
             e["all_rows_bytes"] = gbytes
             e["all_rows_GBps_flushed"] = gbytes / us_gc / 1e3
-            os.environ["DSA_VERIFY_SCHEDULE"] = "onepass"
-            try:
+            with _schedule("onepass"):
                 e["onepass"] = hbm_entry(gbytes, time_warm(gcall, reps, inner=2),
                                          time_flushed(gcall, max(5, reps // 2)), peaks)
-            finally:
-                del os.environ["DSA_VERIFY_SCHEDULE"]
             e["verified_positions_per_s_flushed"] = B * (G + 1) / (us_gc * 1e-6)
             e["mean_accepted_len"] = float(n.float().mean())
             out["greedy_verify_256x8x151552_s2.0"] = e

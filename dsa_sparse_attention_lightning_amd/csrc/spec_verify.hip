@@ -57,10 +57,11 @@ constexpr int kArgStep = kArgThreads * 4;
 #define DSA_VERIFY_STAT_TARGET_WGS 512
 #endif
 constexpr int kStatTargetWgs = DSA_VERIFY_STAT_TARGET_WGS;
-// Early-exit (phased) verification: one launch per position, each reading
-// only the rows of the sequences whose chain is still accepted.  It replaces
-// the one-pass stats when the batch's logits reach this size (G more
-// launches against the rows after each first rejection left unread).
+// Early-exit (phased) verification: one launch per early position, each
+// reading only the rows of the sequences whose chain is still accepted, then
+// one for the rest.  It replaces the one-pass stats when the batch's logits
+// reach this size (a few more dependent launches against the rows after each
+// first rejection left unread).
 #ifndef DSA_VERIFY_PHASED_MIN_MB
 #define DSA_VERIFY_PHASED_MIN_MB 1024
 #endif

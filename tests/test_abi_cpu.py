@@ -200,3 +200,24 @@ def test_boundary_departures_are_the_recorded_ones():
     for extra in ("dsa_last_error", "spec_verify_greedy", "spec_verify_greedy_workspace_size",
                   "dsa_sparse_attn_noalloc"):
         assert extra in declared_functions()
+
+
+def test_verify_workspace_size_does_not_depend_on_the_schedule(monkeypatch):
+    """The verify schedules (one pass, early exit) share one workspace size, so
+    a workspace sized once serves either, whatever DSA_VERIFY_SCHEDULE says;
+    the size covers the early-exit bookkeeping at every size."""
+    shapes = [(1, 1, 10), (16, 7, 151552), (256, 7, 151552), (3, 32, 4099), (300, 1, 80000), (4, 7, 1 << 20)]
+    sizes = {}
+    for sched in (None, "onepass", "phased"):
+        if sched is None:
+            monkeypatch.delenv("DSA_VERIFY_SCHEDULE", raising=False)
+        else:
+            monkeypatch.setenv("DSA_VERIFY_SCHEDULE", sched)
+        sizes[sched] = [(lib.spec_verify_workspace_size(B, G, V), lib.spec_verify_greedy_workspace_size(B, G, V))
+                        for B, G, V in shapes]
+    assert sizes[None] == sizes["onepass"] == sizes["phased"]
+    for (B, G, V), (ws, gws) in zip(shapes, sizes[None]):
+        # at least one (max, sum) partial per row, the reach flags and the
+        # drafted tokens' logits; greedy: one argmax partial per row and the flags
+        assert ws >= B * (2 * G + 1) * 8 + (G + 1) * B * 4 + B * G * 8
+        assert gws >= B * (G + 1) * 8 + (G + 1) * B * 4
